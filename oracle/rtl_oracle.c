@@ -1,0 +1,273 @@
+/*
+ * rtl_oracle.c -- plain CPU reference of the norm-compensated 2:4 activation-sparse
+ * linear layer with a low-rank (LoRA) correction branch.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  The product path never calls it and
+ * shares no code, header, table or constant with it.
+ *
+ * Source of the method: "RT-Lynx: Putting the GEMM Sparsity In a Right Way for
+ * Diffusion Models" (summary page, method overview).
+ *   step 1 (norm-compensated activation sparsification): per token row X of length
+ *     D_in (a multiple of 4), keep 2 of every 4 channels by Top-K to obtain X~, then
+ *     s = ||X||_2 / (||X~||_2 + eps) with eps = 1e-8, and S(X) = s * X~.
+ *   step 2 (LoRA compensation): Y_s = S(X) W^T on the sparse branch, the original dense
+ *     X feeds a rank-R branch Y_r = X (L_A L_B)^T, and Y = Y_s + Y_r.
+ *
+ * Readings of points the page leaves open (each is listed with its reason in the
+ * design notes):
+ *   - "Top-K" ranks channels by magnitude |x|;
+ *   - a group is 4 consecutive channels starting at channel 0;
+ *   - equal magnitudes go to the lower channel index; exactly 2 positions are kept in
+ *     every group, even when fewer than 2 values are nonzero;
+ *   - eps is added to the norm (not to the squared norm);
+ *   - shapes: X [M,K], W [N,K], L_B [R,K], L_A [N,R], Y [M,N], all row-major, so
+ *     X (L_A L_B)^T = (X L_B^T) L_A^T;
+ *   - no bias term.
+ *
+ * Everything is computed in double precision on the exact input values (an fp32 or
+ * bf16 value converts to double without rounding).  Inputs must be finite.
+ * Parity status of every function: pinned by the CPU tests (brute force, closed forms,
+ * invariants and library special cases); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_TIE_LOWER = 0, ORC_TIE_HIGHER = 1, ORC_KEEP_ALL = 2 };
+enum { ORC_OK = 0, ORC_EARG = -1, ORC_ENONFINITE = -2, ORC_ENOMEM = -3 };
+
+/* Exact value of element i of an fp32 or bf16 array (bf16 = top 16 bits of an fp32). */
+static double orc_load(int dt, const void* p, int64_t i) {
+  if (dt == ORC_F32) return (double)((const float*)p)[i];
+  uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Raw element bits (used only to hand back bit copies of kept values). */
+static void orc_copy_elem(int dt, const void* src, int64_t i, void* dst, int64_t j) {
+  if (dt == ORC_F32)
+    ((uint32_t*)dst)[j] = ((const uint32_t*)src)[i];
+  else
+    ((uint16_t*)dst)[j] = ((const uint16_t*)src)[i];
+}
+
+/*
+ * Top-2-of-4 selection on one group (step 1, "Top-K, 2 of every 4").
+ * rank_j = #{l : |x_l| > |x_j|} + #{l tied with j that the tie rule puts ahead of j};
+ * position j is kept iff rank_j < 2.  Returns the 4-bit keep mask (bit j = position j).
+ */
+int orc_select4(const double x[4], int tie) {
+  if (tie == ORC_KEEP_ALL) return 0xF;
+  int mask = 0;
+  for (int j = 0; j < 4; j++) {
+    double aj = fabs(x[j]);
+    int rank = 0;
+    for (int l = 0; l < 4; l++) {
+      if (l == j) continue;
+      double al = fabs(x[l]);
+      if (al > aj) rank++;
+      else if (al == aj && ((tie == ORC_TIE_LOWER && l < j) || (tie == ORC_TIE_HIGHER && l > j))) rank++;
+    }
+    if (rank < 2) mask |= 1 << j;
+  }
+  return mask;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+static int orc_check_common(int dt, int64_t M, int64_t K, int tie) {
+  if (dt != ORC_F32 && dt != ORC_BF16) return ORC_EARG;
+  if (M < 0 || K <= 0 || K % 4 != 0) return ORC_EARG;
+  if (tie != ORC_TIE_LOWER && tie != ORC_TIE_HIGHER && tie != ORC_KEEP_ALL) return ORC_EARG;
+  return ORC_OK;
+}
+
+/*
+ * Selection, compression and norms for every row (step 1).
+ *   mask  [M, K/4]  (nullable) keep mask of each group, bit j = position j
+ *   idx   [M, K/4]  (nullable) idx0 | idx1 << 2 with idx0 < idx1 the kept positions
+ *                   (meaningful when the mask keeps exactly 2 positions)
+ *   vals  [M, K/2]  (nullable) bit copies of the kept values in ascending position order
+ *   nx2, nt2, s [M] (nullable) ||X||^2, ||X~||^2 and s = ||X|| / (||X~|| + eps)
+ * KEEP_ALL mode keeps every position (X~ = X); idx and vals are then not written.
+ */
+int orc_sparsify(int dt, int64_t M, int64_t K, const void* X, int tie, double eps,
+                 uint8_t* mask, uint8_t* idx, void* vals, double* nx2, double* nt2,
+                 double* s) {
+  int rc = orc_check_common(dt, M, K, tie);
+  if (rc) return rc;
+  if (!X) return ORC_EARG;
+  const int64_t G = K / 4;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t i = 0; i < M; i++) {
+    double sx = 0.0, st = 0.0;
+    for (int64_t g = 0; g < G; g++) {
+      double x[4];
+      for (int j = 0; j < 4; j++) {
+        x[j] = orc_load(dt, X, i * K + 4 * g + j);
+        if (!isfinite(x[j])) bad = 1;
+      }
+      int m = orc_select4(x, tie);
+      if (mask) mask[i * G + g] = (uint8_t)m;
+      int kept[4], nk = 0;
+      for (int j = 0; j < 4; j++) {
+        sx += x[j] * x[j];
+        if (m & (1 << j)) {
+          st += x[j] * x[j];
+          kept[nk++] = j;
+        }
+      }
+      if (nk == 2) {
+        if (idx) idx[i * G + g] = (uint8_t)(kept[0] | (kept[1] << 2));
+        if (vals) {
+          orc_copy_elem(dt, X, i * K + 4 * g + kept[0], vals, i * (K / 2) + 2 * g);
+          orc_copy_elem(dt, X, i * K + 4 * g + kept[1], vals, i * (K / 2) + 2 * g + 1);
+        }
+      }
+    }
+    if (nx2) nx2[i] = sx;
+    if (nt2) nt2[i] = st;
+    if (s) s[i] = sqrt(sx) / (sqrt(st) + eps);
+  }
+  return bad ? ORC_ENONFINITE : ORC_OK;
+}
+
+/*
+ * Full layer output for a list of rows (steps 1 and 2):
+ *   Y[r, n] = s_i * sum_k X~[i,k] W[n,k] + sum_q T[i,q] L_A[n,q],
+ *   T[i, q] = sum_k X[i,k] L_B[q,k]   (dense X feeds the low-rank branch),
+ * with i = rows[r] (rows == NULL means every row, i = r).  Y is [nrows, N] double.
+ * s_out [nrows] and T_out [nrows, R] are nullable.  R == 0 drops the low-rank branch.
+ */
+int orc_linear(int dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
+               const void* W, const void* LA, const void* LB, int tie, double eps,
+               const int64_t* rows, int64_t nrows, double* Y, double* s_out,
+               double* T_out) {
+  int rc = orc_check_common(dt, M, K, tie);
+  if (rc) return rc;
+  if (N <= 0 || R < 0 || !X || !W || !Y) return ORC_EARG;
+  if (R > 0 && (!LA || !LB)) return ORC_EARG;
+  if (!rows) nrows = M;
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) return ORC_EARG;
+  }
+  /* Weights as exact doubles, converted once. */
+  double* Wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+  double* LAd = R > 0 ? (double*)malloc(sizeof(double) * (size_t)(N * R)) : NULL;
+  double* LBd = R > 0 ? (double*)malloc(sizeof(double) * (size_t)(R * K)) : NULL;
+  if (!Wd || (R > 0 && (!LAd || !LBd))) {
+    free(Wd); free(LAd); free(LBd);
+    return ORC_ENOMEM;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < N * K; e++) Wd[e] = orc_load(dt, W, e);
+  for (int64_t e = 0; e < N * R; e++) LAd[e] = orc_load(dt, LA, e);
+  for (int64_t e = 0; e < R * K; e++) LBd[e] = orc_load(dt, LB, e);
+
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)K);
+    double* xt = (double*)malloc(sizeof(double) * (size_t)K);
+    double* T = (double*)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    if (!x || !xt || !T) bad |= 2;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; r++) {
+      if (bad & 2) continue;
+      int64_t i = rows ? rows[r] : r;
+      /* Step 1: X~ (dropped positions set to 0), the two norms and s. */
+      double sx = 0.0, st = 0.0;
+      for (int64_t g = 0; g < K / 4; g++) {
+        double q[4];
+        for (int j = 0; j < 4; j++) {
+          q[j] = orc_load(dt, X, i * K + 4 * g + j);
+          if (!isfinite(q[j])) bad |= 1;
+        }
+        int m = orc_select4(q, tie);
+        for (int j = 0; j < 4; j++) {
+          x[4 * g + j] = q[j];
+          xt[4 * g + j] = (m & (1 << j)) ? q[j] : 0.0;
+          sx += q[j] * q[j];
+          st += xt[4 * g + j] * xt[4 * g + j];
+        }
+      }
+      double s = sqrt(sx) / (sqrt(st) + eps);
+      if (s_out) s_out[r] = s;
+      /* Step 2, low-rank branch input: T = X L_B^T on the dense row. */
+      for (int64_t q = 0; q < R; q++) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; k++) acc += x[k] * LBd[q * K + k];
+        T[q] = acc;
+        if (T_out) T_out[r * R + q] = acc;
+      }
+      /* Step 2: Y = s * (X~ W^T) + T L_A^T. */
+      for (int64_t n = 0; n < N; n++) {
+        double ys = 0.0;
+        for (int64_t k = 0; k < K; k++) ys += xt[k] * Wd[n * K + k];
+        double yr = 0.0;
+        for (int64_t q = 0; q < R; q++) yr += T[q] * LAd[n * R + q];
+        Y[r * N + n] = s * ys + yr;
+      }
+    }
+    free(x); free(xt); free(T);
+  }
+  free(Wd); free(LAd); free(LBd);
+  if (bad & 2) return ORC_ENOMEM;
+  return (bad & 1) ? ORC_ENONFINITE : ORC_OK;
+}
+
+/*
+ * Plain dense product Y[r, n] = sum_k X[i,k] W[n,k] for i = rows[r]: the layer that
+ * the sparse one replaces, and the one that layers left dense keep (method step 3,
+ * selective layer skipping).
+ */
+int orc_dense(int dt, int64_t M, int64_t N, int64_t K, const void* X, const void* W,
+              const int64_t* rows, int64_t nrows, double* Y) {
+  if ((dt != ORC_F32 && dt != ORC_BF16) || M < 0 || N <= 0 || K <= 0 || !X || !W || !Y)
+    return ORC_EARG;
+  if (!rows) nrows = M;
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) return ORC_EARG;
+  }
+  double* Wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+  if (!Wd) return ORC_ENOMEM;
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < N * K; e++) Wd[e] = orc_load(dt, W, e);
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!x) bad |= 2;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; r++) {
+      if (bad & 2) continue;
+      int64_t i = rows ? rows[r] : r;
+      for (int64_t k = 0; k < K; k++) x[k] = orc_load(dt, X, i * K + k);
+      for (int64_t n = 0; n < N; n++) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; k++) acc += x[k] * Wd[n * K + k];
+        Y[r * N + n] = acc;
+      }
+    }
+    free(x);
+  }
+  free(Wd);
+  return (bad & 2) ? ORC_ENOMEM : ORC_OK;
+}

@@ -1,0 +1,48 @@
+"""Seeded input generators: determinism, shapes and the input rounding (CPU only)."""
+import numpy as np
+
+import synth
+
+
+def test_deterministic_and_seed_sensitive():
+    a = synth.normal(5, (64, 128))
+    b = synth.normal(5, (64, 128))
+    c = synth.normal(6, (64, 128))
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert abs(a.mean()) < 0.05 and abs(a.std() - 1) < 0.05
+
+
+def test_counter_mode_prefix_stable():
+    """Element e depends only on (seed, e): a longer draw extends a shorter one."""
+    a = synth.normal(9, (100,))
+    b = synth.normal(9, (1000,))
+    assert np.array_equal(a, b[:100])
+
+
+def test_heavy_rows_active_count():
+    X = synth.heavy_rows(1, 2, 32, 3072, 246, 3.0, 0.1)
+    big = (np.abs(X) > 1.0).sum(1)   # N(0, 0.1^2) essentially never exceeds 1
+    assert np.all(big <= 246) and big.mean() > 246 * 0.6
+
+
+def test_bf16_round_to_nearest_even():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8 + 2 ** -20), 3.0e38, 1e-40], np.float32)
+    got = synth.to_bf16(x)
+    want = np.array([0x3F80, 0x3F80, 0x3F82, 0xBF81, 0x7F62, 0x0001], np.uint16)
+    assert got.tolist() == want.tolist()
+    assert np.array_equal(synth.bf16_to_f32(got)[:3], np.array([1.0, 1.0, 1.015625], np.float32))
+
+
+def test_layer_shapes():
+    for name, lay in synth.LAYERS.items():
+        if lay.M * lay.K > 5e6:
+            d = synth.make_layer(name, M=8)
+            assert d["X"].shape == (8, lay.K)
+        else:
+            d = synth.make_layer(name)
+            assert d["X"].shape == (lay.M, lay.K)
+        assert d["W"].shape == (lay.N, lay.K)
+        if lay.R:
+            assert d["LA"].shape == (lay.N, lay.R) and d["LB"].shape == (lay.R, lay.K)
+        want = np.float32 if lay.dtype == "f32" else np.uint16
+        assert d["X"].dtype == want
