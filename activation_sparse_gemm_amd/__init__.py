@@ -1,0 +1,187 @@
+"""Norm-compensated 2:4 activation-sparse linear layer with a low-rank branch, on MI355X.
+
+Thin Python binding of the C ABI in ``include/rtl.h`` (``librtl.so``, gfx950 HIP
+kernels).  Every function here only marshals arguments: tensors stay on the GPU, the
+work runs in the library's kernels on the current torch stream, and nothing falls back
+to the CPU.  If the library is missing the import fails loudly; build it with
+``python activation_sparse_gemm_amd/build.py``.
+
+Method: "RT-Lynx: Putting the GEMM Sparsity In a Right Way for Diffusion Models"
+(summary page, method steps 1, 2 and 4):
+    X~ = top-2-of-4 magnitudes of X,  s = ||X|| / (||X~|| + eps),
+    Y  = s * (X~ W^T) + (X L_B^T) L_A^T.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RTL_F32", "RTL_BF16", "RTL_TIE_LOWER_INDEX", "EPS", "RtlError", "lib", "library_path",
+    "rtl_sparsify", "rtl_linear_fused", "rtl_linear_fused_workspace_bytes", "rtl_lora_down",
+    "rtl_linear_fused_gemm", "rtl_linear_dense_ref",
+    "rtl_status_string", "rtl_version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "librtl.so")
+
+RTL_F32, RTL_BF16 = 0, 1
+RTL_TIE_LOWER_INDEX = 0
+EPS = 1e-8
+STATUS = {0: "RTL_OK", 1: "RTL_ERR_NULL", 2: "RTL_ERR_SHAPE", 3: "RTL_ERR_ALIGN", 4: "RTL_ERR_UNSUPPORTED",
+          5: "RTL_ERR_ARG", 6: "RTL_ERR_WORKSPACE", 7: "RTL_ERR_HIP"}
+
+# Every entry point include/rtl.h declares.
+EXPORTS = ["rtl_sparsify", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused", "rtl_lora_down",
+           "rtl_linear_fused_gemm", "rtl_linear_dense_ref", "rtl_status_string", "rtl_last_error", "rtl_version"]
+
+
+class RtlError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(library_path):
+        raise ImportError(f"{library_path} is missing: build it with `python activation_sparse_gemm_amd/build.py`")
+    L = ctypes.CDLL(library_path)
+    p, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.rtl_sparsify.argtypes = [i32, i64, i64, p, i32, f32, p, p, p, p]
+    L.rtl_sparsify.restype = i32
+    L.rtl_linear_fused_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+    L.rtl_linear_fused_workspace_bytes.restype = sz
+    L.rtl_linear_fused.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, sz, p, p, p]
+    L.rtl_linear_fused.restype = i32
+    L.rtl_lora_down.argtypes = [i32, i64, i64, i64, p, p, p, p]
+    L.rtl_lora_down.restype = i32
+    L.rtl_linear_fused_gemm.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, p, p]
+    L.rtl_linear_fused_gemm.restype = i32
+    L.rtl_linear_dense_ref.argtypes = [i32, i64, i64, i64, p, p, p, p]
+    L.rtl_linear_dense_ref.restype = i32
+    L.rtl_status_string.argtypes = [i32]
+    L.rtl_status_string.restype = ctypes.c_char_p
+    L.rtl_last_error.argtypes = []
+    L.rtl_last_error.restype = ctypes.c_char_p
+    L.rtl_version.argtypes = []
+    L.rtl_version.restype = i32
+    return L
+
+
+lib = _load()
+
+
+def rtl_status_string(status: int) -> str:
+    return lib.rtl_status_string(status).decode()
+
+
+def rtl_version() -> int:
+    return lib.rtl_version()
+
+
+def _check(status: int):
+    if status != 0:
+        raise RtlError(status, lib.rtl_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RTL_F32
+    if t.dtype == torch.bfloat16:
+        return RTL_BF16
+    raise TypeError(f"tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def rtl_sparsify(X: torch.Tensor, tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS, vals=None, idx=None, s=None,
+                 stream=None):
+    """Selection, compression and rescale factor of every row of X [M,K].
+
+    Returns (vals [M,K/2] X.dtype, idx [M,K/4] uint8, s [M] float32); outputs given by
+    the caller are written in place."""
+    M, K = X.shape
+    if vals is None:
+        vals = torch.empty((M, K // 2), dtype=X.dtype, device=X.device)
+    if idx is None:
+        idx = torch.empty((M, K // 4), dtype=torch.uint8, device=X.device)
+    if s is None:
+        s = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib.rtl_sparsify(_dt(X), M, K, _ptr(X), tie, eps, _ptr(vals), _ptr(idx), _ptr(s), _stream(stream)))
+    return vals, idx, s
+
+
+def rtl_linear_fused_workspace_bytes(dtype: int, M: int, N: int, K: int, R: int) -> int:
+    return int(lib.rtl_linear_fused_workspace_bytes(dtype, M, N, K, R))
+
+
+def rtl_linear_fused(X: torch.Tensor, W: torch.Tensor, LA, LB, tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS,
+                     Y=None, workspace=None, dbg_idx=None, dbg_s=None, stream=None) -> torch.Tensor:
+    """Y = s * (X~ W^T) + (X L_B^T) L_A^T.  X [M,K], W [N,K], LA [N,R], LB [R,K] (LA/LB None: R = 0).
+
+    ``workspace`` (a uint8 tensor) is allocated when not given; pass one to keep the call
+    free of allocations.  ``dbg_idx`` [M,K/4] uint8 and ``dbg_s`` [M] float32 receive the
+    selection codes and s computed inside the kernel."""
+    M, K = X.shape
+    N = W.shape[0]
+    R = 0 if LB is None else LB.shape[0]
+    dt = _dt(X)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    need = rtl_linear_fused_workspace_bytes(dt, M, N, K, R)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.rtl_linear_fused(dt, M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
+                                _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
+    return Y
+
+
+def rtl_lora_down(X: torch.Tensor, LB: torch.Tensor, T=None, stream=None) -> torch.Tensor:
+    """T = X L_B^T, [M,R] bf16: the skinny rank-R stage of rtl_linear_fused."""
+    M, K = X.shape
+    R = LB.shape[0]
+    if T is None:
+        T = torch.empty((M, R), dtype=X.dtype, device=X.device)
+    _check(lib.rtl_lora_down(_dt(X), M, K, R, _ptr(X), _ptr(LB), _ptr(T), _stream(stream)))
+    return T
+
+
+def rtl_linear_fused_gemm(X: torch.Tensor, W: torch.Tensor, LA, T, tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS,
+                          Y=None, dbg_idx=None, dbg_s=None, stream=None) -> torch.Tensor:
+    """Y = s * (X~ W^T) + T L_A^T with T from rtl_lora_down: the fused GEMM stage."""
+    M, K = X.shape
+    N = W.shape[0]
+    R = 0 if T is None else T.shape[1]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _check(lib.rtl_linear_fused_gemm(_dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(T), tie, eps, _ptr(Y),
+                                     _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
+    return Y
+
+
+def rtl_linear_dense_ref(X: torch.Tensor, W: torch.Tensor, Y=None, stream=None) -> torch.Tensor:
+    """Dense Y = X W^T with the fused kernel's tiling (the comparison layer)."""
+    M, K = X.shape
+    N = W.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _check(lib.rtl_linear_dense_ref(_dt(X), M, N, K, _ptr(X), _ptr(W), _ptr(Y), _stream(stream)))
+    return Y

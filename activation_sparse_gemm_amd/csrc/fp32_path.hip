@@ -1,0 +1,177 @@
+// fp32_path.hip -- fp32 mode of the layer on the vector ALUs (the matrix cores have no
+// fp32 2:4-sparse instruction).  Same arithmetic as the bf16 path ("RT-Lynx: Putting the
+// GEMM Sparsity In a Right Way for Diffusion Models", summary page, method steps 1-2):
+// selection in the tile prologue, row norms accumulated across the K loop, rank-R
+// down projection of the dense rows in the same loop, s and the rank-R up projection in
+// the epilogue.  Sized for small latency-bound layers.
+#include "rtl_device.h"
+#include "rtl_launch.h"
+
+namespace rtl {
+
+constexpr int kFT = 32;    // tile rows and columns
+constexpr int kFK = 32;    // K per step
+constexpr int kFMaxR = 128;
+
+template <bool SPARSE>
+__global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t K, int64_t R,
+                                                  const float* __restrict__ X, const float* __restrict__ W,
+                                                  const float* __restrict__ LA, const float* __restrict__ LB,
+                                                  float eps, float* __restrict__ Y, uint8_t* __restrict__ dbg_idx,
+                                                  float* __restrict__ dbg_s) {
+  __shared__ float As[kFT][kFK + 1];   // X~ (or X) tile
+  __shared__ float Xs[kFT][kFK + 1];   // dense X tile (rank-R branch input)
+  __shared__ float Ws[kFT][kFK + 1];
+  __shared__ float Bs[kFMaxR][kFK + 1];  // L_B tile
+  __shared__ float Ts[kFT][kFMaxR];
+  __shared__ float red[2][kFT][kFK / 4];
+  __shared__ float srow[kFT];
+
+  const int tid = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * kFT, n0 = (int64_t)blockIdx.x * kFT;
+  // loader role: one group of 4 per thread, tile row lr, group lg
+  const int lr = tid >> 3, lg = tid & 7;
+  const int64_t xr = m0 + lr < M ? m0 + lr : M - 1;
+  const int64_t wr = n0 + lr < N ? n0 + lr : N - 1;
+  // compute role: outputs (ty, tx), (ty, tx+16), (ty+16, tx), (ty+16, tx+16)
+  const int ty = tid >> 4, tx = tid & 15;
+  // rank-R role: T entries tid, tid + 256, ... of the 32 x R tile
+  const int nT = SPARSE ? (int)(kFT * R) : 0;
+
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  float tacc[kFT * kFMaxR / 256];
+#pragma unroll
+  for (int i = 0; i < kFT * kFMaxR / 256; i++) tacc[i] = 0.f;
+  float nx2 = 0.f, nt2 = 0.f;
+
+  for (int64_t k0 = 0; k0 < K; k0 += kFK) {
+    // X group: selection (tile prologue)
+    {
+      const int64_t k = k0 + 4 * lg;
+      uint32_t x[4] = {0u, 0u, 0u, 0u};
+      if (k < K) {
+        const u32x4 d = *reinterpret_cast<const u32x4*>(X + xr * K + k);
+        x[0] = d[0]; x[1] = d[1]; x[2] = d[2]; x[3] = d[3];
+      }
+      float kept[4] = {__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3])};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        Xs[lr][4 * lg + j] = kept[j];
+        nx2 = fmaf(kept[j], kept[j], nx2);
+      }
+      if (SPARSE) {
+        int lo, hi;
+        select_f32(x, lo, hi);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          if (j != lo && j != hi) kept[j] = 0.f;
+        const float vlo = __uint_as_float(x[lo]), vhi = __uint_as_float(x[hi]);
+        nt2 = fmaf(vlo, vlo, nt2);
+        nt2 = fmaf(vhi, vhi, nt2);
+        if (dbg_idx != nullptr && blockIdx.x == 0 && m0 + lr < M && k < K)
+          dbg_idx[(m0 + lr) * (K / 4) + k / 4] = (uint8_t)(lo | (hi << 2));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) As[lr][4 * lg + j] = kept[j];
+      const int64_t kw = k0 + 4 * lg;
+      u32x4 wv = {0u, 0u, 0u, 0u};
+      if (kw < K) wv = *reinterpret_cast<const u32x4*>(W + wr * K + kw);
+#pragma unroll
+      for (int j = 0; j < 4; j++) Ws[lr][4 * lg + j] = __uint_as_float(wv[j]);
+      if (SPARSE) {
+        for (int e = tid; e < (int)R * (kFK / 4); e += 256) {
+          const int rr = e / (kFK / 4), gg = e % (kFK / 4);
+          const int64_t kb = k0 + 4 * gg;
+          u32x4 bv = {0u, 0u, 0u, 0u};
+          if (kb < K) bv = *reinterpret_cast<const u32x4*>(LB + (int64_t)rr * K + kb);
+#pragma unroll
+          for (int j = 0; j < 4; j++) Bs[rr][4 * gg + j] = __uint_as_float(bv[j]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < kFK; kk++) {
+      const float a0 = As[ty][kk], a1 = As[ty + 16][kk];
+      const float b0 = Ws[tx][kk], b1 = Ws[tx + 16][kk];
+      acc[0][0] = fmaf(a0, b0, acc[0][0]);
+      acc[0][1] = fmaf(a0, b1, acc[0][1]);
+      acc[1][0] = fmaf(a1, b0, acc[1][0]);
+      acc[1][1] = fmaf(a1, b1, acc[1][1]);
+    }
+    if (SPARSE) {
+#pragma unroll
+      for (int i = 0; i < kFT * kFMaxR / 256; i++) {
+        const int e = tid + 256 * i;
+        if (e < nT) {
+          const int rr = e / (int)R, qq = e % (int)R;
+          float t = tacc[i];
+          for (int kk = 0; kk < kFK; kk++) t = fmaf(Xs[rr][kk], Bs[qq][kk], t);
+          tacc[i] = t;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (SPARSE) {
+    red[0][lr][lg] = nx2;
+    red[1][lr][lg] = nt2;
+#pragma unroll
+    for (int i = 0; i < kFT * kFMaxR / 256; i++) {
+      const int e = tid + 256 * i;
+      if (e < nT) Ts[e / (int)R][e % (int)R] = tacc[i];
+    }
+    __syncthreads();
+    if (tid < kFT) {
+      float a = 0.f, t = 0.f;
+      for (int g = 0; g < kFK / 4; g++) {
+        a += red[0][tid][g];
+        t += red[1][tid][g];
+      }
+      const float s = sqrtf(a) / (sqrtf(t) + eps);
+      srow[tid] = s;
+      if (dbg_s != nullptr && blockIdx.x == 0 && m0 + tid < M) dbg_s[m0 + tid] = s;
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int rl = ty + 16 * i;
+    const int64_t row = m0 + rl;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int64_t col = n0 + tx + 16 * j;
+      if (col >= N) continue;
+      float y = acc[i][j];
+      if (SPARSE) {
+        y *= srow[rl];
+        for (int qq = 0; qq < (int)R; qq++) y = fmaf(Ts[rl][qq], LA[col * R + qq], y);
+      }
+      Y[row * N + col] = y;
+    }
+  }
+}
+
+size_t fused_f32_workspace(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+hipError_t launch_fused_f32(int64_t M, int64_t N, int64_t K, int64_t R, const float* X, const float* W,
+                            const float* LA, const float* LB, float eps, float* Y, void*, uint8_t* dbg_idx,
+                            float* dbg_s, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + kFT - 1) / kFT), (unsigned)((M + kFT - 1) / kFT));
+  hipLaunchKernelGGL(f32_kernel<true>, grid, dim3(256), 0, stream, M, N, K, R, X, W, LA, LB, eps, Y, dbg_idx,
+                     dbg_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_f32(int64_t M, int64_t N, int64_t K, const float* X, const float* W, float* Y,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((N + kFT - 1) / kFT), (unsigned)((M + kFT - 1) / kFT));
+  hipLaunchKernelGGL(f32_kernel<false>, grid, dim3(256), 0, stream, M, N, K, (int64_t)0, X, W,
+                     (const float*)nullptr, (const float*)nullptr, 0.f, Y, (uint8_t*)nullptr, (float*)nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace rtl

@@ -1,0 +1,224 @@
+// rtl_api.cpp -- the C ABI declared in include/rtl.h: synchronous validation, then
+// dispatch to the gfx950 kernels on the caller's stream.  No exception crosses the ABI,
+// and a call that fails validation launches nothing and writes no output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/rtl.h"
+#include "rtl_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rtl_status fail(rtl_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rtl_status fail(rtl_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+rtl_status ok() {
+  g_err[0] = '\0';
+  return RTL_OK;
+}
+
+size_t elem_size(rtl_dtype dt) { return dt == RTL_BF16 ? 2 : 4; }
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges; empty ranges never overlap).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+rtl_status check_dtype(rtl_dtype dt) {
+  if (dt != RTL_F32 && dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "unsupported dtype %d", (int)dt);
+  return RTL_OK;
+}
+
+rtl_status check_eps(float eps) {
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(RTL_ERR_ARG, "eps must be finite and >= 0");
+  return RTL_OK;
+}
+
+rtl_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RTL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rtl_version(void) { return 100; }
+
+const char* rtl_last_error(void) { return g_err; }
+
+const char* rtl_status_string(rtl_status st) {
+  switch (st) {
+    case RTL_OK: return "RTL_OK";
+    case RTL_ERR_NULL: return "RTL_ERR_NULL: a required pointer is NULL";
+    case RTL_ERR_SHAPE: return "RTL_ERR_SHAPE: invalid shape";
+    case RTL_ERR_ALIGN: return "RTL_ERR_ALIGN: pointer not 16-byte aligned";
+    case RTL_ERR_UNSUPPORTED: return "RTL_ERR_UNSUPPORTED: unsupported tie rule, dtype or shape";
+    case RTL_ERR_ARG: return "RTL_ERR_ARG: invalid argument";
+    case RTL_ERR_WORKSPACE: return "RTL_ERR_WORKSPACE: workspace missing or too small";
+    case RTL_ERR_HIP: return "RTL_ERR_HIP: HIP runtime error";
+  }
+  return "unknown rtl_status";
+}
+
+rtl_status rtl_sparsify(rtl_dtype dt, int64_t M, int64_t K, const void* X, rtl_tie_rule tie, float eps,
+                        void* vals, uint8_t* idx, float* s, void* stream) {
+  rtl_status st;
+  if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
+  if (M <= 0 || K <= 0 || K % 4 != 0) return fail(RTL_ERR_SHAPE, "need M > 0, K > 0, K %% 4 == 0 (M=%lld K=%lld)",
+                                                  (long long)M, (long long)K);
+  if (!X || !vals || !idx || !s) return fail(RTL_ERR_NULL, "X, vals, idx and s are required");
+  if (misaligned(X) || misaligned(vals) || misaligned(idx) || misaligned(s))
+    return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if ((st = check_eps(eps)) != RTL_OK) return st;
+  const size_t es = elem_size(dt);
+  const size_t xb = (size_t)M * K * es, vb = (size_t)M * (K / 2) * es, ib = (size_t)M * (K / 4), sb = (size_t)M * 4;
+  if (overlap(vals, vb, X, xb) || overlap(idx, ib, X, xb) || overlap(s, sb, X, xb) || overlap(vals, vb, idx, ib) ||
+      overlap(vals, vb, s, sb) || overlap(idx, ib, s, sb))
+    return fail(RTL_ERR_ARG, "outputs overlap each other or the input");
+  return hip_status(rtl::launch_sparsify(dt == RTL_BF16 ? rtl::kDtBF16 : rtl::kDtF32, M, K, X, eps, vals, idx, s,
+                                         (hipStream_t)stream),
+                    "rtl_sparsify launch");
+}
+
+size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R) {
+  if (M <= 0 || N <= 0 || K <= 0 || R < 0) return 0;
+  if (dt == RTL_BF16) return rtl::fused_bf16_workspace(M, N, K, R);
+  if (dt == RTL_F32) return rtl::fused_f32_workspace(M, N, K, R);
+  return 0;
+}
+
+rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
+                            const void* W, const void* LA, const void* LB, rtl_tie_rule tie, float eps, void* Y,
+                            void* workspace, size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream) {
+  rtl_status st;
+  if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
+  if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
+    return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
+                (long long)N, (long long)K, (long long)R);
+  if (!X || !W || !Y || (R > 0 && (!LA || !LB))) return fail(RTL_ERR_NULL, "X, W, Y (and LA, LB when R > 0) are required");
+  if (misaligned(X) || misaligned(W) || misaligned(Y) || misaligned(LA) || misaligned(LB) || misaligned(workspace) ||
+      misaligned(dbg_idx) || misaligned(dbg_s))
+    return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (dt == RTL_BF16) {
+    if (K % 64 != 0) return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0 (K=%lld)", (long long)K);
+    if (R % 32 != 0 || R > 128) return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs R %% 32 == 0 and R <= 128 (R=%lld)",
+                                            (long long)R);
+  } else if (R > 128) {
+    return fail(RTL_ERR_UNSUPPORTED, "fp32 path needs R <= 128 (R=%lld)", (long long)R);
+  }
+  if ((st = check_eps(eps)) != RTL_OK) return st;
+  const size_t es = elem_size(dt);
+  const size_t xb = (size_t)M * K * es, wb = (size_t)N * K * es, lab = (size_t)N * R * es, lbb = (size_t)R * K * es;
+  const size_t yb = (size_t)M * N * es, ib = (size_t)M * (K / 4), sb = (size_t)M * 4;
+  const void* ins[4] = {X, W, R > 0 ? LA : nullptr, R > 0 ? LB : nullptr};
+  const size_t inb[4] = {xb, wb, lab, lbb};
+  const size_t need = rtl_linear_fused_workspace_bytes(dt, M, N, K, R);
+  for (int i = 0; i < 4; i++) {
+    if (overlap(Y, yb, ins[i], inb[i]) || overlap(dbg_idx, ib, ins[i], inb[i]) || overlap(dbg_s, sb, ins[i], inb[i]) ||
+        overlap(workspace, need, ins[i], inb[i]))
+      return fail(RTL_ERR_ARG, "an output or the workspace overlaps an input");
+  }
+  if (overlap(Y, yb, dbg_idx, ib) || overlap(Y, yb, dbg_s, sb) || overlap(dbg_idx, ib, dbg_s, sb) ||
+      overlap(workspace, need, Y, yb) || overlap(workspace, need, dbg_idx, ib) || overlap(workspace, need, dbg_s, sb))
+    return fail(RTL_ERR_ARG, "outputs overlap each other or the workspace");
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(RTL_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0);
+  hipError_t e;
+  if (dt == RTL_BF16)
+    e = rtl::launch_fused_bf16(M, N, K, R, X, W, LA, LB, eps, Y, workspace, dbg_idx, dbg_s, (hipStream_t)stream);
+  else
+    e = rtl::launch_fused_f32(M, N, K, R, (const float*)X, (const float*)W, (const float*)LA, (const float*)LB, eps,
+                              (float*)Y, workspace, dbg_idx, dbg_s, (hipStream_t)stream);
+  return hip_status(e, "rtl_linear_fused launch");
+}
+
+rtl_status rtl_lora_down(rtl_dtype dt, int64_t M, int64_t K, int64_t R, const void* X, const void* LB, void* T,
+                         void* stream) {
+  rtl_status st;
+  if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "rtl_lora_down supports bf16 only");
+  if (M <= 0 || K <= 0 || K % 4 != 0 || R <= 0)
+    return fail(RTL_ERR_SHAPE, "need M, K, R > 0 and K %% 4 == 0 (M=%lld K=%lld R=%lld)", (long long)M, (long long)K,
+                (long long)R);
+  if (!X || !LB || !T) return fail(RTL_ERR_NULL, "X, LB and T are required");
+  if (misaligned(X) || misaligned(LB) || misaligned(T)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (K % 64 != 0 || R % 32 != 0 || R > 128)
+    return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0, R %% 32 == 0, R <= 128 (K=%lld R=%lld)",
+                (long long)K, (long long)R);
+  const size_t tb = (size_t)M * R * 2;
+  if (overlap(T, tb, X, (size_t)M * K * 2) || overlap(T, tb, LB, (size_t)R * K * 2))
+    return fail(RTL_ERR_ARG, "T overlaps an input");
+  return hip_status(rtl::launch_lora_down_bf16(M, K, R, X, LB, T, (hipStream_t)stream), "rtl_lora_down launch");
+}
+
+rtl_status rtl_linear_fused_gemm(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
+                                 const void* W, const void* LA, const void* T, rtl_tie_rule tie, float eps, void* Y,
+                                 uint8_t* dbg_idx, float* dbg_s, void* stream) {
+  rtl_status st;
+  if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "rtl_linear_fused_gemm supports bf16 only");
+  if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
+  if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
+    return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
+                (long long)N, (long long)K, (long long)R);
+  if (!X || !W || !Y || (R > 0 && (!LA || !T))) return fail(RTL_ERR_NULL, "X, W, Y (and LA, T when R > 0) are required");
+  if (misaligned(X) || misaligned(W) || misaligned(Y) || misaligned(LA) || misaligned(T) || misaligned(dbg_idx) ||
+      misaligned(dbg_s))
+    return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (K % 64 != 0 || R % 32 != 0 || R > 128)
+    return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0, R %% 32 == 0, R <= 128 (K=%lld R=%lld)",
+                (long long)K, (long long)R);
+  if ((st = check_eps(eps)) != RTL_OK) return st;
+  const size_t yb = (size_t)M * N * 2, ib = (size_t)M * (K / 4), sb = (size_t)M * 4;
+  const void* ins[4] = {X, W, R > 0 ? LA : nullptr, R > 0 ? T : nullptr};
+  const size_t inb[4] = {(size_t)M * K * 2, (size_t)N * K * 2, (size_t)N * R * 2, (size_t)M * R * 2};
+  for (int i = 0; i < 4; i++)
+    if (overlap(Y, yb, ins[i], inb[i]) || overlap(dbg_idx, ib, ins[i], inb[i]) || overlap(dbg_s, sb, ins[i], inb[i]))
+      return fail(RTL_ERR_ARG, "an output overlaps an input");
+  if (overlap(Y, yb, dbg_idx, ib) || overlap(Y, yb, dbg_s, sb) || overlap(dbg_idx, ib, dbg_s, sb))
+    return fail(RTL_ERR_ARG, "outputs overlap each other");
+  return hip_status(rtl::launch_fused_gemm_bf16(M, N, K, R, X, W, LA, T, eps, Y, dbg_idx, dbg_s, (hipStream_t)stream),
+                    "rtl_linear_fused_gemm launch");
+}
+
+rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, const void* X, const void* W, void* Y,
+                                void* stream) {
+  rtl_status st;
+  if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0)
+    return fail(RTL_ERR_SHAPE, "need M, N, K > 0 and K %% 4 == 0 (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
+                (long long)K);
+  if (!X || !W || !Y) return fail(RTL_ERR_NULL, "X, W and Y are required");
+  if (misaligned(X) || misaligned(W) || misaligned(Y)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (dt == RTL_BF16 && K % 64 != 0) return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0 (K=%lld)", (long long)K);
+  const size_t es = elem_size(dt);
+  if (overlap(Y, (size_t)M * N * es, X, (size_t)M * K * es) || overlap(Y, (size_t)M * N * es, W, (size_t)N * K * es))
+    return fail(RTL_ERR_ARG, "Y overlaps an input");
+  hipError_t e;
+  if (dt == RTL_BF16)
+    e = rtl::launch_dense_bf16(M, N, K, X, W, Y, (hipStream_t)stream);
+  else
+    e = rtl::launch_dense_f32(M, N, K, (const float*)X, (const float*)W, (float*)Y, (hipStream_t)stream);
+  return hip_status(e, "rtl_linear_dense_ref launch");
+}
+
+}  // extern "C"

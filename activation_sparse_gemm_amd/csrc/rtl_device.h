@@ -1,0 +1,102 @@
+// rtl_device.h -- device-side helpers shared by the gfx950 kernels of the library:
+// vector types, the exact 2-of-4 selection on bf16 and fp32 bit patterns, and the
+// operand layouts of the CDNA4 matrix instructions used here.
+//
+// Matrix-instruction operand layouts (wave64, lane l, q = l / 16, r = l % 16), as
+// established for gfx950 by a lane-layout probe against a host reference:
+//  - v_mfma_f32_16x16x32_bf16: A lane holds row r, k = 8q..8q+7; B lane holds column r,
+//    k = 8q..8q+7; accumulator lane holds column r, rows 4q..4q+3.
+//  - v_smfmac_f32_16x16x64_bf16 (A 2:4-sparse): A lane holds row r and the 8 kept values
+//    of the 16 dense positions k = 16q..16q+15 (four groups of 4, two values each, in
+//    group order); value slot i takes its position within the group from bits 2i..2i+1
+//    of the selected 16-bit half of the index VGPR (abid picks the half).  B lane holds
+//    column r with values 0..7 at k = 8q..8q+7 and values 8..15 at k = 32+8q..32+8q+7.
+//    Accumulator layout as for the dense instruction.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// 2-of-4 selection on one bf16 group held as d0 = (x1 << 16 | x0), d1 = (x3 << 16 | x2).
+// Magnitudes are compared exactly as the sign-cleared 15-bit patterns; a key per position
+// carries |x_j| in bits 16..30 and (3 - j) in bits 14..15, so the larger key wins and equal
+// magnitudes favour the lower index.  The top two keys come from a max/min network.
+// Outputs: vals = (x_hi << 16 | x_lo) for kept positions lo < hi, code = lo | hi << 2.
+__device__ __forceinline__ void select_bf16(uint32_t d0, uint32_t d1, uint32_t& vals,
+                                            uint32_t& code) {
+  const uint32_t a0 = d0 & 0x7FFF7FFFu, a1 = d1 & 0x7FFF7FFFu;
+  const uint32_t k0 = (a0 << 16) | 0xC000u;
+  const uint32_t k1 = (a0 & 0x7FFF0000u) | 0x8000u;
+  const uint32_t k2 = (a1 << 16) | 0x4000u;
+  const uint32_t k3 = a1 & 0x7FFF0000u;
+  const uint32_t m01 = umax(k0, k1), n01 = umin(k0, k1);
+  const uint32_t m23 = umax(k2, k3), n23 = umin(k2, k3);
+  const uint32_t t1 = umax(m01, m23);
+  const uint32_t t2 = umax(umin(m01, m23), umax(n01, n23));
+  const uint32_t e1 = (t1 >> 14) & 3u, e2 = (t2 >> 14) & 3u;  // 3 - position
+  const uint32_t ehi = umax(e1, e2), elo = umin(e1, e2);      // lower position = larger e
+  // byte selector {2lo, 2lo+1, 2hi, 2hi+1} over the 8 bytes (d1:d0), lo = 3-ehi, hi = 3-elo
+  const uint32_t sel = 0x07060706u - (ehi | (elo << 16)) * 0x0202u;
+  vals = __builtin_amdgcn_perm(d1, d0, sel);
+  code = 15u - (ehi + 4u * elo);
+}
+
+// 2-of-4 selection on one fp32 group (magnitudes as 31-bit patterns, ties to the lower
+// index).  Writes the two kept positions lo < hi.
+__device__ __forceinline__ void select_f32(const uint32_t x[4], int& lo, int& hi) {
+  uint32_t a[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = x[j] & 0x7FFFFFFFu;
+  int kept[2] = {0, 0}, nk = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    int rank = 0;
+#pragma unroll
+    for (int l = 0; l < 4; l++)
+      if (l != j) rank += (a[l] > a[j]) || (a[l] == a[j] && l < j);
+    if (rank < 2) {
+      if (nk < 2) kept[nk] = j;
+      nk++;
+    }
+  }
+  lo = kept[0];
+  hi = kept[1];
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Squared-norm accumulation of two packed bf16 values.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace rtl

@@ -1,0 +1,123 @@
+/*
+ * rtl.h -- C ABI of the norm-compensated 2:4 activation-sparse linear layer with a
+ * low-rank (LoRA) correction branch, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("RT-Lynx: Putting the GEMM Sparsity In a Right Way for Diffusion
+ * Models", summary page, method overview):
+ *   step 1: for each token row X (length K = D_in, a multiple of 4), keep 2 of every 4
+ *           consecutive channels (Top-K by magnitude) to get X~, and rescale by
+ *           s = ||X||_2 / (||X~||_2 + eps), eps = 1e-8;
+ *   step 2: Y = s * (X~ W^T) + X (L_A L_B)^T, the low-rank branch fed with the dense X;
+ *   step 4: the selection, the compression into the 2:4 hardware layout and the sparse
+ *           product run fused in one kernel, with the low-rank product accumulated on
+ *           chip so that no M x N low-rank output reaches device memory.
+ *
+ * Shapes (row-major, contiguous):  X [M,K], W [N,K], L_B [R,K], L_A [N,R], Y [M,N].
+ * Hence X (L_A L_B)^T = (X L_B^T) L_A^T.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor arguments are DEVICE pointers, caller-owned, 16-byte aligned.  The library
+ *    keeps no pointer after a call returns and allocates no device memory.
+ *  - `dt` is the element type of X, W, L_A, L_B, Y and vals; norms, s and accumulation
+ *    are fp32 in both modes.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = default
+ *    stream) and runs asynchronously; buffers must stay alive until it completes.
+ *  - Arguments are validated synchronously.  On any error nothing is launched and no
+ *    output is written; the status says why, and rtl_last_error() gives a message.
+ *  - Selection compares magnitudes exactly (as integers on the sign-cleared bit
+ *    patterns); ties go to the lower channel index; exactly two positions are kept in
+ *    every group even when it holds fewer than two nonzeros.  Inputs must be finite.
+ *  - Thread-safe: no global mutable state apart from the thread-local error message.
+ */
+#ifndef RTL_H
+#define RTL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RTL_OK = 0,
+  RTL_ERR_NULL = 1,        /* a required pointer is NULL */
+  RTL_ERR_SHAPE = 2,       /* M, N or K <= 0, K % 4 != 0, R < 0 */
+  RTL_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned */
+  RTL_ERR_UNSUPPORTED = 4, /* tie rule, dtype, or a shape limit of the bf16 kernels */
+  RTL_ERR_ARG = 5,         /* eps negative or not finite; an output overlaps an input */
+  RTL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+  RTL_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} rtl_status;
+
+typedef enum { RTL_F32 = 0, RTL_BF16 = 1 } rtl_dtype;
+
+/* Tie rule of the 2-of-4 selection: equal magnitudes favour the lower index. */
+typedef enum { RTL_TIE_LOWER_INDEX = 0 } rtl_tie_rule;
+
+/*
+ * Selection, compression and rescale factor of every row (method step 1), standalone.
+ *   X     [M,K]    input activations (dtype dt)
+ *   vals  [M,K/2]  kept values, unscaled bit copies of X, two per group in ascending
+ *                  position order (dtype dt)
+ *   idx   [M,K/4]  per group idx0 | idx1 << 2 with idx0 < idx1 the kept positions (0..3)
+ *   s     [M]      fp32 rescale factor ||X|| / (||X~|| + eps); 0 for an all-zero row
+ * Needs K % 4 == 0.
+ */
+rtl_status rtl_sparsify(rtl_dtype dt, int64_t M, int64_t K, const void* X, rtl_tie_rule tie,
+                        float eps, void* vals, uint8_t* idx, float* s, void* stream);
+
+/* Workspace bytes rtl_linear_fused needs for this shape (0 when R == 0). */
+size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R);
+
+/*
+ * The whole layer (method steps 1, 2 and 4):
+ *   Y = s * (X~ W^T) + (X L_B^T) L_A^T
+ *   X [M,K], W [N,K], LA [N,R], LB [R,K], Y [M,N]; R == 0 drops the low-rank branch
+ *   (LA and LB may then be NULL).
+ * bf16: the selection runs in the prologue of the sparse-MFMA GEMM; the rank-R product
+ *   T = X L_B^T is a separate skinny pass into `workspace` (rounded to bf16), and the
+ *   GEMM's epilogue scales its accumulators by s and adds T L_A^T into them with one
+ *   extra K = R MFMA slice before the single bf16 store of Y.  Limits: K % 64 == 0,
+ *   R % 32 == 0, R <= 128.  M and N are arbitrary.
+ * fp32: same arithmetic in fp32 on the vector ALUs (no fp32 sparse MFMA exists).
+ * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the GEMM
+ *   writes the selection codes and s that its own prologue computed, in the layout of
+ *   rtl_sparsify.
+ * Y must not overlap any input.  Calls that share a workspace must be serialised.
+ */
+rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                            const void* X, const void* W, const void* LA, const void* LB,
+                            rtl_tie_rule tie, float eps, void* Y, void* workspace,
+                            size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream);
+
+/*
+ * The two stages of rtl_linear_fused(bf16), callable one by one (bf16 only):
+ *   rtl_lora_down:         T = X L_B^T, T [M,R] bf16 (the skinny rank-R pass);
+ *   rtl_linear_fused_gemm: Y = s * (X~ W^T) + T L_A^T with T from rtl_lora_down (the
+ *                          fused selection + sparse-MFMA kernel).
+ * Same limits, validation and dbg outputs as rtl_linear_fused; T must not overlap Y.
+ */
+rtl_status rtl_lora_down(rtl_dtype dt, int64_t M, int64_t K, int64_t R, const void* X, const void* LB,
+                         void* T, void* stream);
+rtl_status rtl_linear_fused_gemm(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                                 const void* X, const void* W, const void* LA, const void* T,
+                                 rtl_tie_rule tie, float eps, void* Y, uint8_t* dbg_idx,
+                                 float* dbg_s, void* stream);
+
+/*
+ * Dense product Y = X W^T with the same tiling as the fused kernel: the layer the sparse
+ * one replaces and the one that layers left dense keep (method step 3, selective layer
+ * skipping).  X [M,K], W [N,K], Y [M,N].  bf16 needs K % 64 == 0.
+ */
+rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, const void* X,
+                                const void* W, void* Y, void* stream);
+
+const char* rtl_status_string(rtl_status st);
+const char* rtl_last_error(void); /* message of this thread's last failed call, or "" */
+int rtl_version(void);            /* major * 10000 + minor * 100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RTL_H */

@@ -1,0 +1,172 @@
+"""The C ABI library: it loads, exports every entry point the header declares, and its
+argument validation rejects bad calls before launching anything (CPU only: every call
+here fails validation, so no kernel runs and the "device" pointers are never touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtl.h")
+
+rtl = pytest.importorskip("activation_sparse_gemm_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtl_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(rtl.EXPORTS), names
+    L = ctypes.CDLL(rtl.library_path)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert rtl.rtl_version() >= 100
+    for code in range(8):
+        assert rtl.rtl_status_string(code).startswith(rtl.STATUS[code])
+
+
+def test_workspace_bytes():
+    W = rtl.rtl_linear_fused_workspace_bytes
+    assert W(rtl.RTL_BF16, 4096, 3072, 3072, 0) == 0
+    need = W(rtl.RTL_BF16, 4096, 3072, 3072, 64)
+    assert need >= 4096 * 64 * 2 and need % 256 == 0
+    assert W(rtl.RTL_BF16, 0, 3072, 3072, 64) == 0
+
+
+class Host:
+    """Host buffers standing in for device pointers: never dereferenced, because every
+    call below fails validation first.  Used to check that outputs stay untouched."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def buf(self, nbytes, fill=0xAB):
+        a = np.full(nbytes + 64, fill, np.uint8)
+        self.bufs.append(a)
+        base = a.ctypes.data
+        off = (-base) % 16
+        return ctypes.c_void_p(base + off), a
+
+    def untouched(self):
+        return all((a == a[0]).all() for a in self.bufs)
+
+
+def call_sparsify(dt=rtl.RTL_BF16, M=8, K=64, tie=0, eps=1e-8, **over):
+    h = Host()
+    X, _ = h.buf(M * max(K, 4) * 4)
+    vals, _ = h.buf(M * max(K, 4) * 2)
+    idx, _ = h.buf(M * max(K, 4))
+    s, _ = h.buf(M * 4 + 16)
+    args = dict(X=X, vals=vals, idx=idx, s=s)
+    args.update(over)
+    st = rtl.lib.rtl_sparsify(dt, M, K, args["X"], tie, eps, args["vals"], args["idx"], args["s"], None)
+    return st, h
+
+
+def test_sparsify_rejects_bad_calls():
+    E = rtl.STATUS
+    inv = {v: k for k, v in E.items()}
+    cases = [
+        (dict(K=6), "RTL_ERR_SHAPE"),
+        (dict(M=0), "RTL_ERR_SHAPE"),
+        (dict(K=0), "RTL_ERR_SHAPE"),
+        (dict(tie=1), "RTL_ERR_UNSUPPORTED"),
+        (dict(dt=7), "RTL_ERR_UNSUPPORTED"),
+        (dict(eps=-1.0), "RTL_ERR_ARG"),
+        (dict(eps=float("nan")), "RTL_ERR_ARG"),
+        (dict(eps=float("inf")), "RTL_ERR_ARG"),
+        (dict(X=None), "RTL_ERR_NULL"),
+        (dict(s=None), "RTL_ERR_NULL"),
+    ]
+    for over, want in cases:
+        st, h = call_sparsify(**over)
+        assert st == inv[want], (over, E.get(st))
+        assert h.untouched()
+        assert rtl.lib.rtl_last_error().decode() != ""
+
+
+def test_sparsify_rejects_misaligned_and_aliased():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    h = Host()
+    X, _ = h.buf(8 * 64 * 2)
+    st, _ = call_sparsify(X=ctypes.c_void_p(X.value + 2))
+    assert st == inv["RTL_ERR_ALIGN"]
+    st, _ = call_sparsify(vals=X, X=X)  # output aliases input
+    assert st == inv["RTL_ERR_ARG"]
+
+
+def call_fused(dt=rtl.RTL_BF16, M=64, N=64, K=128, R=32, tie=0, eps=1e-8, ws_bytes=None, **over):
+    h = Host()
+    es = 2 if dt == rtl.RTL_BF16 else 4
+    X, _ = h.buf(M * K * es)
+    W, _ = h.buf(N * K * es)
+    LA, _ = h.buf(max(N * R * es, 16))
+    LB, _ = h.buf(max(R * K * es, 16))
+    Y, _ = h.buf(M * N * es)
+    need = rtl.rtl_linear_fused_workspace_bytes(dt if dt in (0, 1) else 1, max(M, 1), max(N, 1), max(K, 1), max(R, 0))
+    ws, _ = h.buf(max(need, 16))
+    args = dict(X=X, W=W, LA=LA, LB=LB, Y=Y, ws=ws)
+    args.update(over)
+    st = rtl.lib.rtl_linear_fused(dt, M, N, K, R, args["X"], args["W"], args["LA"], args["LB"], tie, eps, args["Y"],
+                                  args["ws"], need if ws_bytes is None else ws_bytes, None, None, None)
+    return st, h
+
+
+def test_fused_rejects_bad_calls():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    cases = [
+        (dict(K=130), "RTL_ERR_SHAPE"),
+        (dict(N=0), "RTL_ERR_SHAPE"),
+        (dict(R=-1), "RTL_ERR_SHAPE"),
+        (dict(K=100), "RTL_ERR_UNSUPPORTED"),   # bf16 needs K % 64 == 0
+        (dict(R=48), "RTL_ERR_UNSUPPORTED"),    # bf16 needs R % 32 == 0
+        (dict(R=160), "RTL_ERR_UNSUPPORTED"),   # R <= 128
+        (dict(tie=2), "RTL_ERR_UNSUPPORTED"),
+        (dict(eps=-1e-8), "RTL_ERR_ARG"),
+        (dict(W=None), "RTL_ERR_NULL"),
+        (dict(LB=None), "RTL_ERR_NULL"),
+        (dict(ws_bytes=16), "RTL_ERR_WORKSPACE"),
+        (dict(ws=None), "RTL_ERR_WORKSPACE"),
+    ]
+    for over, want in cases:
+        st, h = call_fused(**over)
+        assert st == inv[want], (over, rtl.STATUS.get(st))
+        assert h.untouched()
+
+
+def test_fused_rejects_aliasing():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    h = Host()
+    X, _ = h.buf(64 * 128 * 2)
+    st, _ = call_fused(X=X, Y=X)
+    assert st == inv["RTL_ERR_ARG"]
+    st, _ = call_fused(W=X, ws=X)
+    assert st == inv["RTL_ERR_ARG"]
+
+
+def test_dense_rejects_bad_calls():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    h = Host()
+    X, _ = h.buf(64 * 128 * 4)
+    Y, _ = h.buf(64 * 64 * 4)
+    assert rtl.lib.rtl_linear_dense_ref(rtl.RTL_BF16, 64, 64, 96, X, X, Y, None) == inv["RTL_ERR_UNSUPPORTED"]
+    assert rtl.lib.rtl_linear_dense_ref(rtl.RTL_BF16, 64, 64, 128, X, None, Y, None) == inv["RTL_ERR_NULL"]
+    assert rtl.lib.rtl_linear_dense_ref(rtl.RTL_F32, 64, 64, 126, X, X, Y, None) == inv["RTL_ERR_SHAPE"]
+    assert rtl.lib.rtl_linear_dense_ref(rtl.RTL_F32, 64, 64, 128, X, X, X, None) == inv["RTL_ERR_ARG"]
+    assert h.untouched()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    X = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rtl.rtl_sparsify(X, vals=X, idx=X, s=X)

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Selection codes and kept values are compared bit for bit; s within TOL_S; Y within the
+contract tolerance (max row relative error 2e-2 in bf16, 1e-4 in fp32).  Small shapes
+are compared in full and span several tiles plus ragged tails; the workload layers run
+at their full sizes in the launch configuration the benchmark times, with every row's
+selection compared and a sample of output rows checked against the oracle row by row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import TOL_Y, tol_s, f64, layer, log, row_rel_err, sample_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+rtl = pytest.importorskip("activation_sparse_gemm_amd")
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ------------------------------------------------------------------ rtl_sparsify
+
+def check_sparsify(d, tag):
+    M, K, dt = d["M"], d["K"], d["dtype"]
+    log(f"[sparsify] {tag} M={M} K={K} {dt}")
+    Xd = to_dev(d["X"])
+    vals, idx, s = rtl.rtl_sparsify(Xd)
+    torch.cuda.synchronize()
+    ref = oracle.sparsify(d["X"])
+    gi, gv, gs = to_host(idx), to_host(vals), to_host(s)
+    bad = np.argwhere(gi != ref["idx"])
+    assert bad.size == 0, f"idx mismatch at {bad[:5].tolist()}"
+    assert np.array_equal(gv.view(np.uint16 if dt == "bf16" else np.uint32),
+                          ref["vals"].view(np.uint16 if dt == "bf16" else np.uint32)), "vals mismatch"
+    zero = ref["s"] == 0
+    assert np.all(gs[zero] == 0)
+    rel = np.abs(gs[~zero] - ref["s"][~zero]) / ref["s"][~zero]
+    assert rel.max(initial=0) <= tol_s(K), rel.max()
+    return gi
+
+
+@pytest.mark.parametrize("shape", [(37, 208), (64, 256), (5, 100), (1, 4), (130, 3072)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sparsify_small(shape, dt):
+    M, K = shape
+    lay = synth.Layer("t", M, K, 16, 0, dt, "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=900 + M + K)
+    check_sparsify(d, f"heavy{shape}")
+
+
+def test_sparsify_tiny_ties_and_zero_rows():
+    check_sparsify(layer("tiny"), "tiny")
+
+
+@pytest.mark.parametrize("name", ["attn_proj", "fused_qkv", "mlp_up", "mlp_down", "video_up", "video_down"])
+def test_sparsify_workload_layers(name):
+    check_sparsify(layer(name), name)
+
+
+def test_sparsify_two_of_four_input_is_fixed_point():
+    M, K = 64, 512
+    X = synth.normal(42, (M, K))
+    for i in range(M):
+        for g in range(K // 4):
+            X[i, 4 * g + synth.choose(100000 + i * K + g, 4, 2)] = 0.0
+    Xb = synth.to_bf16(X)
+    vals, idx, s = rtl.rtl_sparsify(to_dev(Xb))
+    nz = Xb.reshape(M, -1)[Xb.reshape(M, -1) & 0x7FFF != 0].reshape(M, -1)
+    assert np.array_equal(to_host(vals), nz)  # the kept values are exactly the nonzeros
+    assert np.allclose(to_host(s), 1.0, rtol=2e-6, atol=0)  # same terms, different pairing
+
+
+# ------------------------------------------------------------------ rtl_linear_fused
+
+def run_fused(d, with_dbg=True):
+    M, K, N, R = d["M"], d["K"], d["N"], d["R"]
+    dev = {k: to_dev(d[k]) for k in ("X", "W", "LA", "LB")}
+    dbg_idx = torch.empty((M, K // 4), dtype=torch.uint8, device="cuda") if with_dbg else None
+    dbg_s = torch.empty((M,), dtype=torch.float32, device="cuda") if with_dbg else None
+    Y = rtl.rtl_linear_fused(dev["X"], dev["W"], dev["LA"], dev["LB"], dbg_idx=dbg_idx, dbg_s=dbg_s)
+    torch.cuda.synchronize()
+    return Y, dbg_idx, dbg_s
+
+
+def check_fused_full(d, tag):
+    dt = d["dtype"]
+    log(f"[fused] {tag} M={d['M']} N={d['N']} K={d['K']} R={d['R']} {dt}")
+    Y, dbg_idx, dbg_s = run_fused(d)
+    Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"])
+    err = row_rel_err(f64(to_host(Y), dt), Yref)
+    log(f"  max row rel err {err:.3e}")
+    assert err <= TOL_Y[dt], err
+    ref = oracle.sparsify(d["X"])
+    assert np.array_equal(to_host(dbg_idx), ref["idx"])
+    gs = to_host(dbg_s)
+    zero = sref == 0
+    assert np.all(gs[zero] == 0)
+    assert np.all(np.abs(gs[~zero] - sref[~zero]) <= tol_s(d['K']) * sref[~zero])
+    return err
+
+
+FUSED_SMALL = [
+    # M, N, K, R, dtype: several 256 x 256 tiles plus ragged M and N tails
+    (300, 520, 192, 64, "bf16"),
+    (512, 256, 256, 32, "bf16"),
+    (37, 300, 128, 128, "bf16"),
+    (1, 16, 64, 64, "bf16"),
+    (260, 272, 64, 0, "bf16"),
+    (64, 256, 256, 8, "f32"),
+    (50, 70, 36, 5, "f32"),
+    (33, 40, 64, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_SMALL, ids=lambda c: "x".join(map(str, c)))
+def test_fused_small(case):
+    M, N, K, R, dt = case
+    lay = synth.Layer("t", M, K, N, R, dt, "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=700 + M + N + K + R)
+    check_fused_full(d, "heavy")
+
+
+def test_fused_tiny_config():
+    err = check_fused_full(layer("tiny"), "tiny")
+    assert err <= 1e-4
+
+
+def test_fused_zero_rows_are_exact_and_runs_are_deterministic():
+    lay = synth.Layer("t", 300, 256, 384, 64, "bf16", "heavy", 0.08)
+    d = dict(synth.make_layer(lay, seed_base=4242))
+    X = d["X"].copy()
+    X[[0, 17, 255, 256, 299]] = 0
+    d["X"] = X
+    Y1, _, s1 = run_fused(d)
+    Y2, _, s2 = run_fused(d)
+    y1, y2 = to_host(Y1), to_host(Y2)
+    assert np.array_equal(y1, y2) and np.array_equal(to_host(s1), to_host(s2))
+    assert np.all(y1[[0, 17, 255, 256, 299]] == 0)
+
+
+@pytest.mark.parametrize("name", ["attn_proj", "fused_qkv", "mlp_up", "mlp_down", "video_up", "video_down"])
+def test_fused_workload_layers(name):
+    d = layer(name)
+    M = d["M"]
+    log(f"[fused-full] {name} M={M} N={d['N']} K={d['K']} R={d['R']}")
+    Y, dbg_idx, dbg_s = run_fused(d)
+    ref = oracle.sparsify(d["X"])
+    assert np.array_equal(to_host(dbg_idx), ref["idx"])
+    rows = sample_rows(M)
+    Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+    y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
+    err = row_rel_err(y, Yref)
+    log(f"  sampled {len(rows)} rows, max row rel err {err:.3e}")
+    assert err <= TOL_Y["bf16"]
+    gs = to_host(dbg_s)
+    nz = ref["s"] > 0
+    assert np.all(np.abs(gs[nz] - ref["s"][nz]) <= tol_s(d['K']) * ref["s"][nz])
+
+
+# ------------------------------------------------------------------ rtl_linear_dense_ref
+
+@pytest.mark.parametrize("case", [(300, 520, 192, "bf16"), (1, 16, 64, "bf16"), (64, 256, 256, "f32"),
+                                  (50, 70, 36, "f32")], ids=lambda c: "x".join(map(str, c)))
+def test_dense_small(case):
+    M, N, K, dt = case
+    lay = synth.Layer("t", M, K, N, 0, dt, "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=800 + M + N + K)
+    log(f"[dense] M={M} N={N} K={K} {dt}")
+    Y = rtl.rtl_linear_dense_ref(to_dev(d["X"]), to_dev(d["W"]))
+    torch.cuda.synchronize()
+    err = row_rel_err(f64(to_host(Y), dt), oracle.dense(d["X"], d["W"]))
+    log(f"  max row rel err {err:.3e}")
+    assert err <= TOL_Y[dt]
+
+
+@pytest.mark.parametrize("name", ["attn_proj", "mlp_down", "video_oproj"])
+def test_dense_workload_layers(name):
+    d = layer(name)
+    log(f"[dense-full] {name} M={d['M']} N={d['N']} K={d['K']}")
+    Y = rtl.rtl_linear_dense_ref(to_dev(d["X"]), to_dev(d["W"]))
+    torch.cuda.synchronize()
+    rows = sample_rows(d["M"])
+    y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
+    err = row_rel_err(y, oracle.dense(d["X"], d["W"], rows=rows))
+    log(f"  sampled {len(rows)} rows, max row rel err {err:.3e}")
+    assert err <= TOL_Y["bf16"]
+
+
+# ------------------------------------------------------------------ error paths on the device
+
+def test_validation_leaves_outputs_untouched():
+    X = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")  # K % 64 != 0
+    W = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")
+    Y = torch.full((64, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rtl.RtlError) as ei:
+        rtl.rtl_linear_fused(X, W, None, None, Y=Y)
+    assert ei.value.status == 4
+    torch.cuda.synchronize()
+    assert torch.all(Y == 7.0)
