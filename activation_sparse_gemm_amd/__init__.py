@@ -20,8 +20,9 @@ import torch
 
 __all__ = [
     "RTL_F32", "RTL_BF16", "RTL_TIE_LOWER_INDEX", "EPS", "RtlError", "lib", "library_path",
-    "rtl_sparsify", "rtl_linear_fused", "rtl_linear_fused_workspace_bytes", "rtl_lora_down",
-    "rtl_linear_fused_gemm", "rtl_linear_dense_ref",
+    "rtl_sparsify", "rtl_linear_fused", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused_ex",
+    "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref",
+    "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
     "rtl_status_string", "rtl_version",
 ]
 
@@ -30,13 +31,15 @@ library_path = os.path.join(_PKG, "librtl.so")
 
 RTL_F32, RTL_BF16 = 0, 1
 RTL_TIE_LOWER_INDEX = 0
+RTL_VARIANT_AUTO, RTL_VARIANT_PROLOGUE, RTL_VARIANT_PRECOMPRESSED = 0, 1, 2
 EPS = 1e-8
 STATUS = {0: "RTL_OK", 1: "RTL_ERR_NULL", 2: "RTL_ERR_SHAPE", 3: "RTL_ERR_ALIGN", 4: "RTL_ERR_UNSUPPORTED",
           5: "RTL_ERR_ARG", 6: "RTL_ERR_WORKSPACE", 7: "RTL_ERR_HIP"}
 
 # Every entry point include/rtl.h declares.
-EXPORTS = ["rtl_sparsify", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused", "rtl_lora_down",
-           "rtl_linear_fused_gemm", "rtl_linear_dense_ref", "rtl_status_string", "rtl_last_error", "rtl_version"]
+EXPORTS = ["rtl_sparsify", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused", "rtl_linear_fused_ex",
+           "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref", "rtl_status_string",
+           "rtl_last_error", "rtl_version"]
 
 
 class RtlError(RuntimeError):
@@ -56,10 +59,12 @@ def _load() -> ctypes.CDLL:
     L.rtl_linear_fused_workspace_bytes.restype = sz
     L.rtl_linear_fused.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, sz, p, p, p]
     L.rtl_linear_fused.restype = i32
-    L.rtl_lora_down.argtypes = [i32, i64, i64, i64, p, p, p, p]
-    L.rtl_lora_down.restype = i32
-    L.rtl_linear_fused_gemm.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, p, p]
-    L.rtl_linear_fused_gemm.restype = i32
+    L.rtl_linear_fused_ex.argtypes = [i32, i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, sz, p, p, p]
+    L.rtl_linear_fused_ex.restype = i32
+    L.rtl_linear_fused_prep.argtypes = [i32, i32, i64, i64, i64, i64, p, p, i32, f32, p, sz, p, p, p]
+    L.rtl_linear_fused_prep.restype = i32
+    L.rtl_linear_fused_main.argtypes = [i32, i32, i64, i64, i64, i64, p, p, p, i32, f32, p, p, sz, p, p, p]
+    L.rtl_linear_fused_main.restype = i32
     L.rtl_linear_dense_ref.argtypes = [i32, i64, i64, i64, p, p, p, p]
     L.rtl_linear_dense_ref.restype = i32
     L.rtl_status_string.argtypes = [i32]
@@ -132,48 +137,55 @@ def rtl_linear_fused_workspace_bytes(dtype: int, M: int, N: int, K: int, R: int)
     return int(lib.rtl_linear_fused_workspace_bytes(dtype, M, N, K, R))
 
 
+def _workspace(dt, M, N, K, R, workspace, device):
+    need = rtl_linear_fused_workspace_bytes(dt, M, N, K, R)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=device)
+    return workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
 def rtl_linear_fused(X: torch.Tensor, W: torch.Tensor, LA, LB, tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS,
-                     Y=None, workspace=None, dbg_idx=None, dbg_s=None, stream=None) -> torch.Tensor:
+                     Y=None, workspace=None, dbg_idx=None, dbg_s=None, stream=None,
+                     variant: int = RTL_VARIANT_AUTO) -> torch.Tensor:
     """Y = s * (X~ W^T) + (X L_B^T) L_A^T.  X [M,K], W [N,K], LA [N,R], LB [R,K] (LA/LB None: R = 0).
 
     ``workspace`` (a uint8 tensor) is allocated when not given; pass one to keep the call
     free of allocations.  ``dbg_idx`` [M,K/4] uint8 and ``dbg_s`` [M] float32 receive the
-    selection codes and s computed inside the kernel."""
+    selection codes and s computed inside the kernels.  ``variant`` picks where the bf16
+    path selects (RTL_VARIANT_*; rtl_linear_fused_ex in the C ABI)."""
     M, K = X.shape
     N = W.shape[0]
     R = 0 if LB is None else LB.shape[0]
     dt = _dt(X)
     if Y is None:
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    need = rtl_linear_fused_workspace_bytes(dt, M, N, K, R)
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.rtl_linear_fused(dt, M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
-                                _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
+    workspace, ws_bytes = _workspace(dt, M, N, K, R, workspace, X.device)
+    _check(lib.rtl_linear_fused_ex(variant, dt, M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
+                                   _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
     return Y
 
 
-def rtl_lora_down(X: torch.Tensor, LB: torch.Tensor, T=None, stream=None) -> torch.Tensor:
-    """T = X L_B^T, [M,R] bf16: the skinny rank-R stage of rtl_linear_fused."""
+def rtl_linear_fused_prep(X: torch.Tensor, LB, N: int, workspace: torch.Tensor, variant: int = RTL_VARIANT_AUTO,
+                          tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS, dbg_idx=None, dbg_s=None, stream=None):
+    """First launch of the bf16 layer: the pre-pass over X into ``workspace``."""
     M, K = X.shape
-    R = LB.shape[0]
-    if T is None:
-        T = torch.empty((M, R), dtype=X.dtype, device=X.device)
-    _check(lib.rtl_lora_down(_dt(X), M, K, R, _ptr(X), _ptr(LB), _ptr(T), _stream(stream)))
-    return T
+    R = 0 if LB is None else LB.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.rtl_linear_fused_prep(variant, _dt(X), M, N, K, R, _ptr(X), _ptr(LB), tie, eps, _ptr(workspace),
+                                     ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
 
 
-def rtl_linear_fused_gemm(X: torch.Tensor, W: torch.Tensor, LA, T, tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS,
-                          Y=None, dbg_idx=None, dbg_s=None, stream=None) -> torch.Tensor:
-    """Y = s * (X~ W^T) + T L_A^T with T from rtl_lora_down: the fused GEMM stage."""
+def rtl_linear_fused_main(X: torch.Tensor, W: torch.Tensor, LA, R: int, workspace: torch.Tensor,
+                          variant: int = RTL_VARIANT_AUTO, tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS, Y=None,
+                          dbg_idx=None, dbg_s=None, stream=None) -> torch.Tensor:
+    """Second launch of the bf16 layer: the sparse-MFMA GEMM and its epilogue."""
     M, K = X.shape
     N = W.shape[0]
-    R = 0 if T is None else T.shape[1]
     if Y is None:
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    _check(lib.rtl_linear_fused_gemm(_dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(T), tie, eps, _ptr(Y),
-                                     _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.rtl_linear_fused_main(variant, _dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), tie, eps, _ptr(Y),
+                                     _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
     return Y
 
 

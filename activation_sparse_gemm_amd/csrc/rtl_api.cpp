@@ -105,23 +105,36 @@ size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int6
   return 0;
 }
 
-rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
-                            const void* W, const void* LA, const void* LB, rtl_tie_rule tie, float eps, void* Y,
-                            void* workspace, size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum Stage { kWhole = 0, kPrep = 1, kMain = 2 };
+
+// Validation shared by rtl_linear_fused{,_ex,_prep,_main}.  Pointers a stage does not use
+// are ignored (prep: W, LA, Y; main: LB).
+rtl_status check_fused(Stage stage, rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                       const void* X, const void* W, const void* LA, const void* LB, rtl_tie_rule tie, float eps,
+                       const void* Y, const void* ws, size_t ws_bytes, const void* dbg_idx, const void* dbg_s) {
   rtl_status st;
   if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (variant != RTL_VARIANT_AUTO && variant != RTL_VARIANT_PROLOGUE && variant != RTL_VARIANT_PRECOMPRESSED)
+    return fail(RTL_ERR_UNSUPPORTED, "unsupported variant %d", (int)variant);
+  if (stage != kWhole && dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "the split launches are bf16 only");
   if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
   if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
     return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
                 (long long)N, (long long)K, (long long)R);
-  if (!X || !W || !Y || (R > 0 && (!LA || !LB))) return fail(RTL_ERR_NULL, "X, W, Y (and LA, LB when R > 0) are required");
-  if (misaligned(X) || misaligned(W) || misaligned(Y) || misaligned(LA) || misaligned(LB) || misaligned(workspace) ||
-      misaligned(dbg_idx) || misaligned(dbg_s))
+  const bool uses_w = stage != kPrep, uses_lb = stage != kMain;
+  if (!X || (uses_w && (!W || !Y)) || (R > 0 && ((uses_w && !LA) || (uses_lb && !LB))))
+    return fail(RTL_ERR_NULL, "X, W, Y (and LA, LB when R > 0) are required");
+  if (misaligned(X) || (uses_w && (misaligned(W) || misaligned(Y) || misaligned(LA))) || (uses_lb && misaligned(LB)) ||
+      misaligned(ws) || misaligned(dbg_idx) || misaligned(dbg_s))
     return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (dt == RTL_BF16) {
     if (K % 64 != 0) return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0 (K=%lld)", (long long)K);
-    if (R % 32 != 0 || R > 128) return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs R %% 32 == 0 and R <= 128 (R=%lld)",
-                                            (long long)R);
+    if (R % 32 != 0 || R > 128)
+      return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs R %% 32 == 0 and R <= 128 (R=%lld)", (long long)R);
   } else if (R > 128) {
     return fail(RTL_ERR_UNSUPPORTED, "fp32 path needs R <= 128 (R=%lld)", (long long)R);
   }
@@ -129,75 +142,72 @@ rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64
   const size_t es = elem_size(dt);
   const size_t xb = (size_t)M * K * es, wb = (size_t)N * K * es, lab = (size_t)N * R * es, lbb = (size_t)R * K * es;
   const size_t yb = (size_t)M * N * es, ib = (size_t)M * (K / 4), sb = (size_t)M * 4;
-  const void* ins[4] = {X, W, R > 0 ? LA : nullptr, R > 0 ? LB : nullptr};
-  const size_t inb[4] = {xb, wb, lab, lbb};
   const size_t need = rtl_linear_fused_workspace_bytes(dt, M, N, K, R);
+  const void* ins[4] = {X, uses_w ? W : nullptr, (R > 0 && uses_w) ? LA : nullptr, (R > 0 && uses_lb) ? LB : nullptr};
+  const size_t inb[4] = {xb, wb, lab, lbb};
+  const void* Yc = uses_w ? Y : nullptr;
   for (int i = 0; i < 4; i++) {
-    if (overlap(Y, yb, ins[i], inb[i]) || overlap(dbg_idx, ib, ins[i], inb[i]) || overlap(dbg_s, sb, ins[i], inb[i]) ||
-        overlap(workspace, need, ins[i], inb[i]))
+    if (overlap(Yc, yb, ins[i], inb[i]) || overlap(dbg_idx, ib, ins[i], inb[i]) || overlap(dbg_s, sb, ins[i], inb[i]) ||
+        overlap(ws, need, ins[i], inb[i]))
       return fail(RTL_ERR_ARG, "an output or the workspace overlaps an input");
   }
-  if (overlap(Y, yb, dbg_idx, ib) || overlap(Y, yb, dbg_s, sb) || overlap(dbg_idx, ib, dbg_s, sb) ||
-      overlap(workspace, need, Y, yb) || overlap(workspace, need, dbg_idx, ib) || overlap(workspace, need, dbg_s, sb))
+  if (overlap(Yc, yb, dbg_idx, ib) || overlap(Yc, yb, dbg_s, sb) || overlap(dbg_idx, ib, dbg_s, sb) ||
+      overlap(ws, need, Yc, yb) || overlap(ws, need, dbg_idx, ib) || overlap(ws, need, dbg_s, sb))
     return fail(RTL_ERR_ARG, "outputs overlap each other or the workspace");
-  if (need > 0 && (!workspace || ws_bytes < need))
-    return fail(RTL_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(RTL_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+  return RTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rtl_status rtl_linear_fused_ex(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                               const void* X, const void* W, const void* LA, const void* LB, rtl_tie_rule tie,
+                               float eps, void* Y, void* workspace, size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s,
+                               void* stream) {
+  rtl_status st = check_fused(kWhole, variant, dt, M, N, K, R, X, W, LA, LB, tie, eps, Y, workspace, ws_bytes,
+                              dbg_idx, dbg_s);
+  if (st != RTL_OK) return st;
   hipError_t e;
   if (dt == RTL_BF16)
-    e = rtl::launch_fused_bf16(M, N, K, R, X, W, LA, LB, eps, Y, workspace, dbg_idx, dbg_s, (hipStream_t)stream);
+    e = rtl::launch_fused_bf16((int)variant, M, N, K, R, X, W, LA, LB, eps, Y, workspace, dbg_idx, dbg_s,
+                               (hipStream_t)stream);
   else
     e = rtl::launch_fused_f32(M, N, K, R, (const float*)X, (const float*)W, (const float*)LA, (const float*)LB, eps,
                               (float*)Y, workspace, dbg_idx, dbg_s, (hipStream_t)stream);
   return hip_status(e, "rtl_linear_fused launch");
 }
 
-rtl_status rtl_lora_down(rtl_dtype dt, int64_t M, int64_t K, int64_t R, const void* X, const void* LB, void* T,
-                         void* stream) {
-  rtl_status st;
-  if ((st = check_dtype(dt)) != RTL_OK) return st;
-  if (dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "rtl_lora_down supports bf16 only");
-  if (M <= 0 || K <= 0 || K % 4 != 0 || R <= 0)
-    return fail(RTL_ERR_SHAPE, "need M, K, R > 0 and K %% 4 == 0 (M=%lld K=%lld R=%lld)", (long long)M, (long long)K,
-                (long long)R);
-  if (!X || !LB || !T) return fail(RTL_ERR_NULL, "X, LB and T are required");
-  if (misaligned(X) || misaligned(LB) || misaligned(T)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  if (K % 64 != 0 || R % 32 != 0 || R > 128)
-    return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0, R %% 32 == 0, R <= 128 (K=%lld R=%lld)",
-                (long long)K, (long long)R);
-  const size_t tb = (size_t)M * R * 2;
-  if (overlap(T, tb, X, (size_t)M * K * 2) || overlap(T, tb, LB, (size_t)R * K * 2))
-    return fail(RTL_ERR_ARG, "T overlaps an input");
-  return hip_status(rtl::launch_lora_down_bf16(M, K, R, X, LB, T, (hipStream_t)stream), "rtl_lora_down launch");
+rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,
+                            const void* LA, const void* LB, rtl_tie_rule tie, float eps, void* Y, void* workspace,
+                            size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream) {
+  return rtl_linear_fused_ex(RTL_VARIANT_AUTO, dt, M, N, K, R, X, W, LA, LB, tie, eps, Y, workspace, ws_bytes, dbg_idx,
+                             dbg_s, stream);
 }
 
-rtl_status rtl_linear_fused_gemm(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
-                                 const void* W, const void* LA, const void* T, rtl_tie_rule tie, float eps, void* Y,
-                                 uint8_t* dbg_idx, float* dbg_s, void* stream) {
-  rtl_status st;
-  if ((st = check_dtype(dt)) != RTL_OK) return st;
-  if (dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "rtl_linear_fused_gemm supports bf16 only");
-  if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
-  if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
-    return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
-                (long long)N, (long long)K, (long long)R);
-  if (!X || !W || !Y || (R > 0 && (!LA || !T))) return fail(RTL_ERR_NULL, "X, W, Y (and LA, T when R > 0) are required");
-  if (misaligned(X) || misaligned(W) || misaligned(Y) || misaligned(LA) || misaligned(T) || misaligned(dbg_idx) ||
-      misaligned(dbg_s))
-    return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  if (K % 64 != 0 || R % 32 != 0 || R > 128)
-    return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0, R %% 32 == 0, R <= 128 (K=%lld R=%lld)",
-                (long long)K, (long long)R);
-  if ((st = check_eps(eps)) != RTL_OK) return st;
-  const size_t yb = (size_t)M * N * 2, ib = (size_t)M * (K / 4), sb = (size_t)M * 4;
-  const void* ins[4] = {X, W, R > 0 ? LA : nullptr, R > 0 ? T : nullptr};
-  const size_t inb[4] = {(size_t)M * K * 2, (size_t)N * K * 2, (size_t)N * R * 2, (size_t)M * R * 2};
-  for (int i = 0; i < 4; i++)
-    if (overlap(Y, yb, ins[i], inb[i]) || overlap(dbg_idx, ib, ins[i], inb[i]) || overlap(dbg_s, sb, ins[i], inb[i]))
-      return fail(RTL_ERR_ARG, "an output overlaps an input");
-  if (overlap(Y, yb, dbg_idx, ib) || overlap(Y, yb, dbg_s, sb) || overlap(dbg_idx, ib, dbg_s, sb))
-    return fail(RTL_ERR_ARG, "outputs overlap each other");
-  return hip_status(rtl::launch_fused_gemm_bf16(M, N, K, R, X, W, LA, T, eps, Y, dbg_idx, dbg_s, (hipStream_t)stream),
-                    "rtl_linear_fused_gemm launch");
+rtl_status rtl_linear_fused_prep(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                                 const void* X, const void* LB, rtl_tie_rule tie, float eps, void* workspace,
+                                 size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream) {
+  rtl_status st = check_fused(kPrep, variant, dt, M, N, K, R, X, nullptr, nullptr, LB, tie, eps, nullptr, workspace,
+                              ws_bytes, dbg_idx, dbg_s);
+  if (st != RTL_OK) return st;
+  return hip_status(rtl::launch_prep_bf16((int)variant, M, N, K, R, X, LB, eps, workspace, dbg_idx, dbg_s,
+                                          (hipStream_t)stream),
+                    "rtl_linear_fused_prep launch");
+}
+
+rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                                 const void* X, const void* W, const void* LA, rtl_tie_rule tie, float eps, void* Y,
+                                 const void* workspace, size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s,
+                                 void* stream) {
+  rtl_status st = check_fused(kMain, variant, dt, M, N, K, R, X, W, LA, nullptr, tie, eps, Y, workspace, ws_bytes,
+                              dbg_idx, dbg_s);
+  if (st != RTL_OK) return st;
+  return hip_status(rtl::launch_main_bf16((int)variant, M, N, K, R, X, W, LA, eps, Y, workspace, dbg_idx, dbg_s,
+                                          (hipStream_t)stream),
+                    "rtl_linear_fused_main launch");
 }
 
 rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, const void* X, const void* W, void* Y,

@@ -13,18 +13,21 @@ constexpr int kDtBF16 = 1;
 hipError_t launch_sparsify(int dt, int64_t M, int64_t K, const void* X, float eps, void* vals,
                            uint8_t* idx, float* s, hipStream_t stream);
 
-// bf16 path
+// bf16 path.  Variants of the fused layer: the 2-of-4 selection in the GEMM's A-operand
+// prologue, or in the pre-pass over X with the GEMM reading the compressed operand.
+constexpr int kVariantAuto = 0, kVariantPrologue = 1, kVariantPrecompressed = 2;
+int resolve_variant_bf16(int variant, int64_t M, int64_t N, int64_t K);
 size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R);
-hipError_t launch_fused_bf16(int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
-                             const void* W, const void* LA, const void* LB, float eps, void* Y,
-                             void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream);
-hipError_t launch_lora_down_bf16(int64_t M, int64_t K, int64_t R, const void* X, const void* LB, void* T,
-                                 hipStream_t stream);
-hipError_t launch_fused_gemm_bf16(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,
-                                  const void* LA, const void* T, float eps, void* Y, uint8_t* dbg_idx, float* dbg_s,
-                                  hipStream_t stream);
-hipError_t launch_dense_bf16(int64_t M, int64_t N, int64_t K, const void* X, const void* W,
-                             void* Y, hipStream_t stream);
+hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
+                            float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream);
+hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,
+                            const void* LA, float eps, void* Y, const void* ws, uint8_t* dbg_idx, float* dbg_s,
+                            hipStream_t stream);
+hipError_t launch_fused_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,
+                             const void* LA, const void* LB, float eps, void* Y, void* ws, uint8_t* dbg_idx,
+                             float* dbg_s, hipStream_t stream);
+hipError_t launch_dense_bf16(int64_t M, int64_t N, int64_t K, const void* X, const void* W, void* Y,
+                             hipStream_t stream);
 
 // fp32 path
 size_t fused_f32_workspace(int64_t M, int64_t N, int64_t K, int64_t R);

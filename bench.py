@@ -26,7 +26,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_DENSE = 2.5e15   # MI355X dense bf16 MFMA FLOP/s (published)
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s (published)
-DOMINANT = "gemm_bf16_kernel<256, true>"  # the fused selection + sparse-MFMA kernel
 KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/rtl_device.h"]
 
 
@@ -38,10 +37,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(layer: str):
+def stored_traffic(layer: str, variant: str):
     """HBM bytes per launch of the dominant kernel from the committed counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_fused_gemm_{layer}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{variant}_{layer}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -93,7 +92,12 @@ def cpu_baseline(d, target_s: float):
             "sample": f"{nrows} of {M} rows (evenly spaced), full N={N} and K={K}, fp64, {dt:.1f} s"}
 
 
-def bench_layer(name: str, steps: int, warmup: int):
+VARIANTS = {"prologue": 1, "precompressed": 2}
+
+
+def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "precompressed")):
+    """Times (seconds per call) of the whole layer per variant, of its two launches alone,
+    and of the dense GEMM of the same shape."""
     import torch
 
     import activation_sparse_gemm_amd as rtl
@@ -103,22 +107,18 @@ def bench_layer(name: str, steps: int, warmup: int):
     X, W, LA, LB = (to_dev(d[k]) for k in ("X", "W", "LA", "LB"))
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws_bytes = rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R)
-    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device="cuda")
-    T = torch.empty((M, R), dtype=torch.bfloat16, device="cuda") if R else None
-
+    t = {"dense": time_loop(lambda: rtl.rtl_linear_dense_ref(X, W, Y=Yd), steps, warmup)}
     if synth.LAYERS[name].dense_only:
-        t_dense = time_loop(lambda: rtl.rtl_linear_dense_ref(X, W, Y=Yd), steps, warmup)
-        return d, dict(t_step=t_dense, t_dense=t_dense, t_gemm=t_dense, t_lora=0.0)
-    step = lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws)  # noqa: E731
-    t_step = time_loop(step, steps, warmup)
-    t_dense = time_loop(lambda: rtl.rtl_linear_dense_ref(X, W, Y=Yd), steps, warmup)
-    if R:
-        t_lora = time_loop(lambda: rtl.rtl_lora_down(X, LB, T=T), steps, warmup)
-    else:
-        t_lora = 0.0
-    t_gemm = time_loop(lambda: rtl.rtl_linear_fused_gemm(X, W, LA, T, Y=Y), steps, warmup)
-    return d, dict(t_step=t_step, t_dense=t_dense, t_gemm=t_gemm, t_lora=t_lora)
+        return d, t
+    ws = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R),), dtype=torch.uint8,
+                     device="cuda")
+    for vn in variants:
+        v = VARIANTS[vn]
+        t[vn] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws, variant=v), steps, warmup)
+        t[vn + "_prep"] = time_loop(lambda: rtl.rtl_linear_fused_prep(X, LB, N, ws, variant=v), steps, warmup)
+        t[vn + "_main"] = time_loop(lambda: rtl.rtl_linear_fused_main(X, W, LA, R, ws, variant=v, Y=Y), steps,
+                                    warmup)
+    return d, t
 
 
 def main():
@@ -127,6 +127,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layer", default="attn_proj")
+    ap.add_argument("--variant", default="prologue", choices=sorted(VARIANTS))
     ap.add_argument("--all-layers", action="store_true", help="also time every bf16 layer (one line each, stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -143,28 +144,38 @@ def main():
 
     d, t = bench_layer(args.layer, args.steps, args.warmup)
     M, K, N, R = d["M"], d["K"], d["N"], d["R"]
+    variant = args.variant
     flops = synth.LAYERS[args.layer].flops
-    value = flops / t["t_step"] / 1e12
-    # Dominant kernel: algorithmic work = the sparse MACs actually performed (M N K / 2
-    # multiply-adds = M N K FLOP) plus the rank-R up slice 2 M R N, per launch.
+    t_step = t[variant]
+    value = flops / t_step / 1e12
+    # Dominant kernel = the variant's GEMM launch.  Algorithmic work per launch: the sparse
+    # multiply-adds actually performed (M N K / 2, i.e. M N K FLOP) plus the rank-R slice
+    # 2 M R N; priced against the dense bf16 MFMA peak (the sparse instruction retires the
+    # same number of real multiply-adds per cycle as the dense one).
+    t_main = t[variant + "_main"]
     alg_flops = M * N * K + 2 * M * R * N
-    achieved = alg_flops / t["t_gemm"]
+    achieved = alg_flops / t_main
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_DENSE / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_DENSE, "traffic": stored_traffic(args.layer),
-                "kernel": DOMINANT, "kernel_us": t["t_gemm"] * 1e6}
+                "frac": achieved / PEAK_BF16_DENSE, "traffic": stored_traffic(args.layer, variant),
+                "kernel": f"gemm_kernel<256, {'kModeFused' if variant == 'prologue' else 'kModeComp'}>",
+                "kernel_us": t_main * 1e6}
+    prep_bytes = M * K * 2 + R * K * 2 + M * R * 2 + M * 4
+    if variant == "precompressed":
+        prep_bytes += M * K // 2 * 2 + M * K // 16
     out = {
         "metric": "effective TFLOP/s of fused 2:4 act-sparse+LoRA linear; speedup vs dense bf16",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": t["t_step"] * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.layer}: M={M} K={K} N={N} R={R}, bf16, heavy-tailed activations",
-                   "M": M, "K": K, "N": N, "R": R},
-        "speedup_vs_dense": t["t_dense"] / t["t_step"],
-        "dense_tflops": 2 * M * N * K / t["t_dense"] / 1e12,
-        "dense_ms": t["t_dense"] * 1e3,
+                   "M": M, "K": K, "N": N, "R": R, "variant": variant},
+        "speedup_vs_dense": t["dense"] / t_step,
+        "dense_tflops": 2 * M * N * K / t["dense"] / 1e12,
+        "dense_ms": t["dense"] * 1e3,
         "frac_dense_peak": value * 1e12 / PEAK_BF16_DENSE,
-        "lora_down": {"us": t["t_lora"] * 1e6, "bound": "hbm",
-                      "achieved_GBps": (M * K * 2 + R * K * 2 + M * R * 2) / t["t_lora"] / 1e9 if t["t_lora"] else None},
+        "variants_ms": {vn: t[vn] * 1e3 for vn in VARIANTS},
+        "prep": {"us": t[variant + "_prep"] * 1e6, "bound": "hbm", "bytes": prep_bytes,
+                 "achieved_GBps": prep_bytes / t[variant + "_prep"] / 1e9},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
@@ -175,10 +186,12 @@ def main():
                 continue
             dl, tl = bench_layer(name, max(5, args.steps // 5), 3)
             line = {"layer": name, "M": lay.M, "K": lay.K, "N": lay.N, "R": lay.R,
-                    "step_ms": tl["t_step"] * 1e3, "tflops": lay.flops / tl["t_step"] / 1e12,
-                    "dense_ms": tl["t_dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["t_dense"] / 1e12,
-                    "speedup_vs_dense": tl["t_dense"] / tl["t_step"], "gemm_us": tl["t_gemm"] * 1e6,
-                    "lora_down_us": tl["t_lora"] * 1e6}
+                    "dense_ms": tl["dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["dense"] / 1e12}
+            for vn in VARIANTS:
+                if vn in tl:
+                    line[vn] = {"ms": tl[vn] * 1e3, "tflops": lay.flops / tl[vn] / 1e12,
+                                "speedup": tl["dense"] / tl[vn], "prep_us": tl[vn + "_prep"] * 1e6,
+                                "main_us": tl[vn + "_main"] * 1e6}
             print(json.dumps(line), file=sys.stderr, flush=True)
             del dl
             torch.cuda.empty_cache()

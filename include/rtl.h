@@ -67,7 +67,7 @@ typedef enum { RTL_TIE_LOWER_INDEX = 0 } rtl_tie_rule;
 rtl_status rtl_sparsify(rtl_dtype dt, int64_t M, int64_t K, const void* X, rtl_tie_rule tie,
                         float eps, void* vals, uint8_t* idx, float* s, void* stream);
 
-/* Workspace bytes rtl_linear_fused needs for this shape (0 when R == 0). */
+/* Workspace bytes rtl_linear_fused needs for this shape (any variant). */
 size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R);
 
 /*
@@ -75,10 +75,11 @@ size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int6
  *   Y = s * (X~ W^T) + (X L_B^T) L_A^T
  *   X [M,K], W [N,K], LA [N,R], LB [R,K], Y [M,N]; R == 0 drops the low-rank branch
  *   (LA and LB may then be NULL).
- * bf16: the selection runs in the prologue of the sparse-MFMA GEMM; the rank-R product
- *   T = X L_B^T is a separate skinny pass into `workspace` (rounded to bf16), and the
- *   GEMM's epilogue scales its accumulators by s and adds T L_A^T into them with one
- *   extra K = R MFMA slice before the single bf16 store of Y.  Limits: K % 64 == 0,
+ * bf16: a pre-pass over X forms the rank-R product T = X L_B^T (rounded to bf16) and
+ *   the row norms in `workspace`; the sparse-MFMA GEMM then runs the 2-of-4 selection in
+ *   its A-operand prologue (or reads it from the pre-pass, see rtl_variant), and its
+ *   epilogue scales the accumulators by s and adds T L_A^T into them with one extra
+ *   K = R MFMA slice before the single bf16 store of Y.  Limits: K % 64 == 0,
  *   R % 32 == 0, R <= 128.  M and N are arbitrary.
  * fp32: same arithmetic in fp32 on the vector ALUs (no fp32 sparse MFMA exists).
  * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the GEMM
@@ -91,19 +92,40 @@ rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64
                             rtl_tie_rule tie, float eps, void* Y, void* workspace,
                             size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream);
 
+/* Where the bf16 path runs the 2-of-4 selection. */
+typedef enum {
+  RTL_VARIANT_AUTO = 0,          /* chosen from the shape */
+  RTL_VARIANT_PROLOGUE = 1,      /* in the A-operand prologue of the sparse-MFMA GEMM */
+  RTL_VARIANT_PRECOMPRESSED = 2  /* in the pre-pass over X, which hands the GEMM the
+                                    compressed operand (kept values + positions) */
+} rtl_variant;
+
 /*
- * The two stages of rtl_linear_fused(bf16), callable one by one (bf16 only):
- *   rtl_lora_down:         T = X L_B^T, T [M,R] bf16 (the skinny rank-R pass);
- *   rtl_linear_fused_gemm: Y = s * (X~ W^T) + T L_A^T with T from rtl_lora_down (the
- *                          fused selection + sparse-MFMA kernel).
- * Same limits, validation and dbg outputs as rtl_linear_fused; T must not overlap Y.
+ * rtl_linear_fused with an explicit variant (fp32 ignores it).  Both variants compute the
+ * same Y; the pre-pass over X (T = X L_B^T, the row norms, and in the pre-compressed
+ * variant the selection) always runs, followed by the GEMM.
  */
-rtl_status rtl_lora_down(rtl_dtype dt, int64_t M, int64_t K, int64_t R, const void* X, const void* LB,
-                         void* T, void* stream);
-rtl_status rtl_linear_fused_gemm(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
-                                 const void* X, const void* W, const void* LA, const void* T,
-                                 rtl_tie_rule tie, float eps, void* Y, uint8_t* dbg_idx,
-                                 float* dbg_s, void* stream);
+rtl_status rtl_linear_fused_ex(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K,
+                               int64_t R, const void* X, const void* W, const void* LA,
+                               const void* LB, rtl_tie_rule tie, float eps, void* Y, void* workspace,
+                               size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream);
+
+/*
+ * The two launches of rtl_linear_fused_ex(bf16), callable one by one (bf16 only):
+ *   rtl_linear_fused_prep: the pre-pass over X into `workspace`;
+ *   rtl_linear_fused_main: the GEMM with the epilogue, reading `workspace`.
+ * Call them in this order on the same stream with the same variant, shape and workspace.
+ * Each writes the optional dbg outputs it computes (the prologue variant's main launch,
+ * the pre-compressed variant's prep launch).  Validation as for rtl_linear_fused.
+ */
+rtl_status rtl_linear_fused_prep(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K,
+                                 int64_t R, const void* X, const void* LB, rtl_tie_rule tie, float eps,
+                                 void* workspace, size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s,
+                                 void* stream);
+rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K,
+                                 int64_t R, const void* X, const void* W, const void* LA,
+                                 rtl_tie_rule tie, float eps, void* Y, const void* workspace,
+                                 size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream);
 
 /*
  * Dense product Y = X W^T with the same tiling as the fused kernel: the layer the sparse

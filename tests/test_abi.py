@@ -36,10 +36,12 @@ def test_version_and_status_strings():
 
 def test_workspace_bytes():
     W = rtl.rtl_linear_fused_workspace_bytes
-    assert W(rtl.RTL_BF16, 4096, 3072, 3072, 0) == 0
+    assert W(rtl.RTL_BF16, 4096, 3072, 3072, 0) >= 4096 * 4      # row norms
     need = W(rtl.RTL_BF16, 4096, 3072, 3072, 64)
-    assert need >= 4096 * 64 * 2 and need % 256 == 0
+    # T [M,R] bf16 + per-row floats + the compressed operand (values M*K/2 bf16, positions M*K/16 bytes)
+    assert need >= 4096 * 64 * 2 + 4096 * 4 + 4096 * 3072 + 4096 * 3072 // 16 and need % 256 == 0
     assert W(rtl.RTL_BF16, 0, 3072, 3072, 64) == 0
+    assert W(rtl.RTL_F32, 64, 256, 256, 8) == 0
 
 
 class Host:
@@ -141,6 +143,32 @@ def test_fused_rejects_bad_calls():
         st, h = call_fused(**over)
         assert st == inv[want], (over, rtl.STATUS.get(st))
         assert h.untouched()
+
+
+def test_fused_variant_and_stage_checks():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    h = Host()
+    X, _ = h.buf(64 * 128 * 4)
+    W, _ = h.buf(64 * 128 * 4)
+    Y, _ = h.buf(64 * 64 * 4)
+    ws, _ = h.buf(1 << 20)
+    L = rtl.lib
+    # unknown variant
+    assert L.rtl_linear_fused_ex(7, rtl.RTL_BF16, 64, 64, 128, 0, X, W, None, None, 0, 1e-8, Y, ws, 1 << 20,
+                                 None, None, None) == inv["RTL_ERR_UNSUPPORTED"]
+    # the split launches are bf16 only
+    assert L.rtl_linear_fused_prep(0, rtl.RTL_F32, 64, 64, 128, 0, X, None, 0, 1e-8, ws, 1 << 20, None, None,
+                                   None) == inv["RTL_ERR_UNSUPPORTED"]
+    assert L.rtl_linear_fused_main(0, rtl.RTL_F32, 64, 64, 128, 0, X, W, None, 0, 1e-8, Y, ws, 1 << 20, None, None,
+                                   None) == inv["RTL_ERR_UNSUPPORTED"]
+    # prep needs L_B when R > 0; main needs L_A and Y
+    assert L.rtl_linear_fused_prep(0, rtl.RTL_BF16, 64, 64, 128, 32, X, None, 0, 1e-8, ws, 1 << 20, None, None,
+                                   None) == inv["RTL_ERR_NULL"]
+    assert L.rtl_linear_fused_main(0, rtl.RTL_BF16, 64, 64, 128, 32, X, W, None, 0, 1e-8, Y, ws, 1 << 20, None, None,
+                                   None) == inv["RTL_ERR_NULL"]
+    assert L.rtl_linear_fused_main(0, rtl.RTL_BF16, 64, 64, 128, 0, X, W, None, 0, 1e-8, Y, ws, 16, None, None,
+                                   None) == inv["RTL_ERR_WORKSPACE"]
+    assert h.untouched()
 
 
 def test_fused_rejects_aliasing():
