@@ -100,7 +100,7 @@ struct PrepArgs {
 // (L2-resident) with the same split.  Loads run one step ahead; the waves' partial norms
 // and partial T are summed through LDS at the end.
 constexpr int kPrepWaves = 8;
-template <bool COMPRESS>
+template <bool COMPRESS, int RC>  // RC = R / 32
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a) {
   __shared__ f32x4 tred[kPrepWaves][kMaxR / 16][64];
   __shared__ float nred[kPrepWaves][16][2];
@@ -114,12 +114,15 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a)
   const int rb = (int)(rbk & 3);
   const int64_t K = a.K;
   const int KT = (int)(K / kBK);
-  const int R = (int)a.R, CB = R / 16;
+  constexpr int R = 32 * RC, CB = 2 * RC;
   // rows past M read as zeros
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.X + rbk * 16 * K, (a.M - rbk * 16) * K * 2);
   const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LB, (int64_t)R * K * 2);
   const uint32_t x_voff = (uint32_t)(r16 * K * 2 + 32 * q);
   const uint32_t l_voff = (uint32_t)(r16 * K * 2 + 32 * q);
+  // selection codes of the block's rows; rows past M fall outside and are dropped
+  const __amdgpu_buffer_rsrc_t dres = make_rsrc(a.dbg_idx ? a.dbg_idx + rbk * 16 * (K / 4) : nullptr,
+                                                a.dbg_idx ? (a.M - rbk * 16) * (K / 4) : 0);
 
   struct Stage {
     u32x4 x[2];
@@ -144,47 +147,58 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a)
   for (int cb = 0; cb < kMaxR / 16; cb++) tacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float nx2 = 0.f, nt2 = 0.f;
 
-  auto compute = [&](int kt, const Stage& st) {
-    const uint32_t w8[8] = {st.x[0][0], st.x[0][1], st.x[0][2], st.x[0][3],
-                            st.x[1][0], st.x[1][1], st.x[1][2], st.x[1][3]};
+  // A step past the end (valid == false) reruns the last step's idempotent stores and
+  // adds nothing to the sums, so every wave issues the same loads and stores.
+  auto compute = [&](int kt, const Stage& st, bool valid) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 xv0 = valid ? st.x[0] : z, xv1 = valid ? st.x[1] : z;
+    const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
 #pragma unroll
     for (int g = 0; g < 8; g++) nx2 = dot2_bf16(w8[g], w8[g], nx2);
     if (COMPRESS) {
       u32x4 v;
       uint32_t code16 = 0, bytes = 0;
+      const uint32_t r8[8] = {st.x[0][0], st.x[0][1], st.x[0][2], st.x[0][3],
+                              st.x[1][0], st.x[1][1], st.x[1][2], st.x[1][3]};
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         uint32_t vv, cc;
-        select_bf16(w8[2 * g], w8[2 * g + 1], vv, cc);
+        select_bf16(r8[2 * g], r8[2 * g + 1], vv, cc);
         v[g] = vv;
         code16 |= cc << (4 * g);
         bytes |= cc << (8 * g);
-        nt2 = dot2_bf16(vv, vv, nt2);
+        const float t = dot2_bf16(vv, vv, nt2);
+        nt2 = valid ? t : nt2;
       }
       *reinterpret_cast<u32x4*>(a.cvals + cvals_off(p, KT, kt) + rb * 1024 + lane * 16) = v;
       *reinterpret_cast<uint16_t*>(a.cidx + cidx_off(p, KT, kt) + lane * 8 + rb * 2) = (uint16_t)code16;
-      if (a.dbg_idx != nullptr && row_ok)
-        *reinterpret_cast<uint32_t*>(a.dbg_idx + row * (K / 4) + (int64_t)kt * 16 + 4 * q) = bytes;
+      __builtin_amdgcn_raw_buffer_store_b32(bytes, dres, (uint32_t)(r16 * (K / 4) + 4 * q), kt * 16, 0);
     }
 #pragma unroll
     for (int cb = 0; cb < kMaxR / 16; cb++) {
       if (cb < CB) {
-        tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.x[0]),
+        tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv0),
                                                            __builtin_bit_cast(bf16x8, st.l[cb][0]), tacc[cb], 0, 0, 0);
-        tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.x[1]),
+        tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv1),
                                                            __builtin_bit_cast(bf16x8, st.l[cb][1]), tacc[cb], 0, 0, 0);
       }
     }
   };
 
-  Stage s0, s1;
-  if (wave < KT) load(wave, s0);
-  for (int kt = wave; kt < KT; kt += 2 * kPrepWaves) {
-    const int k1 = kt + kPrepWaves, k2 = kt + 2 * kPrepWaves;
-    if (k1 < KT) load(k1, s1);
-    compute(kt, s0);
-    if (k2 < KT) load(k2, s0);
-    if (k1 < KT) compute(k1, s1);
+  // Steps per wave (the same for all waves), loaded two steps ahead.
+  const int NIT = (KT + kPrepWaves - 1) / kPrepWaves;
+  auto kstep = [&](int i) { return min(wave + kPrepWaves * i, KT - 1); };
+  auto ok = [&](int i) { return wave + kPrepWaves * i < KT; };
+  Stage s0, s1, s2;
+  load(kstep(0), s0);
+  load(kstep(1), s1);
+  for (int i = 0; i < NIT; i += 3) {
+    load(kstep(i + 2), s2);
+    compute(kstep(i), s0, ok(i));
+    load(kstep(i + 3), s0);
+    compute(kstep(i + 1), s1, ok(i + 1));
+    load(kstep(i + 4), s1);
+    compute(kstep(i + 2), s2, ok(i + 2));
   }
 
   // Norms: over the 4 lanes of a row, then over the waves.
@@ -245,23 +259,27 @@ struct GemmArgs {
   int tiles_m, tiles_n, n_panels;
 };
 
-// GEMM workgroup: 8 waves (two per SIMD, so each SIMD can switch to the other wave while
-// one waits on memory) on a 256 x 256 output tile.  Wave w owns rows 64(w % 4)..+63 and
-// columns 128(w / 4)..+127.  Fused mode: of each row slab, the two waves that share it
+// GEMM workgroup: 8 waves (two per SIMD) on a 256 x 256 output tile; wave w owns rows
+// 64(w % 4)..+63 and columns 128(w / 4)..+127.  Operand tiles go memory -> registers ->
+// LDS two K steps ahead of their use (double-buffered LDS), so a K step's loads have two
+// steps of MFMA work to arrive.  Fused mode: of each row slab, the two waves that share it
 // select two 16-row blocks each and trade the compressed operand through LDS.
 constexpr int kGemmThreads = 512;
-constexpr int kTileN = 256;
-constexpr int kXBlk = 64 * 16 + 64 * 2;  // one row block of the compressed operand: values, positions
+constexpr int kXBlk = 64 * 16 + 64 * 2;   // fused: one row block of the compressed operand
+constexpr int kALds = kBM * 128;          // A tile bytes per LDS buffer (dense layout, the largest)
+constexpr int kCompIdx = 16384;           // pre-compressed: offset of the position words in an A buffer
 
-template <int MODE>
+template <int MODE, bool DBG, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const GemmArgs a) {
-  constexpr int NB = 8;                         // 16-column blocks per wave
-  constexpr int WLD = kTileN * 8 / kGemmThreads;  // direct-to-LDS W loads per thread per K step
+  static_assert(TN == 256 || TN == 192, "tile widths");
+  constexpr int NB = TN / 32;                     // 16-column blocks per wave (each wave: TN/2 columns)
+  constexpr int WLD = TN * 8 / kGemmThreads;      // 16-byte W chunks per thread per K step
   constexpr bool SPARSE = MODE != kModeDense;
   constexpr bool FUSED = MODE == kModeFused;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kTileN * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t xch[FUSED ? 2 * 16 * kXBlk : 16];
+  constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[2 * TN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : 2 * kALds];
   __shared__ float sred[FUSED ? 256 : 1];
 
   int tm, tn;
@@ -270,7 +288,7 @@ void gemm_kernel(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int wm = wave & 3, wn = wave >> 2;
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kTileN;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * TN;
   const int64_t M = a.M, N = a.N, K = a.K;
   const int KT = (int)(K / kBK);
 
@@ -279,45 +297,82 @@ void gemm_kernel(const GemmArgs a) {
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(a.W + n0 * K, (N - n0) * K * 2);
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.X + (MODE == kModeComp ? 0 : m0 * K), (M - m0) * K * 2);
 
-  // W: load i of wave w fills the 1 KB block (8i + w) of the LDS tile, lane l its 16-byte
-  // slot, i.e. tile row n = 8(8i + w) + l/8 and chunk c = (l % 8) ^ (n % 8).
-  const uint32_t w_voff = (uint32_t)((8 * wave + (lane >> 3)) * K * 2 + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
-  auto load_w = [&](int kt, int buf) {
+  // Tile staging: thread t moves 16-byte chunks id = t + 512 i; chunk id of a [rows][64]
+  // bf16 tile is row id / 8, k chunk id % 8, stored XOR-swizzled (sw_off).
+  const int srow = tid >> 3, schunk = tid & 7;
+  const uint32_t w_voff = (uint32_t)(srow * K * 2 + 16 * schunk);
+  typedef u32x4 WStage[WLD];
+  auto load_w = [&](int kt, WStage& st) {
 #pragma unroll
     for (int i = 0; i < WLD; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void*)(lds + buf * kTileN * 128 + (i * 8 + wave) * 1024),
-                                               16, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
+  };
+  auto store_w = [&](const WStage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < WLD; i++)
+      *reinterpret_cast<u32x4*>(wl + buf * TN * 128 + sw_off(srow + 64 * i, schunk)) = st[i];
   };
 
-  // A operand rows of this wave: 64wm + 16rb + r16.
-  const uint32_t x_voff = (uint32_t)((64 * wm + r16) * K * 2 + (FUSED ? 32 * q : 16 * q));
-  const int64_t panel = min((int64_t)tm * 4 + wm, (int64_t)a.n_panels - 1);
-  const uint8_t* cv = MODE == kModeComp ? a.cvals + cvals_off(panel, KT, 0) + lane * 16 : nullptr;
-  const uint8_t* ci = MODE == kModeComp ? a.cidx + cidx_off(panel, KT, 0) + lane * 8 : nullptr;
+  // A staging (dense: X tile like W; pre-compressed: the tile's four 64-row panels, values
+  // then position words).
+  typedef u32x4 AStage[ALD];
+  const int64_t panel0 = (int64_t)tm * 4;
+  auto cpanel = [&](int pp) { return min(panel0 + pp, (int64_t)a.n_panels - 1); };
+  auto load_at = [&](int kt, AStage& st) {
+    if (MODE == kModeDense) {
+#pragma unroll
+      for (int i = 0; i < ALD; i++)
+        st[i] = __builtin_amdgcn_raw_buffer_load_b128(xres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
+    } else if (MODE == kModeComp) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int id = tid + 512 * i, pp = id >> 8;
+        st[i] = *reinterpret_cast<const u32x4*>(a.cvals + cvals_off(cpanel(pp), KT, kt) + (id & 255) * 16);
+      }
+      const int id = tid & 127, pp = id >> 5;
+      st[2] = *reinterpret_cast<const u32x4*>(a.cidx + cidx_off(cpanel(pp), KT, kt) + (id & 31) * 16);
+    }
+  };
+  auto store_at = [&](const AStage& st, int buf) {
+    uint8_t* b = al + buf * kALds;
+    if (MODE == kModeDense) {
+#pragma unroll
+      for (int i = 0; i < ALD; i++) *reinterpret_cast<u32x4*>(b + sw_off(srow + 64 * i, schunk)) = st[i];
+    } else if (MODE == kModeComp) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int id = tid + 512 * i;
+        *reinterpret_cast<u32x4*>(b + (id >> 8) * 4096 + (id & 255) * 16) = st[i];
+      }
+      const int id = tid & 127;  // threads beyond 128 rewrite the same bytes
+      *reinterpret_cast<u32x4*>(b + kCompIdx + (id >> 5) * 512 + (id & 31) * 16) = st[2];
+    }
+  };
 
   struct AFrag {
     u32x4 v[4][2];   // dense: [rb][kk]; sparse: [rb][0] kept values
     uint32_t iw[2];  // sparse: 16-bit position words, row block rb in half rb & 1 of iw[rb / 2]
   };
-  auto load_a = [&](int kt, AFrag& f) {  // dense / pre-compressed, straight from memory
+  auto read_a = [&](int buf, AFrag& f) {  // dense / pre-compressed: the wave's rows from LDS
+    const uint8_t* b = al + buf * kALds;
+    if (MODE == kModeDense) {
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-      if (MODE == kModeDense) {
-        const int so = (int)(16 * rb * K * 2 + (int64_t)kt * kBK * 2);
-        f.v[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff, so, 0);
-        f.v[rb][1] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff + 64, so, 0);
-      } else if (MODE == kModeComp) {
-        f.v[rb][0] = *reinterpret_cast<const u32x4*>(cv + (int64_t)kt * 4096 + rb * 1024);
+      for (int rb = 0; rb < 4; rb++) {
+        const int row = 64 * wm + 16 * rb + r16;
+        f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + sw_off(row, q));
+        f.v[rb][1] = *reinterpret_cast<const u32x4*>(b + sw_off(row, 4 + q));
       }
-    }
-    if (MODE == kModeComp) {
-      const uint2 w = *reinterpret_cast<const uint2*>(ci + (int64_t)kt * 512);
+    } else if (MODE == kModeComp) {
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + wm * 4096 + rb * 1024 + lane * 16);
+      const uint2 w = *reinterpret_cast<const uint2*>(b + kCompIdx + wm * 512 + lane * 8);
       f.iw[0] = w.x;
       f.iw[1] = w.y;
     }
   };
 
   // Fused: raw X (16 consecutive values per lane) of the two row blocks 2wn, 2wn + 1.
+  const uint32_t x_voff = (uint32_t)((64 * wm + r16) * K * 2 + 32 * q);
   typedef u32x4 Raw[2][2];
   auto load_raw = [&](int kt, Raw& x) {
 #pragma unroll
@@ -328,10 +383,13 @@ void gemm_kernel(const GemmArgs a) {
     }
   };
   float nt2[2] = {0.f, 0.f};
-  const bool write_dbg = FUSED && a.dbg_idx != nullptr && tn == 0;
+  // Selection codes of this tile's rows (first tile column only); rows past M fall outside
+  // the buffer and their stores are dropped.
+  const __amdgpu_buffer_rsrc_t dres =
+      make_rsrc(DBG ? a.dbg_idx + m0 * (K / 4) : nullptr, (DBG && tn == 0) ? (M - m0) * (K / 4) : 0);
   // Fused prologue for row block 2wn + j: 2-of-4 selection, compression into the sparse
   // operand (to LDS for both waves of the slab), kept-value norm.
-  auto select_rb = [&](int kt, const Raw& x, int j, int buf) {
+  auto select_rb = [&](int kt, const Raw& x, int j, int buf, bool valid) {
     const int rb = 2 * wn + j;
     const uint32_t w8[8] = {x[j][0][0], x[j][0][1], x[j][0][2], x[j][0][3],
                             x[j][1][0], x[j][1][1], x[j][1][2], x[j][1][3]};
@@ -344,25 +402,24 @@ void gemm_kernel(const GemmArgs a) {
       v[g] = vv;
       code16 |= cc << (4 * g);
       bytes |= cc << (8 * g);
-      nt2[j] = dot2_bf16(vv, vv, nt2[j]);
+      const float t = dot2_bf16(vv, vv, nt2[j]);
+      nt2[j] = valid ? t : nt2[j];
     }
-    uint8_t* blk = xch + ((buf * 4 + wm) * 4 + rb) * kXBlk;
+    uint8_t* blk = al + ((buf * 4 + wm) * 4 + rb) * kXBlk;
     *reinterpret_cast<u32x4*>(blk + lane * 16) = v;
     *reinterpret_cast<uint16_t*>(blk + 1024 + lane * 2) = (uint16_t)code16;
-    const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-    if (write_dbg && row < M)
-      *reinterpret_cast<uint32_t*>(a.dbg_idx + row * (K / 4) + (int64_t)kt * 16 + 4 * q) = bytes;
+    if (DBG)
+      __builtin_amdgcn_raw_buffer_store_b32(bytes, dres, (uint32_t)((64 * wm + 16 * rb + r16) * (K / 4) + 4 * q),
+                                            kt * 16, 0);
   };
   auto read_sel = [&](int buf, AFrag& f) {
+    const uint8_t* b = al + (buf * 4 + wm) * 4 * kXBlk;
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-      const uint8_t* blk = xch + ((buf * 4 + wm) * 4 + rb) * kXBlk;
-      f.v[rb][0] = *reinterpret_cast<const u32x4*>(blk + lane * 16);
-    }
-    const uint32_t i0 = *reinterpret_cast<const uint16_t*>(xch + ((buf * 4 + wm) * 4 + 0) * kXBlk + 1024 + lane * 2);
-    const uint32_t i1 = *reinterpret_cast<const uint16_t*>(xch + ((buf * 4 + wm) * 4 + 1) * kXBlk + 1024 + lane * 2);
-    const uint32_t i2 = *reinterpret_cast<const uint16_t*>(xch + ((buf * 4 + wm) * 4 + 2) * kXBlk + 1024 + lane * 2);
-    const uint32_t i3 = *reinterpret_cast<const uint16_t*>(xch + ((buf * 4 + wm) * 4 + 3) * kXBlk + 1024 + lane * 2);
+    for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + rb * kXBlk + lane * 16);
+    const uint32_t i0 = *reinterpret_cast<const uint16_t*>(b + 0 * kXBlk + 1024 + lane * 2);
+    const uint32_t i1 = *reinterpret_cast<const uint16_t*>(b + 1 * kXBlk + 1024 + lane * 2);
+    const uint32_t i2 = *reinterpret_cast<const uint16_t*>(b + 2 * kXBlk + 1024 + lane * 2);
+    const uint32_t i3 = *reinterpret_cast<const uint16_t*>(b + 3 * kXBlk + 1024 + lane * 2);
     f.iw[0] = i0 | (i1 << 16);
     f.iw[1] = i2 | (i3 << 16);
   };
@@ -373,20 +430,20 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One main-loop step on LDS buffer kt & 1: issue the loads of later steps, run the
-  // MFMAs of step kt with the B operand read two column blocks ahead, and (fused) select
-  // the raw X of step kt + 1 between them.
-  auto step = [&](int kt, AFrag& cur, AFrag& nxt, Raw& xsel, Raw& xload) {
+  // One main-loop step on LDS buffer kt & 1.  Every memory operation in the loop is
+  // issued unconditionally (the last steps reload the final K step), so the wait counts
+  // the compiler derives are exact and loads stay in flight across the barrier.
+  auto step = [&](int kt, Raw& xsel, Raw& xload, WStage& wnext, WStage& wfar, AStage& anext, AStage& afar) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) load_w(kt + 1, buf ^ 1);
-    if (!FUSED) {
-      if (kt + 1 < KT) load_a(kt + 1, nxt);
-    } else {
-      if (kt + 2 < KT) load_raw(kt + 2, xload);
-    }
-    const uint8_t* base = lds + buf * kTileN * 128;
+    load_w(min(kt + 2, KT - 1), wfar);
+    if (FUSED) load_raw(min(kt + 2, KT - 1), xload);
+    else load_at(min(kt + 2, KT - 1), afar);
+    AFrag cur;
+    if (FUSED) read_sel(buf, cur);
+    else read_a(buf, cur);
+    const uint8_t* base = wl + buf * TN * 128;
     auto read_b = [&](int nb) {
-      const int n = 128 * wn + nb * 16 + r16;
+      const int n = (TN / 2) * wn + nb * 16 + r16;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
       const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
       return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -419,34 +476,36 @@ void gemm_kernel(const GemmArgs a) {
                                                                 __builtin_bit_cast(bf16x8, b1), acc[rb][nb], 0, 0, 0);
         }
       }
-      if (FUSED && kt + 1 < KT && (nb % (NB / 2)) == 0) select_rb(kt + 1, xsel, nb / (NB / 2), buf ^ 1);
+      if (FUSED && (nb == 0 || nb == NB / 2))
+        select_rb(min(kt + 1, KT - 1), xsel, nb == 0 ? 0 : 1, buf ^ 1, kt + 1 < KT);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<0>();
+    store_w(wnext, buf ^ 1);
+    if (!FUSED) store_at(anext, buf ^ 1);
     __syncthreads();
-    if (FUSED && kt + 1 < KT) read_sel(buf ^ 1, nxt);
   };
 
-  AFrag fa, fb;
   Raw xr0, xr1;
-  load_w(0, 0);
+  WStage w0, w1;
+  AStage a0, a1;
+  load_w(0, w0);
+  load_w(min(1, KT - 1), w1);
   if (FUSED) {
     load_raw(0, xr0);
-    if (KT > 1) load_raw(1, xr1);
-    select_rb(0, xr0, 0, 0);
-    select_rb(0, xr0, 1, 0);
+    load_raw(min(1, KT - 1), xr1);
+    select_rb(0, xr0, 0, 0, true);
+    select_rb(0, xr0, 1, 0, true);
   } else {
-    load_a(0, fa);
+    load_at(0, a0);
+    load_at(min(1, KT - 1), a1);
+    store_at(a0, 0);
   }
-  wait_vmcnt<0>();
+  store_w(w0, 0);
   __syncthreads();
-  if (FUSED) read_sel(0, fa);
   for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, fa, fb, xr1, xr0);
-    if (kt + 1 < KT) step(kt + 1, fb, fa, xr0, xr1);
+    step(kt, xr1, xr0, w1, w0, a1, a0);
+    if (kt + 1 < KT) step(kt + 1, xr0, xr1, w0, w1, a0, a1);
   }
-  const AFrag& last = (KT & 1) ? fb : fa;
-  (void)last;
 
   if (SPARSE) {
     // s of row 16rb + r16 (the row this lane feeds as A operand) ...
@@ -498,7 +557,7 @@ void gemm_kernel(const GemmArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) {
-        const int64_t col = n0 + 128 * wn + nb * 16 + r16;
+        const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
         const u32x4 la = *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
 #pragma unroll
         for (int rb = 0; rb < 4; rb++)
@@ -516,7 +575,7 @@ void gemm_kernel(const GemmArgs a) {
         uint16_t* yrow = a.Y + row * N;
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
-          const int64_t col = n0 + 128 * wn + nb * 16 + r16;
+          const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
           if (col < N) yrow[col] = (uint16_t)f32_to_bf16_bits(acc[rb][nb][j] * s_acc[rb][j]);
         }
       }
@@ -535,14 +594,13 @@ void gemm_kernel(const GemmArgs a) {
       uint16_t* yrow = a.Y + row * N;
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) {
-        const int64_t col = n0 + 128 * wn + nb * 16 + r16;
+        const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
         if (col < N) yrow[col] = (uint16_t)f32_to_bf16_bits(acc[rb][nb][j]);
       }
     }
   }
 }
 
-constexpr int kBN = kTileN;
 
 static int64_t padded_rows(int64_t M) { return (M + kPanel - 1) / kPanel * kPanel; }
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -575,13 +633,13 @@ size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R) {
 }
 
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
-                          void* Y, float eps) {
+                          void* Y, float eps, int tn_width) {
   GemmArgs g{};
   g.M = M; g.N = N; g.K = K; g.R = R;
   g.X = (const uint16_t*)X; g.W = (const uint16_t*)W; g.LA = (const uint16_t*)LA;
   g.eps = eps; g.Y = (uint16_t*)Y;
   g.tiles_m = (int)((M + kBM - 1) / kBM);
-  g.tiles_n = (int)((N + kBN - 1) / kBN);
+  g.tiles_n = (int)((N + tn_width - 1) / tn_width);
   g.n_panels = (int)(padded_rows(M) / kPanel);
   return g;
 }
@@ -601,12 +659,50 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     p.cidx = base + L.cidx;
     p.dbg_idx = dbg_idx;
     p.dbg_s = dbg_s;
-    hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, stream, p);
   } else {
     p.nx2 = (float*)(base + L.norm);
-    hipLaunchKernelGGL(prep_kernel<false>, grid, block, 0, stream, p);
   }
+#define RTL_PREP(C, RC) hipLaunchKernelGGL((prep_kernel<C, RC>), grid, block, 0, stream, p)
+  switch ((comp ? 8 : 0) + (int)(R / 32)) {
+    case 0: RTL_PREP(false, 0); break;
+    case 1: RTL_PREP(false, 1); break;
+    case 2: RTL_PREP(false, 2); break;
+    case 3: RTL_PREP(false, 3); break;
+    case 4: RTL_PREP(false, 4); break;
+    case 8: RTL_PREP(true, 0); break;
+    case 9: RTL_PREP(true, 1); break;
+    case 10: RTL_PREP(true, 2); break;
+    case 11: RTL_PREP(true, 3); break;
+    default: RTL_PREP(true, 4); break;
+  }
+#undef RTL_PREP
   return hipGetLastError();
+}
+
+// Output tile width: the candidate whose tile count best fills whole waves of
+// workgroups over the 256 CUs (a 192-wide tile costs a little more per column).
+static int choose_tn(int64_t M, int64_t N) {
+  const int64_t tm = (M + kBM - 1) / kBM;
+  double best = 1e300;
+  int pick = 256;
+  for (int tn : {256, 192}) {
+    const int64_t tiles = tm * ((N + tn - 1) / tn);
+    const double cost = (double)((tiles + 255) / 256) * tn * (tn == 192 ? 1.05 : 1.0);
+    if (cost < best) { best = cost; pick = tn; }
+  }
+  return pick;
+}
+
+template <int TN>
+static void launch_main_tn(bool comp, GemmArgs g, uint8_t* dbg_idx, hipStream_t stream) {
+  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(kGemmThreads);
+  if (comp) {
+    hipLaunchKernelGGL((gemm_kernel<kModeComp, false, TN>), grid, block, 0, stream, g);
+  } else if (dbg_idx != nullptr) {
+    hipLaunchKernelGGL((gemm_kernel<kModeFused, true, TN>), grid, block, 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<kModeFused, false, TN>), grid, block, 0, stream, g);
+  }
 }
 
 hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,
@@ -615,20 +711,20 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
   const WsLayout L = ws_layout(M, K, R, comp);
   const uint8_t* base = (const uint8_t*)ws;
-  GemmArgs g = gemm_args(M, N, K, R, X, W, LA, Y, eps);
+  const int tn = choose_tn(M, N);
+  GemmArgs g = gemm_args(M, N, K, R, X, W, LA, Y, eps, tn);
   g.T = (const uint16_t*)(base + L.t);
-  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(kGemmThreads);
   if (comp) {
     g.s = (const float*)(base + L.norm);
     g.cvals = base + L.cvals;
     g.cidx = base + L.cidx;
-    hipLaunchKernelGGL((gemm_kernel<kModeComp>), grid, block, 0, stream, g);
   } else {
     g.nx2 = (const float*)(base + L.norm);
     g.dbg_idx = dbg_idx;
     g.dbg_s = dbg_s;
-    hipLaunchKernelGGL((gemm_kernel<kModeFused>), grid, block, 0, stream, g);
   }
+  if (tn == 192) launch_main_tn<192>(comp, g, dbg_idx, stream);
+  else launch_main_tn<256>(comp, g, dbg_idx, stream);
   return hipGetLastError();
 }
 
@@ -642,9 +738,11 @@ hipError_t launch_fused_bf16(int variant, int64_t M, int64_t N, int64_t K, int64
 
 hipError_t launch_dense_bf16(int64_t M, int64_t N, int64_t K, const void* X, const void* W, void* Y,
                              hipStream_t stream) {
-  GemmArgs g = gemm_args(M, N, K, 0, X, W, nullptr, Y, 0.f);
-  hipLaunchKernelGGL((gemm_kernel<kModeDense>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kGemmThreads), 0,
-                     stream, g);
+  const int tn = choose_tn(M, N);
+  GemmArgs g = gemm_args(M, N, K, 0, X, W, nullptr, Y, 0.f, tn);
+  const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(kGemmThreads);
+  if (tn == 192) hipLaunchKernelGGL((gemm_kernel<kModeDense, false, 192>), grid, block, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_kernel<kModeDense, false, 256>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 
