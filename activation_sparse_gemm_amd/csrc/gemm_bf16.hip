@@ -1,59 +1,23 @@
-// gemm_bf16.hip -- bf16 kernels on the CDNA4 matrix cores for the norm-compensated
-// 2:4 activation-sparse linear layer ("RT-Lynx: Putting the GEMM Sparsity In a Right Way
-// for Diffusion Models", summary page, method steps 1, 2 and 4):
+// gemm_bf16.hip -- the bf16 GEMMs on the CDNA4 matrix cores for the norm-compensated 2:4
+// activation-sparse linear layer ("RT-Lynx: Putting the GEMM Sparsity In a Right Way for
+// Diffusion Models", summary page, method steps 1, 2 and 4):
 //
-//  * prep_kernel: one pass over the dense X per 64-row panel.  It forms the rank-R down
-//    projection T = X L_B^T on the matrix cores (L_B staged through LDS and shared by the
-//    panel's rows), the squared row norms, and, in the pre-compressed mode, the 2-of-4
-//    selection itself: the kept values and their 2-bit positions written in the exact
-//    register order of the sparse MFMA's A operand, plus s.
-//  * gemm_kernel<BN, MODE>: the main product on a 256 x BN output tile.
-//      MODE kFused: the 2-of-4 selection and compression run in the A-operand prologue
-//        of the GEMM itself, software-pipelined one K step ahead of the sparse MFMAs;
-//        the kept-value norm is accumulated across the K loop.
-//      MODE kComp:  the A operand arrives already compressed from prep_kernel.
-//      MODE kDense: the dense product X W^T (v_mfma_f32_16x16x32_bf16), same tiling.
-//    Sparse modes run v_smfmac_f32_16x16x64_bf16; their epilogue multiplies the
-//    accumulators by s and adds T L_A^T with an extra K = R MFMA slice into the same
-//    accumulators, so the M x N low-rank product never reaches device memory.
-//
-// Tiling: 4 waves own a 256 x BN tile; wave w owns rows 64w..64w+63 and all BN columns,
-// so every X element of the tile is selected by exactly one lane and the A operand goes
-// from memory straight into registers.  The W tile (BN x 64 per K step) streams into LDS
-// with direct-to-LDS loads, double-buffered; its 16-byte chunks are XOR-swizzled so the
-// B-operand reads are free of bank conflicts.
-#include "rtl_device.h"
-#include "rtl_launch.h"
+//  gemm_kernel<MODE, DBG, TN>: the product on a 256 x TN output tile.
+//    kModeComp:  the A operand arrives compressed from the pre-pass (kept values and
+//                2-bit positions in sparse-MFMA register order).
+//    kModeFused: the 2-of-4 selection and compression run in the GEMM's own A-operand
+//                prologue, one K step ahead of the sparse MFMAs; the kept-value norm is
+//                accumulated across the K loop.
+//    kModeDense: the dense product X W^T (v_mfma_f32_16x16x32_bf16), same tiling.
+//  Sparse modes run v_smfmac_f32_16x16x64_bf16; their epilogue adds (T / s) L_A^T into the
+//  accumulators with an extra K = R MFMA slice and stores s * acc, so the M x N low-rank
+//  product never reaches device memory.
+#include "bf16_common.h"
 
 namespace rtl {
 
 constexpr int kBM = 256;  // rows per GEMM workgroup
-constexpr int kBK = 64;   // K per main-loop step
-constexpr int kThreads = 256;
-constexpr int kPanel = 64;     // rows per prep workgroup (and per GEMM wave)
-constexpr int kMaxR = 128;
 constexpr int kModeDense = 0, kModeFused = 1, kModeComp = 2;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Byte offset of 16-byte chunk c (k = 8c..8c+7) of row n in a [rows][64] bf16 LDS tile.
-__device__ __forceinline__ uint32_t sw_off(int n, int c) { return (uint32_t)(n * 128 + ((c ^ (n & 7)) << 4)); }
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Direct-to-LDS loads count in vmcnt and
-// complete in issue order with the other vector-memory loads.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Raw buffer resource over [base, base + bytes) (bytes clamped to 32 bits): loads at or
-// past the end return zeros, stores there are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, 0x00020000);
-}
 
 // Workgroup id -> (tile_m, tile_n).  Workgroups are dealt round-robin to the 8 XCDs;
 // remap so that each XCD gets a contiguous run of logical tiles, and walk logical tiles
@@ -70,176 +34,6 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   const int gsz = min(tiles_m - first_m, kGroupM);
   tm = first_m + (t % width) % gsz;
   tn = (t % width) / gsz;
-}
-
-// Pre-compressed operand layout: per (64-row panel p, 64-wide K step kt) a 4 KB block of
-// kept values, row block rb at +1024*rb, lane l (row 16rb + l%16, dense k 16(l/16)..+15)
-// at +16*l; and a 512-byte block of 16-bit position words, lane l at +8*l, row block rb
-// at +2*rb.
-__device__ __forceinline__ int64_t cvals_off(int64_t p, int KT, int kt) { return (p * KT + kt) * 4096; }
-__device__ __forceinline__ int64_t cidx_off(int64_t p, int KT, int kt) { return (p * KT + kt) * 512; }
-
-struct PrepArgs {
-  int64_t M, K, R;
-  const uint16_t* X;
-  const uint16_t* LB;
-  float eps;
-  uint16_t* T;        // [Mp, R] bf16
-  float* nx2;         // [Mp] (fused mode)
-  float* s;           // [Mp] (pre-compressed mode)
-  uint8_t* cvals;     // pre-compressed mode
-  uint8_t* cidx;
-  uint8_t* dbg_idx;   // [M, K/4] or null (pre-compressed mode)
-  float* dbg_s;       // [M] or null (pre-compressed mode)
-};
-
-// One workgroup per 16-row block, 8 waves; wave w takes the 64-wide K steps kt = w + 8i.
-// Every lane holds 16 consecutive values of its row (k = 16q..16q+15 of the step), which
-// serve both the selection (four groups of 4) and, read as two 8-wide K slices, the A
-// operand of the rank-R product; the matching L_B values are read straight from memory
-// (L2-resident) with the same split.  Loads run one step ahead; the waves' partial norms
-// and partial T are summed through LDS at the end.
-constexpr int kPrepWaves = 8;
-template <bool COMPRESS, int RC>  // RC = R / 32
-__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a) {
-  __shared__ f32x4 tred[kPrepWaves][kMaxR / 16][64];
-  __shared__ float nred[kPrepWaves][16][2];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
-  const int q = lane >> 4, r16 = lane & 15;
-  const int64_t rbk = blockIdx.x;  // 16-row block
-  const int64_t row = rbk * 16 + r16;
-  const bool row_ok = row < a.M;
-  const int64_t p = rbk >> 2;
-  const int rb = (int)(rbk & 3);
-  const int64_t K = a.K;
-  const int KT = (int)(K / kBK);
-  constexpr int R = 32 * RC, CB = 2 * RC;
-  // rows past M read as zeros
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.X + rbk * 16 * K, (a.M - rbk * 16) * K * 2);
-  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LB, (int64_t)R * K * 2);
-  const uint32_t x_voff = (uint32_t)(r16 * K * 2 + 32 * q);
-  const uint32_t l_voff = (uint32_t)(r16 * K * 2 + 32 * q);
-  // selection codes of the block's rows; rows past M fall outside and are dropped
-  const __amdgpu_buffer_rsrc_t dres = make_rsrc(a.dbg_idx ? a.dbg_idx + rbk * 16 * (K / 4) : nullptr,
-                                                a.dbg_idx ? (a.M - rbk * 16) * (K / 4) : 0);
-
-  struct Stage {
-    u32x4 x[2];
-    u32x4 l[kMaxR / 16][2];
-  };
-  auto load = [&](int kt, Stage& st) {
-    const int so = kt * kBK * 2;
-    st.x[0] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff, so, 0);
-    st.x[1] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff + 16, so, 0);
-#pragma unroll
-    for (int cb = 0; cb < kMaxR / 16; cb++) {
-      if (cb < CB) {
-        const int so2 = so + (int)(cb * 16 * K * 2);
-        st.l[cb][0] = __builtin_amdgcn_raw_buffer_load_b128(lres, l_voff, so2, 0);
-        st.l[cb][1] = __builtin_amdgcn_raw_buffer_load_b128(lres, l_voff + 16, so2, 0);
-      }
-    }
-  };
-
-  f32x4 tacc[kMaxR / 16];
-#pragma unroll
-  for (int cb = 0; cb < kMaxR / 16; cb++) tacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float nx2 = 0.f, nt2 = 0.f;
-
-  // A step past the end (valid == false) reruns the last step's idempotent stores and
-  // adds nothing to the sums, so every wave issues the same loads and stores.
-  auto compute = [&](int kt, const Stage& st, bool valid) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 xv0 = valid ? st.x[0] : z, xv1 = valid ? st.x[1] : z;
-    const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
-#pragma unroll
-    for (int g = 0; g < 8; g++) nx2 = dot2_bf16(w8[g], w8[g], nx2);
-    if (COMPRESS) {
-      u32x4 v;
-      uint32_t code16 = 0, bytes = 0;
-      const uint32_t r8[8] = {st.x[0][0], st.x[0][1], st.x[0][2], st.x[0][3],
-                              st.x[1][0], st.x[1][1], st.x[1][2], st.x[1][3]};
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        uint32_t vv, cc;
-        select_bf16(r8[2 * g], r8[2 * g + 1], vv, cc);
-        v[g] = vv;
-        code16 |= cc << (4 * g);
-        bytes |= cc << (8 * g);
-        const float t = dot2_bf16(vv, vv, nt2);
-        nt2 = valid ? t : nt2;
-      }
-      *reinterpret_cast<u32x4*>(a.cvals + cvals_off(p, KT, kt) + rb * 1024 + lane * 16) = v;
-      *reinterpret_cast<uint16_t*>(a.cidx + cidx_off(p, KT, kt) + lane * 8 + rb * 2) = (uint16_t)code16;
-      __builtin_amdgcn_raw_buffer_store_b32(bytes, dres, (uint32_t)(r16 * (K / 4) + 4 * q), kt * 16, 0);
-    }
-#pragma unroll
-    for (int cb = 0; cb < kMaxR / 16; cb++) {
-      if (cb < CB) {
-        tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv0),
-                                                           __builtin_bit_cast(bf16x8, st.l[cb][0]), tacc[cb], 0, 0, 0);
-        tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv1),
-                                                           __builtin_bit_cast(bf16x8, st.l[cb][1]), tacc[cb], 0, 0, 0);
-      }
-    }
-  };
-
-  // Steps per wave (the same for all waves), loaded two steps ahead.
-  const int NIT = (KT + kPrepWaves - 1) / kPrepWaves;
-  auto kstep = [&](int i) { return min(wave + kPrepWaves * i, KT - 1); };
-  auto ok = [&](int i) { return wave + kPrepWaves * i < KT; };
-  Stage s0, s1, s2;
-  load(kstep(0), s0);
-  load(kstep(1), s1);
-  for (int i = 0; i < NIT; i += 3) {
-    load(kstep(i + 2), s2);
-    compute(kstep(i), s0, ok(i));
-    load(kstep(i + 3), s0);
-    compute(kstep(i + 1), s1, ok(i + 1));
-    load(kstep(i + 4), s1);
-    compute(kstep(i + 2), s2, ok(i + 2));
-  }
-
-  // Norms: over the 4 lanes of a row, then over the waves.
-  nx2 += __shfl_xor(nx2, 16, 64);
-  nt2 += __shfl_xor(nt2, 16, 64);
-  nx2 += __shfl_xor(nx2, 32, 64);
-  nt2 += __shfl_xor(nt2, 32, 64);
-  if (q == 0) {
-    nred[wave][r16][0] = nx2;
-    nred[wave][r16][1] = nt2;
-  }
-#pragma unroll
-  for (int cb = 0; cb < kMaxR / 16; cb++)
-    if (cb < CB) tred[wave][cb][lane] = tacc[cb];
-  __syncthreads();
-  if (wave == 0) {
-    if (q == 0) {
-      float x2 = 0.f, t2 = 0.f;
-#pragma unroll
-      for (int w = 0; w < kPrepWaves; w++) {
-        x2 += nred[w][r16][0];
-        t2 += nred[w][r16][1];
-      }
-      if (COMPRESS) {
-        const float sv = sqrtf(x2) / (sqrtf(t2) + a.eps);
-        a.s[row] = sv;
-        if (a.dbg_s != nullptr && row_ok) a.dbg_s[row] = sv;
-      } else {
-        a.nx2[row] = x2;
-      }
-    }
-    // T rows 4q + j of the block, column cb*16 + r16 (accumulator layout), rounded to bf16.
-    for (int cb = 0; cb < CB; cb++) {
-      f32x4 v = tred[0][cb][lane];
-#pragma unroll
-      for (int w = 1; w < kPrepWaves; w++) v += tred[w][cb][lane];
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(v[j]);
-    }
-  }
 }
 
 struct GemmArgs {
@@ -601,37 +395,6 @@ void gemm_kernel(const GemmArgs a) {
   }
 }
 
-
-static int64_t padded_rows(int64_t M) { return (M + kPanel - 1) / kPanel * kPanel; }
-static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-
-// Workspace: T [Mp,R] bf16 | nx2 or s [Mp] f32 | (pre-compressed) values, position words.
-struct WsLayout {
-  size_t t, norm, cvals, cidx, total;
-};
-static WsLayout ws_layout(int64_t M, int64_t K, int64_t R, bool comp) {
-  const int64_t Mp = padded_rows(M);
-  WsLayout L;
-  L.t = 0;
-  L.norm = align256((size_t)Mp * R * 2);
-  L.cvals = L.norm + align256((size_t)Mp * 4);
-  L.cidx = L.cvals + (comp ? align256((size_t)Mp * (K / 2) * 2) : 0);
-  L.total = L.cidx + (comp ? align256((size_t)(Mp / kPanel) * (K / kBK) * 512) : 0);
-  return L;
-}
-
-int resolve_variant_bf16(int variant, int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
-  if (variant == kVariantPrologue || variant == kVariantPrecompressed) return variant;
-  return kVariantPrologue;
-}
-
-size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R) {
-  (void)N;
-  const WsLayout a = ws_layout(M, K, R, false), b = ws_layout(M, K, R, true);
-  return a.total > b.total ? a.total : b.total;
-}
-
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
                           void* Y, float eps, int tn_width) {
   GemmArgs g{};
@@ -642,41 +405,6 @@ static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void
   g.tiles_n = (int)((N + tn_width - 1) / tn_width);
   g.n_panels = (int)(padded_rows(M) / kPanel);
   return g;
-}
-
-hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
-                            float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream) {
-  const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
-  const WsLayout L = ws_layout(M, K, R, comp);
-  uint8_t* base = (uint8_t*)ws;
-  PrepArgs p{};
-  p.M = M; p.K = K; p.R = R; p.X = (const uint16_t*)X; p.LB = (const uint16_t*)LB; p.eps = eps;
-  p.T = (uint16_t*)(base + L.t);
-  const dim3 grid((unsigned)(padded_rows(M) / 16)), block(64 * kPrepWaves);
-  if (comp) {
-    p.s = (float*)(base + L.norm);
-    p.cvals = base + L.cvals;
-    p.cidx = base + L.cidx;
-    p.dbg_idx = dbg_idx;
-    p.dbg_s = dbg_s;
-  } else {
-    p.nx2 = (float*)(base + L.norm);
-  }
-#define RTL_PREP(C, RC) hipLaunchKernelGGL((prep_kernel<C, RC>), grid, block, 0, stream, p)
-  switch ((comp ? 8 : 0) + (int)(R / 32)) {
-    case 0: RTL_PREP(false, 0); break;
-    case 1: RTL_PREP(false, 1); break;
-    case 2: RTL_PREP(false, 2); break;
-    case 3: RTL_PREP(false, 3); break;
-    case 4: RTL_PREP(false, 4); break;
-    case 8: RTL_PREP(true, 0); break;
-    case 9: RTL_PREP(true, 1); break;
-    case 10: RTL_PREP(true, 2); break;
-    case 11: RTL_PREP(true, 3); break;
-    default: RTL_PREP(true, 4); break;
-  }
-#undef RTL_PREP
-  return hipGetLastError();
 }
 
 // Output tile width: the candidate whose tile count best fills whole waves of

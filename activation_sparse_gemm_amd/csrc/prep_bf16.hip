@@ -1,0 +1,298 @@
+// prep_bf16.hip -- the bf16 pre-pass over X for the norm-compensated 2:4 activation-
+// sparse linear layer ("RT-Lynx: Putting the GEMM Sparsity In a Right Way for Diffusion
+// Models", summary page, method steps 1 and 2).  One read of the dense X forms the
+// rank-R down projection T = X L_B^T on the matrix cores, the squared row norms and, for
+// the pre-compressed variant, the 2-of-4 selection itself: the kept values and their
+// 2-bit positions, written in the register order of the sparse MFMA's A operand, and s.
+#include "bf16_common.h"
+
+namespace rtl {
+
+struct PrepArgs {
+  int64_t M, K, R;
+  const uint16_t* X;
+  const uint16_t* LB;
+  float eps;
+  uint16_t* T;        // [Mp, R] bf16
+  float* nx2;         // [Mp] (fused mode)
+  float* s;           // [Mp] (pre-compressed mode)
+  uint8_t* cvals;     // pre-compressed mode
+  uint8_t* cidx;
+  uint8_t* dbg_idx;   // [M, K/4] or null (pre-compressed mode)
+  float* dbg_s;       // [M] or null (pre-compressed mode)
+  float* tpart;       // [ks, Mp, R] partial T when ks > 1
+  float* npart;       // [ks, Mp, 2] partial squared norms when ks > 1
+  int ks;             // K splits
+  int kts;            // K steps per split
+};
+
+// Pre-pass over X.  Workgroup (row tile, K split): 8 waves, wave w the 16-row block w of
+// a 128-row tile, all K steps of the split.  Every lane holds 16 consecutive values of its
+// row (k = 16q..16q+15 of a step), which serve both the selection (four groups of 4) and,
+// read as two 8-wide K slices, the A operand of the rank-R product; the L_B slice of each
+// step passes through LDS once per workgroup and is shared by its 128 rows.  X and L_B
+// are loaded two steps ahead.  With several K splits the partial T and norms go to the
+// workspace and prep_reduce_kernel sums them in a fixed order.
+template <bool COMPRESS, int RC>  // RC = R / 32
+__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a) {
+  constexpr int R = 32 * RC, CB = 2 * RC;
+  constexpr int LCH = RC > 0 ? (R * 8 + 511) / 512 : 1;  // 16-byte L_B chunks per thread per step
+  __shared__ __attribute__((aligned(1024))) uint8_t lb[2][RC > 0 ? R * 128 : 16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t K = a.K;
+  const int KT = (int)(K / kBK);
+  const int split = blockIdx.y;
+  const int kt0 = split * a.kts, nk = min(a.kts, KT - kt0);
+  const int64_t rbk = (int64_t)blockIdx.x * kPrepWaves + wave;  // global 16-row block
+  const int64_t row = rbk * 16 + r16;
+  const bool row_ok = row < a.M;
+  const int64_t p = rbk >> 2;
+  const int rb = (int)(rbk & 3);
+  // rows past M read as zeros
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.X + rbk * 16 * K, (a.M - rbk * 16) * K * 2);
+  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LB, (int64_t)R * K * 2);
+  const uint32_t x_voff = (uint32_t)(r16 * K * 2 + 32 * q);
+  // selection codes of the block's rows; rows past M fall outside and are dropped
+  const __amdgpu_buffer_rsrc_t dres = make_rsrc(a.dbg_idx ? a.dbg_idx + rbk * 16 * (K / 4) : nullptr,
+                                                a.dbg_idx ? (a.M - rbk * 16) * (K / 4) : 0);
+
+  struct Stage {
+    u32x4 x[2];
+    u32x4 l[LCH];
+  };
+  // L_B chunk id = tid + 512 j of the step's [R][64] slice: row id / 8, k chunk id % 8.
+  auto load = [&](int kt, Stage& st) {
+    const int so = kt * kBK * 2;
+    st.x[0] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff, so, 0);
+    st.x[1] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff + 16, so, 0);
+#pragma unroll
+    for (int j = 0; j < LCH; j++) {
+      const int id = (tid + 512 * j) % (RC > 0 ? R * 8 : 8);
+      st.l[j] = __builtin_amdgcn_raw_buffer_load_b128(lres, (uint32_t)((id >> 3) * K * 2 + 16 * (id & 7)), so, 0);
+    }
+  };
+  auto store_lb = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int j = 0; j < LCH; j++) {
+      const int id = (tid + 512 * j) % (RC > 0 ? R * 8 : 8);  // duplicates rewrite the same bytes
+      if (RC > 0) *reinterpret_cast<u32x4*>(&lb[buf][sw_off(id >> 3, id & 7)]) = st.l[j];
+    }
+  };
+
+  f32x4 tacc[CB > 0 ? CB : 1];
+#pragma unroll
+  for (int cb = 0; cb < (CB > 0 ? CB : 1); cb++) tacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float nx2 = 0.f, nt2 = 0.f;
+
+  // A step past the end of the split (valid == false) reruns the last step's idempotent
+  // stores and adds nothing to the sums, so every wave issues the same memory operations.
+  auto compute = [&](int kt, const Stage& st, int buf, bool valid) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 xv0 = valid ? st.x[0] : z, xv1 = valid ? st.x[1] : z;
+    const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
+#pragma unroll
+    for (int g = 0; g < 8; g++) nx2 = dot2_bf16(w8[g], w8[g], nx2);
+    if (COMPRESS) {
+      u32x4 v;
+      uint32_t code16 = 0, bytes = 0;
+      const uint32_t r8[8] = {st.x[0][0], st.x[0][1], st.x[0][2], st.x[0][3],
+                              st.x[1][0], st.x[1][1], st.x[1][2], st.x[1][3]};
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        uint32_t vv, cc;
+        select_bf16(r8[2 * g], r8[2 * g + 1], vv, cc);
+        v[g] = vv;
+        code16 |= cc << (4 * g);
+        bytes |= cc << (8 * g);
+        const float t = dot2_bf16(vv, vv, nt2);
+        nt2 = valid ? t : nt2;
+      }
+      *reinterpret_cast<u32x4*>(a.cvals + cvals_off(p, KT, kt) + rb * 1024 + lane * 16) = v;
+      *reinterpret_cast<uint16_t*>(a.cidx + cidx_off(p, KT, kt) + lane * 8 + rb * 2) = (uint16_t)code16;
+      __builtin_amdgcn_raw_buffer_store_b32(bytes, dres, (uint32_t)(r16 * (K / 4) + 4 * q), kt * 16, 0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      const int r = cb * 16 + r16;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(&lb[buf][sw_off(r, 2 * q)]);
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(&lb[buf][sw_off(r, 2 * q + 1)]);
+      tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv0),
+                                                         __builtin_bit_cast(bf16x8, b0), tacc[cb], 0, 0, 0);
+      tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv1),
+                                                         __builtin_bit_cast(bf16x8, b1), tacc[cb], 0, 0, 0);
+    }
+  };
+
+  // Step i of the split works on K step kt0 + i with L_B in LDS buffer i % 2; stage
+  // i + 2 is loaded while step i computes, and stage i + 1's L_B goes to the other buffer
+  // before the step's barrier.
+  auto kc = [&](int i) { return kt0 + min(i, nk - 1); };
+  Stage s0, s1, s2;
+  load(kc(0), s0);
+  load(kc(1), s1);
+  store_lb(s0, 0);
+  __syncthreads();
+  auto step = [&](int i, Stage& cur, Stage& nxt, Stage& far) {
+    load(kc(i + 2), far);
+    compute(kc(i), cur, i & 1, i < nk);
+    store_lb(nxt, (i + 1) & 1);
+    __syncthreads();
+  };
+  for (int i = 0; i < nk; i += 3) {
+    step(i, s0, s1, s2);
+    step(i + 1, s1, s2, s0);
+    step(i + 2, s2, s0, s1);
+  }
+
+  // Norms over the 4 lanes of a row.
+  nx2 += __shfl_xor(nx2, 16, 64);
+  nt2 += __shfl_xor(nt2, 16, 64);
+  nx2 += __shfl_xor(nx2, 32, 64);
+  nt2 += __shfl_xor(nt2, 32, 64);
+  if (a.ks == 1) {
+    if (q == 0) {
+      if (COMPRESS) {
+        const float sv = sqrtf(nx2) / (sqrtf(nt2) + a.eps);
+        a.s[row] = sv;
+        if (a.dbg_s != nullptr && row_ok) a.dbg_s[row] = sv;
+      } else {
+        a.nx2[row] = nx2;
+      }
+    }
+    // T rows 4q + j of the block, column cb*16 + r16 (accumulator layout), rounded to bf16.
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(tacc[cb][j]);
+  } else {
+    const int64_t Mp = (int64_t)gridDim.x * kPrepRows;
+    if (q == 0) {
+      a.npart[(split * Mp + row) * 2 + 0] = nx2;
+      a.npart[(split * Mp + row) * 2 + 1] = nt2;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) a.tpart[(split * Mp + rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = tacc[cb][j];
+  }
+}
+
+// Sums the K-split partials of prep_kernel in split order: T (rounded to bf16) and s (or
+// ||X||^2 for the prologue variant).  One thread per (row, 4 columns of T).
+template <bool COMPRESS>
+__global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepArgs a, int64_t Mp) {
+  const int64_t R = a.R;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // row * (R/4 + 1) + c
+  const int64_t per = R / 4 + 1;
+  if (e >= Mp * per) return;
+  const int64_t row = e / per, c = e % per;
+  if (c < R / 4) {
+    // Loads in batches of 8 (all in flight together), sums in split order.
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.ks; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int sp = min(s0 + u, a.ks - 1);
+        v[u] = *reinterpret_cast<const f32x4*>(a.tpart + (sp * Mp + row) * R + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        if (s0 + u < a.ks) t += v[u];
+    }
+    uint2 o;
+    o.x = pack_bf16x2(t[0], t[1]);
+    o.y = pack_bf16x2(t[2], t[3]);
+    *reinterpret_cast<uint2*>(a.T + row * R + 4 * c) = o;
+  } else {
+    float x2 = 0.f, t2 = 0.f;
+    for (int s0 = 0; s0 < a.ks; s0 += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int sp = min(s0 + u, a.ks - 1);
+        v[u] = *reinterpret_cast<const float2*>(a.npart + (sp * Mp + row) * 2);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        if (s0 + u < a.ks) {
+          x2 += v[u].x;
+          t2 += v[u].y;
+        }
+    }
+    if (COMPRESS) {
+      const float sv = sqrtf(x2) / (sqrtf(t2) + a.eps);
+      a.s[row] = sv;
+      if (a.dbg_s != nullptr && row < a.M) a.dbg_s[row] = sv;
+    } else {
+      a.nx2[row] = x2;
+    }
+  }
+}
+
+// Selecting in the GEMM prologue costs about 28 VALU instructions per group of 4 in
+// every tile column, which stalls the matrix cores; selecting once in the pre-pass and
+// streaming the compressed operand is faster at every measured shape.
+int resolve_variant_bf16(int variant, int64_t M, int64_t N, int64_t K) {
+  (void)M; (void)N; (void)K;
+  if (variant == kVariantPrologue || variant == kVariantPrecompressed) return variant;
+  return kVariantPrecompressed;
+}
+
+size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R) {
+  (void)N;
+  const WsLayout a = ws_layout(M, K, R, false), b = ws_layout(M, K, R, true);
+  return a.total > b.total ? a.total : b.total;
+}
+
+hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
+                            float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream) {
+  const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
+  const WsLayout L = ws_layout(M, K, R, comp);
+  uint8_t* base = (uint8_t*)ws;
+  PrepArgs p{};
+  p.M = M; p.K = K; p.R = R; p.X = (const uint16_t*)X; p.LB = (const uint16_t*)LB; p.eps = eps;
+  p.T = (uint16_t*)(base + L.t);
+  const int64_t Mp = padded_rows(M);
+  const PrepSplit sp = prep_split(M, K);
+  p.ks = sp.ks;
+  p.kts = sp.kts;
+  p.tpart = (float*)(base + L.tpart);
+  p.npart = (float*)(base + L.npart);
+  if (comp) {
+    p.s = (float*)(base + L.norm);
+    p.cvals = base + L.cvals;
+    p.cidx = base + L.cidx;
+    p.dbg_idx = dbg_idx;
+    p.dbg_s = dbg_s;
+  } else {
+    p.nx2 = (float*)(base + L.norm);
+  }
+  const dim3 grid((unsigned)(Mp / kPrepRows), (unsigned)sp.ks), block(64 * kPrepWaves);
+#define RTL_PREP(C, RC) hipLaunchKernelGGL((prep_kernel<C, RC>), grid, block, 0, stream, p)
+  switch ((comp ? 8 : 0) + (int)(R / 32)) {
+    case 0: RTL_PREP(false, 0); break;
+    case 1: RTL_PREP(false, 1); break;
+    case 2: RTL_PREP(false, 2); break;
+    case 3: RTL_PREP(false, 3); break;
+    case 4: RTL_PREP(false, 4); break;
+    case 8: RTL_PREP(true, 0); break;
+    case 9: RTL_PREP(true, 1); break;
+    case 10: RTL_PREP(true, 2); break;
+    case 11: RTL_PREP(true, 3); break;
+    default: RTL_PREP(true, 4); break;
+  }
+#undef RTL_PREP
+  if (sp.ks > 1) {
+    const int64_t items = Mp * (R / 4 + 1);
+    const dim3 rgrid((unsigned)((items + 255) / 256)), rblock(256);
+    if (comp) hipLaunchKernelGGL((prep_reduce_kernel<true>), rgrid, rblock, 0, stream, p, Mp);
+    else hipLaunchKernelGGL((prep_reduce_kernel<false>), rgrid, rblock, 0, stream, p, Mp);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rtl

@@ -2,9 +2,10 @@
 
     python bench.py [--steps K] [--warmup W] [--layer attn_proj] [--all-layers]
 
-One step = one rtl_linear_fused call (the whole hot path: the rank-R down projection
-pass and the fused selection + sparse-MFMA + epilogue kernel) on one batch of synthetic
-inputs already resident in HBM.  Prints ONE JSON line with the effective throughput
+One step = one rtl_linear_fused call (the whole hot path: the pre-pass over X that
+forms the rank-R product, the row norms and the compressed 2:4 operand, then the
+sparse-MFMA GEMM with the rescale + low-rank epilogue) on one batch of synthetic inputs
+already resident in HBM.  Prints ONE JSON line with the effective throughput
 (dense-equivalent 2MNK plus rank-R FLOPs per second), the speedup over the in-library
 dense GEMM of the same shape, the roofline position of the dominant kernel (timed alone
 with HIP events on the stream it runs on) and the CPU oracle timed on a bounded sample.
@@ -26,7 +27,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_DENSE = 2.5e15   # MI355X dense bf16 MFMA FLOP/s (published)
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s (published)
-KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/rtl_device.h"]
+KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/bf16_common.h",
+                  "activation_sparse_gemm_amd/csrc/rtl_device.h"]
 
 
 def kernel_source_hash() -> str:
@@ -93,11 +95,13 @@ def cpu_baseline(d, target_s: float):
 
 
 VARIANTS = {"prologue": 1, "precompressed": 2}
+AUTO_RESOLVES_TO = "precompressed"   # what RTL_VARIANT_AUTO runs on gfx950 (include/rtl.h)
 
 
 def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "precompressed")):
-    """Times (seconds per call) of the whole layer per variant, of its two launches alone,
-    and of the dense GEMM of the same shape."""
+    """Times (seconds per call) of the whole layer through the default entry point
+    (rtl_linear_fused, variant AUTO), of each explicit variant whole and of its two
+    launches alone, and of the dense GEMM of the same shape."""
     import torch
 
     import activation_sparse_gemm_amd as rtl
@@ -112,6 +116,7 @@ def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "preco
         return d, t
     ws = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R),), dtype=torch.uint8,
                      device="cuda")
+    t["auto"] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws), steps, warmup)
     for vn in variants:
         v = VARIANTS[vn]
         t[vn] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws, variant=v), steps, warmup)
@@ -121,16 +126,41 @@ def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "preco
     return d, t
 
 
+def prep_bytes(M: int, K: int, R: int, variant: str) -> int:
+    """Algorithmic HBM bytes of the pre-pass: read X and L_B, write T (bf16) and one float
+    per row; the pre-compressed variant also writes the kept values (K/2 bf16 per row) and
+    their positions (K/16 bytes per row)."""
+    b = M * K * 2 + R * K * 2 + M * R * 2 + M * 4
+    if variant == "precompressed":
+        b += M * (K // 2) * 2 + M * K // 16
+    return b
+
+
+def copy_calibration(mib: int):
+    """A plain device copy of known size, for scaling the HBM byte counters of a profile
+    run: each launch reads and writes exactly `mib` MiB."""
+    import torch
+    src = torch.ones((mib << 19,), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layer", default="attn_proj")
-    ap.add_argument("--variant", default="prologue", choices=sorted(VARIANTS))
+    ap.add_argument("--variant", default="auto", choices=["auto", *sorted(VARIANTS)],
+                    help="entry point timed as the step (auto = rtl_linear_fused's own pick)")
     ap.add_argument("--all-layers", action="store_true", help="also time every bf16 layer (one line each, stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB three times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
@@ -142,26 +172,29 @@ def main():
     torch.cuda.set_device(0)
     import synth
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     d, t = bench_layer(args.layer, args.steps, args.warmup)
     M, K, N, R = d["M"], d["K"], d["N"], d["R"]
     variant = args.variant
+    kernel_variant = AUTO_RESOLVES_TO if variant == "auto" else variant
     flops = synth.LAYERS[args.layer].flops
     t_step = t[variant]
     value = flops / t_step / 1e12
-    # Dominant kernel = the variant's GEMM launch.  Algorithmic work per launch: the sparse
-    # multiply-adds actually performed (M N K / 2, i.e. M N K FLOP) plus the rank-R slice
-    # 2 M R N; priced against the dense bf16 MFMA peak (the sparse instruction retires the
-    # same number of real multiply-adds per cycle as the dense one).
-    t_main = t[variant + "_main"]
+    # Dominant kernel = the GEMM launch of the variant that runs.  Algorithmic work per
+    # launch: the multiply-adds the sparse instruction really performs (M N K / 2 of them,
+    # i.e. M N K FLOP) plus the rank-R slice 2 M R N, priced against the dense bf16 MFMA
+    # peak: the 2:4 instruction retires real multiply-adds at the dense instruction's rate
+    # (twice the dense-equivalent rate).
+    t_main = t[kernel_variant + "_main"]
     alg_flops = M * N * K + 2 * M * R * N
     achieved = alg_flops / t_main
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_DENSE / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_DENSE, "traffic": stored_traffic(args.layer, variant),
-                "kernel": f"gemm_kernel<256, {'kModeFused' if variant == 'prologue' else 'kModeComp'}>",
-                "kernel_us": t_main * 1e6}
-    prep_bytes = M * K * 2 + R * K * 2 + M * R * 2 + M * 4
-    if variant == "precompressed":
-        prep_bytes += M * K // 2 * 2 + M * K // 16
+                "frac": achieved / PEAK_BF16_DENSE, "traffic": stored_traffic(args.layer, kernel_variant),
+                "kernel": f"gemm_kernel ({kernel_variant} operand), {t_main * 1e6:.1f} us per launch",
+                "flop_per_launch": alg_flops}
+    pbytes = prep_bytes(M, K, R, kernel_variant)
+    t_prep = t[kernel_variant + "_prep"]
     out = {
         "metric": "effective TFLOP/s of fused 2:4 act-sparse+LoRA linear; speedup vs dense bf16",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -173,28 +206,32 @@ def main():
         "dense_tflops": 2 * M * N * K / t["dense"] / 1e12,
         "dense_ms": t["dense"] * 1e3,
         "frac_dense_peak": value * 1e12 / PEAK_BF16_DENSE,
-        "variants_ms": {vn: t[vn] * 1e3 for vn in VARIANTS},
-        "prep": {"us": t[variant + "_prep"] * 1e6, "bound": "hbm", "bytes": prep_bytes,
-                 "achieved_GBps": prep_bytes / t[variant + "_prep"] / 1e9},
+        "variants_ms": {vn: t[vn] * 1e3 for vn in ("auto", *VARIANTS)},
+        "prep": {"variant": kernel_variant, "us": t_prep * 1e6, "bound": "hbm", "bytes": pbytes,
+                 "achieved_GBps": pbytes / t_prep / 1e9, "frac": pbytes / t_prep / PEAK_HBM},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     if args.all_layers:
+        layers = []
         for name, lay in synth.LAYERS.items():
             if lay.dtype != "bf16":
                 continue
             dl, tl = bench_layer(name, max(5, args.steps // 5), 3)
             line = {"layer": name, "M": lay.M, "K": lay.K, "N": lay.N, "R": lay.R,
                     "dense_ms": tl["dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["dense"] / 1e12}
-            for vn in VARIANTS:
+            for vn in ("auto", *VARIANTS):
                 if vn in tl:
                     line[vn] = {"ms": tl[vn] * 1e3, "tflops": lay.flops / tl[vn] / 1e12,
-                                "speedup": tl["dense"] / tl[vn], "prep_us": tl[vn + "_prep"] * 1e6,
-                                "main_us": tl[vn + "_main"] * 1e6}
+                                "speedup": tl["dense"] / tl[vn]}
+                    if vn != "auto":
+                        line[vn].update(prep_us=tl[vn + "_prep"] * 1e6, main_us=tl[vn + "_main"] * 1e6)
             print(json.dumps(line), file=sys.stderr, flush=True)
+            layers.append(line)
             del dl
             torch.cuda.empty_cache()
+        out["layers"] = layers
     print(json.dumps(out), flush=True)
 
 

@@ -75,12 +75,13 @@ size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int6
  *   Y = s * (X~ W^T) + (X L_B^T) L_A^T
  *   X [M,K], W [N,K], LA [N,R], LB [R,K], Y [M,N]; R == 0 drops the low-rank branch
  *   (LA and LB may then be NULL).
- * bf16: a pre-pass over X forms the rank-R product T = X L_B^T (rounded to bf16) and
- *   the row norms in `workspace`; the sparse-MFMA GEMM then runs the 2-of-4 selection in
- *   its A-operand prologue (or reads it from the pre-pass, see rtl_variant), and its
- *   epilogue scales the accumulators by s and adds T L_A^T into them with one extra
- *   K = R MFMA slice before the single bf16 store of Y.  Limits: K % 64 == 0,
- *   R % 32 == 0, R <= 128.  M and N are arbitrary.
+ * bf16: a pre-pass over X forms the rank-R product T = X L_B^T (rounded to bf16), the
+ *   row norms and (default variant) the 2-of-4 selection, packed as the compressed
+ *   sparse-MFMA operand, in `workspace`; the sparse-MFMA GEMM then reads that operand
+ *   (or, in the prologue variant, selects in its own A-operand prologue, see
+ *   rtl_variant), and its epilogue scales the accumulators by s and adds T L_A^T into
+ *   them with one extra K = R MFMA slice before the single bf16 store of Y.  Limits:
+ *   K % 64 == 0, R % 32 == 0, R <= 128.  M and N are arbitrary.
  * fp32: same arithmetic in fp32 on the vector ALUs (no fp32 sparse MFMA exists).
  * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the GEMM
  *   writes the selection codes and s that its own prologue computed, in the layout of
@@ -94,7 +95,8 @@ rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64
 
 /* Where the bf16 path runs the 2-of-4 selection. */
 typedef enum {
-  RTL_VARIANT_AUTO = 0,          /* chosen from the shape */
+  RTL_VARIANT_AUTO = 0,          /* the library's pick: currently PRECOMPRESSED, faster at
+                                    every measured shape on gfx950 */
   RTL_VARIANT_PROLOGUE = 1,      /* in the A-operand prologue of the sparse-MFMA GEMM */
   RTL_VARIANT_PRECOMPRESSED = 2  /* in the pre-pass over X, which hands the GEMM the
                                     compressed operand (kept values + positions) */
