@@ -116,6 +116,8 @@ FUSED_SMALL = [
     (37, 300, 128, 128, "bf16"),
     (1, 16, 64, 64, "bf16"),
     (260, 272, 64, 0, "bf16"),
+    (300, 200, 1024, 64, "bf16"),   # pre-pass split over K (4 splits) with a reduction
+    (1, 48, 512, 32, "bf16"),       # one row, 2 K splits
     (64, 256, 256, 8, "f32"),
     (50, 70, 36, 5, "f32"),
     (33, 40, 64, 0, "f32"),
