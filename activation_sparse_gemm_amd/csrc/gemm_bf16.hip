@@ -73,7 +73,7 @@ void gemm_kernel(const GemmArgs a) {
   constexpr bool FUSED = MODE == kModeFused;
   constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
   __shared__ __attribute__((aligned(1024))) uint8_t wl[2 * TN * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : 2 * kALds];
+  __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
   __shared__ float sred[FUSED ? 256 : 1];
 
   int tm, tn;
@@ -227,14 +227,9 @@ void gemm_kernel(const GemmArgs a) {
   // One main-loop step on LDS buffer kt & 1.  Every memory operation in the loop is
   // issued unconditionally (the last steps reload the final K step), so the wait counts
   // the compiler derives are exact and loads stay in flight across the barrier.
-  auto step = [&](int kt, Raw& xsel, Raw& xload, WStage& wnext, WStage& wfar, AStage& anext, AStage& afar) {
-    const int buf = kt & 1;
-    load_w(min(kt + 2, KT - 1), wfar);
-    if (FUSED) load_raw(min(kt + 2, KT - 1), xload);
-    else load_at(min(kt + 2, KT - 1), afar);
-    AFrag cur;
-    if (FUSED) read_sel(buf, cur);
-    else read_a(buf, cur);
+  // The MFMAs of one K step: B fragments from LDS buffer `buf` (read two column blocks
+  // ahead), A fragments in `cur`.  Fused mode selects the next step's rows in between.
+  auto mma = [&](int kt, int buf, const AFrag& cur, Raw& xsel) {
     const uint8_t* base = wl + buf * TN * 128;
     auto read_b = [&](int nb) {
       const int n = (TN / 2) * wn + nb * 16 + r16;
@@ -274,13 +269,76 @@ void gemm_kernel(const GemmArgs a) {
         select_rb(min(kt + 1, KT - 1), xsel, nb == 0 ? 0 : 1, buf ^ 1, kt + 1 < KT);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // One main-loop step on LDS buffer kt & 1.  Every memory operation in the loop is
+  // issued unconditionally (the last steps reload the final K step), so the wait counts
+  // the compiler derives are exact and loads stay in flight across the barrier.
+  auto step = [&](int kt, Raw& xsel, Raw& xload, WStage& wnext, WStage& wfar, AStage& anext, AStage& afar) {
+    const int buf = kt & 1;
+    load_w(min(kt + 2, KT - 1), wfar);
+    if (FUSED) load_raw(min(kt + 2, KT - 1), xload);
+    else load_at(min(kt + 2, KT - 1), afar);
+    AFrag cur;
+    if (FUSED) read_sel(buf, cur);
+    else read_a(buf, cur);
+    mma(kt, buf, cur, xsel);
     store_w(wnext, buf ^ 1);
     if (!FUSED) store_at(anext, buf ^ 1);
     __syncthreads();
   };
 
+  // Pre-compressed mode: the operand is stored in MFMA register order, so each wave loads
+  // its own 64 rows straight into registers (one 16-byte load per lane and row block, one
+  // 8-byte load of position words), two K steps ahead; only W goes through LDS.
+  auto load_frag = [&](int kt, AFrag& f) {
+    const int64_t p = cpanel(wm);
+    const uint8_t* v = a.cvals + cvals_off(p, KT, kt) + lane * 16;
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(v + rb * 1024);
+    const uint2 w = *reinterpret_cast<const uint2*>(a.cidx + cidx_off(p, KT, kt) + lane * 8);
+    f.iw[0] = w.x;
+    f.iw[1] = w.y;
+  };
+  auto step_c = [&](int kt, WStage& wnext, WStage& wfar, const AFrag& cur, AFrag& afar, Raw& xdummy) {
+    const int buf = kt & 1;
+    load_w(min(kt + 2, KT - 1), wfar);
+    load_frag(min(kt + 2, KT - 1), afar);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(kt, buf, cur, xdummy);
+    store_w(wnext, buf ^ 1);
+    __syncthreads();
+  };
+
   Raw xr0, xr1;
   WStage w0, w1;
+  if constexpr (MODE == kModeComp) {
+    AFrag f0, f1, f2;
+    // same issue order as the loop (W, then A, per stage) so the wait counts at the loop
+    // head match the steady state
+    load_w(0, w0);
+    load_frag(0, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(min(1, KT - 1), w1);
+    load_frag(min(1, KT - 1), f1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(w0, 0);
+    __syncthreads();
+    // W stages alternate with period 2, A fragment sets with period 3.
+    for (int kt = 0; kt < KT; kt += 6) {
+      step_c(kt, w1, w0, f0, f2, xr0);
+      if (kt + 1 >= KT) break;
+      step_c(kt + 1, w0, w1, f1, f0, xr0);
+      if (kt + 2 >= KT) break;
+      step_c(kt + 2, w1, w0, f2, f1, xr0);
+      if (kt + 3 >= KT) break;
+      step_c(kt + 3, w0, w1, f0, f2, xr0);
+      if (kt + 4 >= KT) break;
+      step_c(kt + 4, w1, w0, f1, f0, xr0);
+      if (kt + 5 >= KT) break;
+      step_c(kt + 5, w0, w1, f2, f1, xr0);
+    }
+  } else {
   AStage a0, a1;
   load_w(0, w0);
   load_w(min(1, KT - 1), w1);
@@ -299,6 +357,7 @@ void gemm_kernel(const GemmArgs a) {
   for (int kt = 0; kt < KT; kt += 2) {
     step(kt, xr1, xr0, w1, w0, a1, a0);
     if (kt + 1 < KT) step(kt + 1, xr0, xr1, w0, w1, a0, a1);
+  }
   }
 
   if (SPARSE) {
