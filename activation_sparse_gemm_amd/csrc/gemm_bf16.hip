@@ -291,52 +291,79 @@ void gemm_kernel(const GemmArgs a) {
   // Pre-compressed mode: the operand is stored in MFMA register order, so each wave loads
   // its own 64 rows straight into registers (one 16-byte load per lane and row block, one
   // 8-byte load of position words), two K steps ahead; only W goes through LDS.
+  // The wave's panel through buffer resources (wave-uniform base, scalar step offsets).
+  const __amdgpu_buffer_rsrc_t cvres =
+      make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 4096);
+  const __amdgpu_buffer_rsrc_t cires =
+      make_rsrc(MODE == kModeComp ? a.cidx + cidx_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 512);
   auto load_frag = [&](int kt, AFrag& f) {
-    const int64_t p = cpanel(wm);
-    const uint8_t* v = a.cvals + cvals_off(p, KT, kt) + lane * 16;
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(v + rb * 1024);
-    const uint2 w = *reinterpret_cast<const uint2*>(a.cidx + cidx_off(p, KT, kt) + lane * 8);
-    f.iw[0] = w.x;
-    f.iw[1] = w.y;
+    for (int rb = 0; rb < 4; rb++)
+      f.v[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + rb * 1024), kt * 4096, 0);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
+    f.iw[0] = w[0];
+    f.iw[1] = w[1];
   };
+  // Pre-compressed step with the memory operations spread over the MFMA loop, so the
+  // load and LDS-write traffic of the step is issued evenly instead of in bursts at its
+  // ends: column block 0 issues the A loads for step kt + 1, block 1 the W loads for step
+  // kt + 2, and the last blocks write W stage kt + 1 (loaded a step ago) to the other LDS
+  // buffer.
   auto step_c = [&](int kt, WStage& wnext, WStage& wfar, const AFrag& cur, AFrag& afar, Raw& xdummy) {
+    (void)xdummy;
     const int buf = kt & 1;
-    load_w(min(kt + 2, KT - 1), wfar);
-    load_frag(min(kt + 2, KT - 1), afar);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(kt, buf, cur, xdummy);
-    store_w(wnext, buf ^ 1);
+    const uint8_t* base = wl + buf * TN * 128;
+    auto read_b = [&](int nb) {
+      const int n = (TN / 2) * wn + nb * 16 + r16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
+      return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    const int kn = min(kt + 2, KT - 1), ka = min(kt + 1, KT - 1);
+    u32x8 bq[3];
+    bq[0] = read_b(0);
+    bq[1] = read_b(1);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(nb + 2);
+      if (nb == 0) load_frag(ka, afar);
+      if (nb == 1) load_w(kn, wfar);
+      if (nb >= NB - WLD) {
+        const int i = nb - (NB - WLD);
+        *reinterpret_cast<u32x4*>(wl + (buf ^ 1) * TN * 128 + sw_off(srow + 64 * i, schunk)) = wnext[i];
+      }
+      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
+      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
+                                                             (int)cur.iw[0], 0, 0);
+      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1][0]), bv, acc[1][nb],
+                                                             (int)cur.iw[0], 0, 1);
+      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2][0]), bv, acc[2][nb],
+                                                             (int)cur.iw[1], 0, 0);
+      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3][0]), bv, acc[3][nb],
+                                                             (int)cur.iw[1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();
   };
 
   Raw xr0, xr1;
   WStage w0, w1;
   if constexpr (MODE == kModeComp) {
-    AFrag f0, f1, f2;
-    // same issue order as the loop (W, then A, per stage) so the wait counts at the loop
-    // head match the steady state
-    load_w(0, w0);
+    AFrag f0, f1;
+    // same issue order as the loop (A, then W) so the wait counts at the loop head match
+    // the steady state
     load_frag(0, f0);
     __builtin_amdgcn_sched_barrier(0);
+    load_w(0, w0);
+    __builtin_amdgcn_sched_barrier(0);
     load_w(min(1, KT - 1), w1);
-    load_frag(min(1, KT - 1), f1);
     __builtin_amdgcn_sched_barrier(0);
     store_w(w0, 0);
     __syncthreads();
-    // W stages alternate with period 2, A fragment sets with period 3.
-    for (int kt = 0; kt < KT; kt += 6) {
-      step_c(kt, w1, w0, f0, f2, xr0);
+    for (int kt = 0; kt < KT; kt += 2) {
+      step_c(kt, w1, w0, f0, f1, xr0);
       if (kt + 1 >= KT) break;
       step_c(kt + 1, w0, w1, f1, f0, xr0);
-      if (kt + 2 >= KT) break;
-      step_c(kt + 2, w1, w0, f2, f1, xr0);
-      if (kt + 3 >= KT) break;
-      step_c(kt + 3, w0, w1, f0, f2, xr0);
-      if (kt + 4 >= KT) break;
-      step_c(kt + 4, w1, w0, f1, f0, xr0);
-      if (kt + 5 >= KT) break;
-      step_c(kt + 5, w0, w1, f2, f1, xr0);
     }
   } else {
   AStage a0, a1;
