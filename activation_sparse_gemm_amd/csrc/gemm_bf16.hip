@@ -72,7 +72,7 @@ void gemm_kernel(const GemmArgs a) {
   constexpr bool SPARSE = MODE != kModeDense;
   constexpr bool FUSED = MODE == kModeFused;
   constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[2 * TN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[(MODE == kModeComp ? 3 : 2) * TN * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
   __shared__ float sred[FUSED ? 256 : 1];
 
@@ -304,33 +304,46 @@ void gemm_kernel(const GemmArgs a) {
     f.iw[0] = w[0];
     f.iw[1] = w[1];
   };
-  // Pre-compressed step with the memory operations spread over the MFMA loop, so the
-  // load and LDS-write traffic of the step is issued evenly instead of in bursts at its
-  // ends: column block 0 issues the A loads for step kt + 1, block 1 the W loads for step
-  // kt + 2, and the last blocks write W stage kt + 1 (loaded a step ago) to the other LDS
-  // buffer.
-  auto step_c = [&](int kt, WStage& wnext, WStage& wfar, const AFrag& cur, AFrag& afar, Raw& xdummy) {
-    (void)xdummy;
-    const int buf = kt & 1;
+  // Pre-compressed step kt on a 3-buffer LDS ring for W (buffer kt % 3), with the memory
+  // operations spread over the MFMA loop instead of bursting at the step boundaries:
+  // column block 0 issues the A loads for step kt + 1, block 1 the W loads for step
+  // kt + 3, and the last blocks write W stage kt + 2 (loaded a step ago) to buffer
+  // (kt + 2) % 3.  The first two B fragments of the step arrive in bp0, bp1, read at the
+  // end of the previous step: with three buffers, that buffer is complete before the
+  // barrier, so no LDS latency is exposed at the step boundary.
+  u32x8 bp0, bp1;
+  // K order: tile (tm, tn) starts at K step (tm + tn) % 8 and wraps around, so the
+  // workgroups of an XCD that share a W column block (same tn) or a compressed row panel
+  // (same tm) reach each K step at different times: one of them takes the L2 miss and the
+  // others find the lines in L2.  Logical step i (clamped to the last one) -> physical.
+#ifndef RTL_KSTAGGER
+#define RTL_KSTAGGER 8
+#endif
+  const int koff = (tm + tn) % RTL_KSTAGGER % KT;
+  auto kp = [&](int i) {
+    const int k = min(i, KT - 1) + koff;
+    return k >= KT ? k - KT : k;
+  };
+  auto read_bc = [&](int buf, int nb) {
     const uint8_t* base = wl + buf * TN * 128;
-    auto read_b = [&](int nb) {
-      const int n = (TN / 2) * wn + nb * 16 + r16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
-      return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    const int kn = min(kt + 2, KT - 1), ka = min(kt + 1, KT - 1);
+    const int n = (TN / 2) * wn + nb * 16 + r16;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
+    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto step_c = [&](int kt, int buf, WStage& wst, WStage& wfree, const AFrag& cur, AFrag& anext) {
+    const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
     u32x8 bq[3];
-    bq[0] = read_b(0);
-    bq[1] = read_b(1);
+    bq[0] = bp0;
+    bq[1] = bp1;
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
-      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(nb + 2);
-      if (nb == 0) load_frag(ka, afar);
-      if (nb == 1) load_w(kn, wfar);
+      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
+      if (nb == 0) load_frag(kp(kt + 1), anext);
+      if (nb == 1) load_w(kp(kt + 3), wfree);
       if (nb >= NB - WLD) {
         const int i = nb - (NB - WLD);
-        *reinterpret_cast<u32x4*>(wl + (buf ^ 1) * TN * 128 + sw_off(srow + 64 * i, schunk)) = wnext[i];
+        *reinterpret_cast<u32x4*>(wl + sbuf * TN * 128 + sw_off(srow + 64 * i, schunk)) = wst[i];
       }
       const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
@@ -343,6 +356,8 @@ void gemm_kernel(const GemmArgs a) {
                                                              (int)cur.iw[1], 0, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    bp0 = read_bc(nbuf, 0);
+    bp1 = read_bc(nbuf, 1);
     __syncthreads();
   };
 
@@ -352,18 +367,32 @@ void gemm_kernel(const GemmArgs a) {
     AFrag f0, f1;
     // same issue order as the loop (A, then W) so the wait counts at the loop head match
     // the steady state
-    load_frag(0, f0);
+    load_frag(kp(0), f0);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(0, w0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(min(1, KT - 1), w1);
+    load_w(kp(0), w0);
+    load_w(kp(1), w1);
     __builtin_amdgcn_sched_barrier(0);
     store_w(w0, 0);
+    store_w(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(kp(2), w0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-      step_c(kt, w1, w0, f0, f1, xr0);
+    bp0 = read_bc(0, 0);
+    bp1 = read_bc(0, 1);
+    // LDS buffers cycle with period 3, W register sets and A fragment sets with period 2.
+    for (int kt = 0; kt < KT; kt += 6) {
+      step_c(kt, 0, w0, w1, f0, f1);
       if (kt + 1 >= KT) break;
-      step_c(kt + 1, w0, w1, f1, f0, xr0);
+      step_c(kt + 1, 1, w1, w0, f1, f0);
+      if (kt + 2 >= KT) break;
+      step_c(kt + 2, 2, w0, w1, f0, f1);
+      if (kt + 3 >= KT) break;
+      step_c(kt + 3, 0, w1, w0, f1, f0);
+      if (kt + 4 >= KT) break;
+      step_c(kt + 4, 1, w0, w1, f0, f1);
+      if (kt + 5 >= KT) break;
+      step_c(kt + 5, 2, w1, w0, f1, f0);
     }
   } else {
   AStage a0, a1;
