@@ -62,6 +62,7 @@ constexpr int kGemmThreads = 512;
 constexpr int kXBlk = 64 * 16 + 64 * 2;   // fused: one row block of the compressed operand
 constexpr int kALds = kBM * 128;          // A tile bytes per LDS buffer (dense layout, the largest)
 constexpr int kCompIdx = 16384;           // pre-compressed: offset of the position words in an A buffer
+constexpr int kCompStage = 16384 + 2048;  // pre-compressed: one K step of the tile's four panels
 
 template <int MODE, bool DBG, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(2, 2)))
@@ -73,6 +74,10 @@ void gemm_kernel(const GemmArgs a) {
   constexpr bool FUSED = MODE == kModeFused;
   constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
   __shared__ __attribute__((aligned(1024))) uint8_t wl[(MODE == kModeComp ? 3 : 2) * TN * 128];
+  // Pre-compressed operand through LDS on 256-wide tiles (there the smaller VMEM traffic
+  // wins); straight to registers on 192-wide tiles (there the smaller LDS traffic wins).
+  constexpr bool CALDS = MODE == kModeComp && TN == 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t alc[CALDS ? 3 * kCompStage : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
   __shared__ float sred[FUSED ? 256 : 1];
 
@@ -331,6 +336,78 @@ void gemm_kernel(const GemmArgs a) {
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
     return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
+  // Compressed operand through LDS: thread t moves value chunks t and t + 512 (panels
+  // t / 256 and t / 256 + 2) and position word t (panel t / 128) of a K step; one LDS
+  // stage holds the tile's four panels (values, then position words).
+  struct AStg {
+    u32x4 v[2];
+    uint32_t i;
+  };
+  const int64_t pan4 = (int64_t)tm * 4;
+  const int64_t npan4 = min<int64_t>(4, (int64_t)a.n_panels - pan4);
+  const __amdgpu_buffer_rsrc_t tvres = make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(pan4, KT, 0) : nullptr, npan4 * KT * 4096);
+  const __amdgpu_buffer_rsrc_t tires = make_rsrc(MODE == kModeComp ? a.cidx + cidx_off(pan4, KT, 0) : nullptr, npan4 * KT * 512);
+  const uint32_t av0 = (uint32_t)((tid >> 8) * KT * 4096 + (tid & 255) * 16);
+  const uint32_t av1 = av0 + (uint32_t)(2 * KT * 4096);
+  const uint32_t ai = (uint32_t)((tid >> 7) * KT * 512 + (tid & 127) * 4);
+  const uint32_t lv0 = (uint32_t)((tid >> 8) * 4096 + (tid & 255) * 16), lv1 = lv0 + 2 * 4096;
+  const uint32_t li = (uint32_t)(16384 + (tid >> 7) * 512 + (tid & 127) * 4);
+  auto load_ast = [&](int kt, AStg& st) {
+    st.v[0] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av0, kt * 4096, 0);
+    st.v[1] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av1, kt * 4096, 0);
+    st.i = __builtin_amdgcn_raw_buffer_load_b32(tires, ai, kt * 512, 0);
+  };
+  auto store_ast = [&](const AStg& st, int buf) {
+    uint8_t* b = alc + buf * kCompStage;
+    *reinterpret_cast<u32x4*>(b + lv0) = st.v[0];
+    *reinterpret_cast<u32x4*>(b + lv1) = st.v[1];
+    *reinterpret_cast<uint32_t*>(b + li) = st.i;
+  };
+  auto read_afrag = [&](int buf, AFrag& f) {
+    const uint8_t* b = alc + buf * kCompStage;
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + wm * 4096 + rb * 1024 + lane * 16);
+    const uint2 w = *reinterpret_cast<const uint2*>(b + 16384 + wm * 512 + lane * 8);
+    f.iw[0] = w.x;
+    f.iw[1] = w.y;
+  };
+  // As step_c below, with the compressed operand staged through LDS like W: stage kt + 3
+  // (A and W) is loaded in the first column blocks, stage kt + 2 written to buffer
+  // (kt + 2) % 3 in the last ones, and the next step's A fragments and first B fragments
+  // are read from buffer (kt + 1) % 3 before the barrier.
+  auto step_ca = [&](int kt, int buf, WStage& wst, WStage& wfree, AStg& ast, AStg& afree, const AFrag& cur,
+                     AFrag& nxt) {
+    const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
+    u32x8 bq[3];
+    bq[0] = bp0;
+    bq[1] = bp1;
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
+      if (nb == 0) load_ast(kp(kt + 3), afree);
+      if (nb == 1) load_w(kp(kt + 3), wfree);
+      if (nb == NB - WLD - 1) store_ast(ast, sbuf);
+      if (nb >= NB - WLD) {
+        const int i = nb - (NB - WLD);
+        *reinterpret_cast<u32x4*>(wl + sbuf * TN * 128 + sw_off(srow + 64 * i, schunk)) = wst[i];
+      }
+      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
+      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
+                                                             (int)cur.iw[0], 0, 0);
+      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1][0]), bv, acc[1][nb],
+                                                             (int)cur.iw[0], 0, 1);
+      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2][0]), bv, acc[2][nb],
+                                                             (int)cur.iw[1], 0, 0);
+      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3][0]), bv, acc[3][nb],
+                                                             (int)cur.iw[1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bp0 = read_bc(nbuf, 0);
+    bp1 = read_bc(nbuf, 1);
+    read_afrag(nbuf, nxt);
+    __syncthreads();
+  };
+
   auto step_c = [&](int kt, int buf, WStage& wst, WStage& wfree, const AFrag& cur, AFrag& anext) {
     const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
     u32x8 bq[3];
@@ -363,7 +440,44 @@ void gemm_kernel(const GemmArgs a) {
 
   Raw xr0, xr1;
   WStage w0, w1;
-  if constexpr (MODE == kModeComp) {
+  if constexpr (CALDS) {
+    AFrag f0, f1;
+    AStg s0, s1;
+    // same issue order as the loop (A, then W, per stage) so the wait counts at the loop
+    // head match the steady state
+    load_ast(kp(0), s0);
+    load_w(kp(0), w0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_ast(kp(1), s1);
+    load_w(kp(1), w1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_ast(s0, 0);
+    store_w(w0, 0);
+    store_ast(s1, 1);
+    store_w(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_ast(kp(2), s0);
+    load_w(kp(2), w0);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    bp0 = read_bc(0, 0);
+    bp1 = read_bc(0, 1);
+    read_afrag(0, f0);
+    // LDS buffers cycle with period 3, register sets with period 2.
+    for (int kt = 0; kt < KT; kt += 6) {
+      step_ca(kt, 0, w0, w1, s0, s1, f0, f1);
+      if (kt + 1 >= KT) break;
+      step_ca(kt + 1, 1, w1, w0, s1, s0, f1, f0);
+      if (kt + 2 >= KT) break;
+      step_ca(kt + 2, 2, w0, w1, s0, s1, f0, f1);
+      if (kt + 3 >= KT) break;
+      step_ca(kt + 3, 0, w1, w0, s1, s0, f1, f0);
+      if (kt + 4 >= KT) break;
+      step_ca(kt + 4, 1, w0, w1, s0, s1, f0, f1);
+      if (kt + 5 >= KT) break;
+      step_ca(kt + 5, 2, w1, w0, s1, s0, f1, f0);
+    }
+  } else if constexpr (MODE == kModeComp) {
     AFrag f0, f1;
     // same issue order as the loop (A, then W) so the wait counts at the loop head match
     // the steady state

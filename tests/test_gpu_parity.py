@@ -189,6 +189,24 @@ def test_fused_workload_layers(name, variant):
     assert np.all(np.abs(gs[nz] - ref["s"][nz]) <= tol_s(d['K']) * ref["s"][nz])
 
 
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+def test_fused_wide_tiles_ragged(variant):
+    # 4000 x 4000 output: 16 x 16 tiles of 256 x 256 (one wave of workgroups) beat 16 x 21
+    # tiles of 256 x 192, so this runs the 256-wide kernels, with ragged M and N tails.
+    lay = synth.Layer("t", 4000, 512, 4000, 64, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=6161)
+    log(f"[fused-wide] M=4000 N=4000 K=512 R=64 variant={variant}")
+    Y, dbg_idx, dbg_s = run_fused(d, variant=variant)
+    ref = oracle.sparsify(d["X"])
+    assert np.array_equal(to_host(dbg_idx), ref["idx"])
+    rows = np.unique(np.concatenate([sample_rows(4000, n=64), np.arange(3840, 4000, 7)]))
+    Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+    y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
+    err = row_rel_err(y, Yref)
+    log(f"  sampled {len(rows)} rows, max row rel err {err:.3e}")
+    assert err <= TOL_Y["bf16"]
+
+
 # ------------------------------------------------------------------ rtl_linear_dense_ref
 
 @pytest.mark.parametrize("case", [(300, 520, 192, "bf16"), (1, 16, 64, "bf16"), (64, 256, 256, "f32"),
