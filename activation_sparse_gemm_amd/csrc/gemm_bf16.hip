@@ -321,10 +321,7 @@ void gemm_kernel(const GemmArgs a) {
   // workgroups of an XCD that share a W column block (same tn) or a compressed row panel
   // (same tm) reach each K step at different times: one of them takes the L2 miss and the
   // others find the lines in L2.  Logical step i (clamped to the last one) -> physical.
-#ifndef RTL_KSTAGGER
-#define RTL_KSTAGGER 8
-#endif
-  const int koff = (tm + tn) % RTL_KSTAGGER % KT;
+  const int koff = (tm + tn) % 8 % KT;
   auto kp = [&](int i) {
     const int k = min(i, KT - 1) + koff;
     return k >= KT ? k - KT : k;
@@ -372,7 +369,7 @@ void gemm_kernel(const GemmArgs a) {
     f.iw[1] = w.y;
   };
   // As step_c below, with the compressed operand staged through LDS like W: stage kt + 3
-  // (A and W) is loaded in the first column blocks, stage kt + 2 written to buffer
+  // (A and W) is loaded in early column blocks, stage kt + 2 written to buffer
   // (kt + 2) % 3 in the last ones, and the next step's A fragments and first B fragments
   // are read from buffer (kt + 1) % 3 before the barrier.
   auto step_ca = [&](int kt, int buf, WStage& wst, WStage& wfree, AStg& ast, AStg& afree, const AFrag& cur,
@@ -384,8 +381,9 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
-      if (nb == 0) load_ast(kp(kt + 3), afree);
-      if (nb == 1) load_w(kp(kt + 3), wfree);
+      // loads a few column blocks into the step, away from the burst after the barrier
+      if (nb == 2) load_ast(kp(kt + 3), afree);
+      if (nb == 4) load_w(kp(kt + 3), wfree);
       if (nb == NB - WLD - 1) store_ast(ast, sbuf);
       if (nb >= NB - WLD) {
         const int i = nb - (NB - WLD);

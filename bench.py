@@ -61,12 +61,18 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_loop(fn, steps: int, warmup: int) -> float:
-    """Mean seconds per call of fn over `steps` calls after `warmup`, timed with events
-    on the current stream (the stream the library launches on)."""
+def time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.05) -> float:
+    """Mean seconds per call of fn over `steps` calls after `warmup` calls (and at least
+    `min_warm_s` seconds of them, so the clocks have settled), timed with events on the
+    current stream (the stream the library launches on)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_warm_s:
         fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
