@@ -436,9 +436,71 @@ void gemm_kernel(const GemmArgs a) {
     __syncthreads();
   };
 
+  // Dense step with the memory operations spread over the MFMA loop (as in the
+  // pre-compressed steps): column block 1 issues the A loads and block 2 the W loads for
+  // step kt + 2, and the last blocks write stage kt + 1 (loaded a step ago) to the other
+  // LDS buffer.  K order staggered per tile as above.
+  auto step_d = [&](int kt, WStage& wnext, WStage& wfar, AStage& anext, AStage& afar) {
+    const int buf = kt & 1;
+    AFrag cur;
+    read_a(buf, cur);
+    const uint8_t* base = wl + buf * TN * 128;
+    auto read_b = [&](int nb) {
+      const int n = (TN / 2) * wn + nb * 16 + r16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
+      return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    u32x8 bq[3];
+    bq[0] = read_b(0);
+    bq[1] = read_b(1);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(nb + 2);
+      if (nb == 1) load_at(kp(kt + 2), afar);
+      if (nb == 2) load_w(kp(kt + 2), wfar);
+      if (nb >= NB - ALD) {
+        const int i = nb - (NB - ALD);
+        *reinterpret_cast<u32x4*>(al + (buf ^ 1) * kALds + sw_off(srow + 64 * i, schunk)) = anext[i];
+      }
+      if (nb >= NB - WLD) {
+        const int i = nb - (NB - WLD);
+        *reinterpret_cast<u32x4*>(wl + (buf ^ 1) * TN * 128 + sw_off(srow + 64 * i, schunk)) = wnext[i];
+      }
+      const u32x8 bb = bq[nb % 3];
+      const u32x4 b0 = {bb[0], bb[1], bb[2], bb[3]}, b1 = {bb[4], bb[5], bb[6], bb[7]};
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) {
+        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[rb][0]),
+                                                              __builtin_bit_cast(bf16x8, b0), acc[rb][nb], 0, 0, 0);
+        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[rb][1]),
+                                                              __builtin_bit_cast(bf16x8, b1), acc[rb][nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+
   Raw xr0, xr1;
   WStage w0, w1;
-  if constexpr (CALDS) {
+  if constexpr (MODE == kModeDense) {
+    AStage a0, a1;
+    // same issue order as the loop (A, then W) so the wait counts at the loop head match
+    load_at(kp(0), a0);
+    load_w(kp(0), w0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_at(kp(1), a1);
+    load_w(kp(1), w1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_at(a0, 0);
+    store_w(w0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+      step_d(kt, w1, w0, a1, a0);
+      if (kt + 1 >= KT) break;
+      step_d(kt + 1, w0, w1, a0, a1);
+    }
+  } else if constexpr (CALDS) {
     AFrag f0, f1;
     AStg s0, s1;
     // same issue order as the loop (A, then W, per stage) so the wait counts at the loop
