@@ -684,6 +684,193 @@ void gemm_kernel(const GemmArgs a) {
   }
 }
 
+// Pre-compressed GEMM with two workgroups per CU: 4 waves (one per SIMD) on a 256 x TW
+// output tile, wave w owns rows 64w..64w+63 and all TW columns.  The two workgroups on a
+// CU reach their barriers at different times, so one's matrix-core work covers the
+// other's step boundary.  Per step each wave loads its own compressed rows straight into
+// registers (no sharing, no duplication) and the workgroup stages a TW x 64 W tile
+// through a 3-buffer LDS ring, with the same interleaving and K stagger as gemm_kernel.
+constexpr int kHalfThreads = 256;
+
+template <int TW>
+__global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads), amdgpu_waves_per_eu(2, 2)))
+void half_kernel(const GemmArgs a) {
+  static_assert(TW == 128 || TW == 96, "tile widths");
+  constexpr int NB = TW / 16;                   // 16-column blocks per wave
+  constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[3 * TW * 128];
+
+  int tm, tn;
+  tile_coords(a.tiles_m, a.tiles_n, tm, tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * TW;
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int KT = (int)(K / kBK);
+
+  // W staging: thread t moves chunks (row t/8 + 32i, k chunk t%8), i < WLD; columns past
+  // N read as zeros.
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(a.W + n0 * K, (N - n0) * K * 2);
+  const int srow = tid >> 3, schunk = tid & 7;
+  const uint32_t w_voff = (uint32_t)(srow * K * 2 + 16 * schunk);
+  typedef u32x4 WStage[WLD];
+  auto load_w = [&](int kt, WStage& st) {
+#pragma unroll
+    for (int i = 0; i < WLD; i++)
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0);
+  };
+  auto store_w = [&](const WStage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < WLD; i++)
+      *reinterpret_cast<u32x4*>(wl + buf * TW * 128 + sw_off(srow + 32 * i, schunk)) = st[i];
+  };
+
+  // The wave's 64-row panel of the compressed operand (register order).
+  struct AF {
+    u32x4 v[4];
+    uint32_t iw[2];
+  };
+  const int64_t pan = min((int64_t)tm * 4 + wave, (int64_t)a.n_panels - 1);
+  const __amdgpu_buffer_rsrc_t cvres = make_rsrc(a.cvals + cvals_off(pan, KT, 0), (int64_t)KT * 4096);
+  const __amdgpu_buffer_rsrc_t cires = make_rsrc(a.cidx + cidx_off(pan, KT, 0), (int64_t)KT * 512);
+  auto load_frag = [&](int kt, AF& f) {
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++)
+      f.v[rb] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + rb * 1024), kt * 4096, 0);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
+    f.iw[0] = w[0];
+    f.iw[1] = w[1];
+  };
+  auto read_b = [&](int buf, int nb) {
+    const uint8_t* base = wl + buf * TW * 128;
+    const int n = nb * 16 + r16;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
+    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int koff = (tm + tn) % 8 % KT;
+  auto kp = [&](int i) {
+    const int k = min(i, KT - 1) + koff;
+    return k >= KT ? k - KT : k;
+  };
+  u32x8 bp0, bp1;
+  // Step kt on LDS buffer kt % 3: A for step kt + 1 loads in column block 0, W for step
+  // kt + 3 in block 1, W stage kt + 2 goes to buffer (kt + 2) % 3 in the last blocks, and
+  // the next step's first B fragments are read before the barrier.
+  auto step = [&](int kt, int buf, WStage& wst, WStage& wfree, const AF& cur, AF& anext) {
+    const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
+    u32x8 bq[3];
+    bq[0] = bp0;
+    bq[1] = bp1;
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(buf, nb + 2);
+      if (nb == 0) load_frag(kp(kt + 1), anext);
+      if (nb == 1) load_w(kp(kt + 3), wfree);
+      if (nb >= NB - WLD) {
+        const int i = nb - (NB - WLD);
+        *reinterpret_cast<u32x4*>(wl + sbuf * TW * 128 + sw_off(srow + 32 * i, schunk)) = wst[i];
+      }
+      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
+      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0]), bv, acc[0][nb],
+                                                             (int)cur.iw[0], 0, 0);
+      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1]), bv, acc[1][nb],
+                                                             (int)cur.iw[0], 0, 1);
+      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2]), bv, acc[2][nb],
+                                                             (int)cur.iw[1], 0, 0);
+      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3]), bv, acc[3][nb],
+                                                             (int)cur.iw[1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bp0 = read_b(nbuf, 0);
+    bp1 = read_b(nbuf, 1);
+    __syncthreads();
+  };
+
+  WStage w0, w1;
+  AF f0, f1;
+  load_frag(kp(0), f0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(kp(0), w0);
+  load_w(kp(1), w1);
+  __builtin_amdgcn_sched_barrier(0);
+  store_w(w0, 0);
+  store_w(w1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(kp(2), w0);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  bp0 = read_b(0, 0);
+  bp1 = read_b(0, 1);
+  for (int kt = 0; kt < KT; kt += 6) {
+    step(kt, 0, w0, w1, f0, f1);
+    if (kt + 1 >= KT) break;
+    step(kt + 1, 1, w1, w0, f1, f0);
+    if (kt + 2 >= KT) break;
+    step(kt + 2, 2, w0, w1, f0, f1);
+    if (kt + 3 >= KT) break;
+    step(kt + 3, 0, w1, w0, f1, f0);
+    if (kt + 4 >= KT) break;
+    step(kt + 4, 1, w0, w1, f0, f1);
+    if (kt + 5 >= KT) break;
+    step(kt + 5, 2, w1, w0, f1, f0);
+  }
+
+  // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
+  // accumulator rows 16rb + 4q + j (lane 4q + j); the rank-R slice acc += (T / s) L_A^T,
+  // then Y = s * acc (a zero row has s = 0 and T = 0; its T / s is taken as 0).
+  float s_row[4], inv_s[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+    const int64_t row = m0 + 64 * wave + 16 * rb + r16;
+    s_row[rb] = a.s[row < M ? row : M - 1];
+    inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
+  }
+  const int64_t R = a.R;
+  for (int kk = 0; kk < (int)(R / 32); kk++) {
+    u32x4 ta[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+      const int64_t row = m0 + 64 * wave + 16 * rb + r16;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
+#pragma unroll
+      for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const int64_t col = n0 + nb * 16 + r16;
+      const u32x4 la = *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++)
+        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
+                                                              __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float sj = __shfl(s_row[rb], 4 * q + j, 64);
+      const int64_t row = m0 + 64 * wave + 16 * rb + 4 * q + j;
+      if (row >= M) continue;
+      uint16_t* yrow = a.Y + row * N;
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        const int64_t col = n0 + nb * 16 + r16;
+        if (col < N) yrow[col] = (uint16_t)f32_to_bf16_bits(acc[rb][nb][j] * sj);
+      }
+    }
+  }
+}
+
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
                           void* Y, float eps, int tn_width) {
   GemmArgs g{};
@@ -708,6 +895,18 @@ static int choose_tn(int64_t M, int64_t N) {
     if (cost < best) { best = cost; pick = tn; }
   }
   return pick;
+}
+
+// Pre-compressed GEMM: two 256 x 128 workgroups per CU instead of one 256 x TN one, when
+// that gives the busiest CU less work (128 columns per workgroup, a little dearer per
+// column than the 256-wide kernel).
+static bool use_half_tiles(int64_t M, int64_t N) {
+  const int64_t tm = (M + kBM - 1) / kBM;
+  const int tn = choose_tn(M, N);
+  const int64_t full = tm * ((N + tn - 1) / tn), half = tm * ((N + 127) / 128);
+  const double full_cost = (double)((full + 255) / 256) * tn * (tn == 192 ? 1.05 : 1.0);
+  const double half_cost = (double)((half + 255) / 256) * 128 * 1.08;
+  return half_cost < full_cost;
 }
 
 template <int TN>
@@ -739,6 +938,12 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     g.nx2 = (const float*)(base + L.norm);
     g.dbg_idx = dbg_idx;
     g.dbg_s = dbg_s;
+  }
+  if (comp && use_half_tiles(M, N)) {
+    GemmArgs h = g;
+    h.tiles_n = (int)((N + 127) / 128);
+    hipLaunchKernelGGL((half_kernel<128>), dim3((unsigned)(h.tiles_m * h.tiles_n)), dim3(kHalfThreads), 0, stream, h);
+    return hipGetLastError();
   }
   if (tn == 192) launch_main_tn<192>(comp, g, dbg_idx, stream);
   else launch_main_tn<256>(comp, g, dbg_idx, stream);

@@ -189,17 +189,24 @@ def test_fused_workload_layers(name, variant):
     assert np.all(np.abs(gs[nz] - ref["s"][nz]) <= tol_s(d['K']) * ref["s"][nz])
 
 
+# Output shapes that make the library pick each GEMM tiling (ragged M and N tails in all):
+#   4000 x 4000: 16 x 16 tiles of 256 x 256, one per CU (256-wide kernels);
+#   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels);
+# the small cases above get two 256 x 128 workgroups per CU (pre-compressed variant).
+WIDE = [(4000, 4000, 512), (2000, 6100, 256)]
+
+
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
-def test_fused_wide_tiles_ragged(variant):
-    # 4000 x 4000 output: 16 x 16 tiles of 256 x 256 (one wave of workgroups) beat 16 x 21
-    # tiles of 256 x 192, so this runs the 256-wide kernels, with ragged M and N tails.
-    lay = synth.Layer("t", 4000, 512, 4000, 64, "bf16", "heavy", 0.08)
-    d = synth.make_layer(lay, seed_base=6161)
-    log(f"[fused-wide] M=4000 N=4000 K=512 R=64 variant={variant}")
+@pytest.mark.parametrize("shape", WIDE, ids=lambda c: "x".join(map(str, c)))
+def test_fused_wide_tiles_ragged(shape, variant):
+    M, N, K = shape
+    lay = synth.Layer("t", M, K, N, 64, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=6161 + N)
+    log(f"[fused-wide] M={M} N={N} K={K} R=64 variant={variant}")
     Y, dbg_idx, dbg_s = run_fused(d, variant=variant)
     ref = oracle.sparsify(d["X"])
     assert np.array_equal(to_host(dbg_idx), ref["idx"])
-    rows = np.unique(np.concatenate([sample_rows(4000, n=64), np.arange(3840, 4000, 7)]))
+    rows = np.unique(np.concatenate([sample_rows(M, n=64), np.arange(M - 160, M, 7)]))
     Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
     y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
     err = row_rel_err(y, Yref)
