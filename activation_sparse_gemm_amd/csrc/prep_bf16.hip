@@ -31,7 +31,7 @@ struct PrepArgs {
 // row (k = 16q..16q+15 of a step), which serve both the selection (four groups of 4) and,
 // read as two 8-wide K slices, the A operand of the rank-R product; the L_B slice of each
 // step passes through LDS once per workgroup and is shared by its 128 rows.  X and L_B
-// are loaded two steps ahead.  With several K splits the partial T and norms go to the
+// are loaded three steps ahead.  With several K splits the partial T and norms go to the
 // workspace and prep_reduce_kernel sums them in a fixed order.
 template <bool COMPRESS, int RC>  // RC = R / 32
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a) {
@@ -126,24 +126,29 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a)
   };
 
   // Step i of the split works on K step kt0 + i with L_B in LDS buffer i % 2; stage
-  // i + 2 is loaded while step i computes, and stage i + 1's L_B goes to the other buffer
-  // before the step's barrier.
+  // i + 3 is loaded while step i computes (four register stages), and stage i + 1's L_B
+  // goes to the other buffer before the step's barrier.
   auto kc = [&](int i) { return kt0 + min(i, nk - 1); };
-  Stage s0, s1, s2;
+  Stage s0, s1, s2, s3;
   load(kc(0), s0);
   load(kc(1), s1);
+  load(kc(2), s2);
   store_lb(s0, 0);
   __syncthreads();
   auto step = [&](int i, Stage& cur, Stage& nxt, Stage& far) {
-    load(kc(i + 2), far);
+    load(kc(i + 3), far);
     compute(kc(i), cur, i & 1, i < nk);
     store_lb(nxt, (i + 1) & 1);
     __syncthreads();
   };
-  for (int i = 0; i < nk; i += 3) {
-    step(i, s0, s1, s2);
+  for (int i = 0; i < nk; i += 4) {
+    step(i, s0, s1, s3);
+    if (i + 1 >= nk) break;
     step(i + 1, s1, s2, s0);
-    step(i + 2, s2, s0, s1);
+    if (i + 2 >= nk) break;
+    step(i + 2, s2, s3, s1);
+    if (i + 3 >= nk) break;
+    step(i + 3, s3, s0, s2);
   }
 
   // Norms over the 4 lanes of a row.
