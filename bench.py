@@ -118,6 +118,9 @@ def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "preco
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     t = {"dense": time_loop(lambda: rtl.rtl_linear_dense_ref(X, W, Y=Yd), steps, warmup)}
+    # the vendor library's dense GEMM of the same shape (torch.matmul -> hipBLASLt), for context
+    Wt = W.t()
+    t["dense_torch"] = time_loop(lambda: torch.matmul(X, Wt, out=Yd), steps, warmup)
     if synth.LAYERS[name].dense_only:
         return d, t
     ws = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R),), dtype=torch.uint8,
@@ -211,6 +214,8 @@ def main():
         "speedup_vs_dense": t["dense"] / t_step,
         "dense_tflops": 2 * M * N * K / t["dense"] / 1e12,
         "dense_ms": t["dense"] * 1e3,
+        "torch_matmul_ms": t["dense_torch"] * 1e3,
+        "speedup_vs_torch_matmul": t["dense_torch"] / t_step,
         "frac_dense_peak": value * 1e12 / PEAK_BF16_DENSE,
         "variants_ms": {vn: t[vn] * 1e3 for vn in ("auto", *VARIANTS)},
         "prep": {"variant": kernel_variant, "us": t_prep * 1e6, "bound": "hbm", "bytes": pbytes,
@@ -226,11 +231,12 @@ def main():
                 continue
             dl, tl = bench_layer(name, max(5, args.steps // 5), 3)
             line = {"layer": name, "M": lay.M, "K": lay.K, "N": lay.N, "R": lay.R,
-                    "dense_ms": tl["dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["dense"] / 1e12}
+                    "dense_ms": tl["dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["dense"] / 1e12,
+                    "torch_matmul_ms": tl["dense_torch"] * 1e3}
             for vn in ("auto", *VARIANTS):
                 if vn in tl:
                     line[vn] = {"ms": tl[vn] * 1e3, "tflops": lay.flops / tl[vn] / 1e12,
-                                "speedup": tl["dense"] / tl[vn]}
+                                "speedup": tl["dense"] / tl[vn], "speedup_vs_torch": tl["dense_torch"] / tl[vn]}
                     if vn != "auto":
                         line[vn].update(prep_us=tl[vn + "_prep"] * 1e6, main_us=tl[vn + "_main"] * 1e6)
             print(json.dumps(line), file=sys.stderr, flush=True)

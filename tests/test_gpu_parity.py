@@ -191,9 +191,10 @@ def test_fused_workload_layers(name, variant):
 
 # Output shapes that make the library pick each GEMM tiling (ragged M and N tails in all):
 #   4000 x 4000: 16 x 16 tiles of 256 x 256, one per CU (256-wide kernels);
-#   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels);
+#   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels; K = 320 is an
+#                odd number of 64-wide steps);
 # the small cases above get two 256 x 128 workgroups per CU (pre-compressed variant).
-WIDE = [(4000, 4000, 512), (2000, 6100, 256)]
+WIDE = [(4000, 4000, 512), (2000, 6100, 256), (2000, 6100, 320)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
