@@ -39,29 +39,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ int64_t cvals_off(int64_t p, int KT, int kt) { return (p * KT + kt) * 4096; }
 __device__ __forceinline__ int64_t cidx_off(int64_t p, int KT, int kt) { return (p * KT + kt) * 512; }
 
-constexpr int kPrepWaves = 8;                 // waves per pre-pass workgroup, one 16-row block each
-constexpr int kPrepRows = 16 * kPrepWaves;    // rows per pre-pass workgroup
+constexpr int kPrepRows = 128;                // row padding of the pre-pass outputs
 
 inline int64_t padded_rows(int64_t M) { return (M + kPrepRows - 1) / kPrepRows * kPrepRows; }
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Pre-pass K split: enough (row tile, K split) workgroups to cover the chip, at least
-// kPrepMinSteps K steps per split.
-#ifndef RTL_PREP_TARGET_WGS
-#define RTL_PREP_TARGET_WGS 256
-#endif
-constexpr int kPrepTargetWgs = RTL_PREP_TARGET_WGS;
+// Pre-pass decomposition.  Rows are padded to 128.  When 128-row workgroups (8 waves)
+// already cover the chip, each takes a whole row tile and all of K; otherwise 64-row
+// workgroups (4 waves, two per CU) split K so that about 512 of them run, each with at
+// least kPrepMinSteps K steps, and a small kernel sums the splits.
 constexpr int kPrepMinSteps = 4;
 struct PrepSplit {
-  int ks, kts;
+  int waves, ks, kts;
 };
 inline PrepSplit prep_split(int64_t M, int64_t K) {
-  const int64_t tiles = padded_rows(M) / kPrepRows, KT = K / kBK;
-  int64_t ks = (kPrepTargetWgs + tiles - 1) / tiles;
+  const int64_t Mp = padded_rows(M), KT = K / kBK;
+  if (Mp / kPrepRows >= 256) return PrepSplit{8, 1, (int)KT};
+  const int64_t tiles = Mp / 64;
+  int64_t ks = (512 + tiles - 1) / tiles;
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, KT / kPrepMinSteps));
   ks = std::max<int64_t>(ks, 1);
   const int64_t kts = (KT + ks - 1) / ks;
-  return PrepSplit{(int)((KT + kts - 1) / kts), (int)kts};
+  return PrepSplit{4, (int)((KT + kts - 1) / kts), (int)kts};
 }
 
 // Workspace: T [Mp,R] bf16 | nx2 or s [Mp] f32 | (pre-compressed) values, position words

@@ -26,17 +26,18 @@ struct PrepArgs {
   int kts;            // K steps per split
 };
 
-// Pre-pass over X.  Workgroup (row tile, K split): 8 waves, wave w the 16-row block w of
-// a 128-row tile, all K steps of the split.  Every lane holds 16 consecutive values of its
+// Pre-pass over X.  Workgroup (row tile, K split): PW waves, wave w the 16-row block w of
+// a 16 PW-row tile, all K steps of the split.  Every lane holds 16 consecutive values of its
 // row (k = 16q..16q+15 of a step), which serve both the selection (four groups of 4) and,
 // read as two 8-wide K slices, the A operand of the rank-R product; the L_B slice of each
-// step passes through LDS once per workgroup and is shared by its 128 rows.  X and L_B
+// step passes through LDS once per workgroup and is shared by its rows.  X and L_B
 // are loaded three steps ahead.  With several K splits the partial T and norms go to the
 // workspace and prep_reduce_kernel sums them in a fixed order.
-template <bool COMPRESS, int RC>  // RC = R / 32
-__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a) {
+template <bool COMPRESS, int RC, int PW>  // RC = R / 32, PW waves = 16-row blocks per workgroup
+__global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   constexpr int R = 32 * RC, CB = 2 * RC;
-  constexpr int LCH = RC > 0 ? (R * 8 + 511) / 512 : 1;  // 16-byte L_B chunks per thread per step
+  constexpr int NT = 64 * PW;
+  constexpr int LCH = RC > 0 ? (R * 8 + NT - 1) / NT : 1;  // 16-byte L_B chunks per thread per step
   __shared__ __attribute__((aligned(1024))) uint8_t lb[2][RC > 0 ? R * 128 : 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a)
   const int KT = (int)(K / kBK);
   const int split = blockIdx.y;
   const int kt0 = split * a.kts, nk = min(a.kts, KT - kt0);
-  const int64_t rbk = (int64_t)blockIdx.x * kPrepWaves + wave;  // global 16-row block
+  const int64_t rbk = (int64_t)blockIdx.x * PW + wave;  // global 16-row block
   const int64_t row = rbk * 16 + r16;
   const bool row_ok = row < a.M;
   const int64_t p = rbk >> 2;
@@ -62,21 +63,21 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a)
     u32x4 x[2];
     u32x4 l[LCH];
   };
-  // L_B chunk id = tid + 512 j of the step's [R][64] slice: row id / 8, k chunk id % 8.
+  // L_B chunk id = tid + NT j of the step's [R][64] slice: row id / 8, k chunk id % 8.
   auto load = [&](int kt, Stage& st) {
     const int so = kt * kBK * 2;
     st.x[0] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff, so, 0);
     st.x[1] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff + 16, so, 0);
 #pragma unroll
     for (int j = 0; j < LCH; j++) {
-      const int id = (tid + 512 * j) % (RC > 0 ? R * 8 : 8);
+      const int id = (tid + NT * j) % (RC > 0 ? R * 8 : 8);
       st.l[j] = __builtin_amdgcn_raw_buffer_load_b128(lres, (uint32_t)((id >> 3) * K * 2 + 16 * (id & 7)), so, 0);
     }
   };
   auto store_lb = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int j = 0; j < LCH; j++) {
-      const int id = (tid + 512 * j) % (RC > 0 ? R * 8 : 8);  // duplicates rewrite the same bytes
+      const int id = (tid + NT * j) % (RC > 0 ? R * 8 : 8);  // duplicates rewrite the same bytes
       if (RC > 0) *reinterpret_cast<u32x4*>(&lb[buf][sw_off(id >> 3, id & 7)]) = st.l[j];
     }
   };
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs a)
       for (int j = 0; j < 4; j++)
         a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(tacc[cb][j]);
   } else {
-    const int64_t Mp = (int64_t)gridDim.x * kPrepRows;
+    const int64_t Mp = (int64_t)gridDim.x * 16 * PW;
     if (q == 0) {
       a.npart[(split * Mp + row) * 2 + 0] = nx2;
       a.npart[(split * Mp + row) * 2 + 1] = nt2;
@@ -276,8 +277,12 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   } else {
     p.nx2 = (float*)(base + L.norm);
   }
-  const dim3 grid((unsigned)(Mp / kPrepRows), (unsigned)sp.ks), block(64 * kPrepWaves);
-#define RTL_PREP(C, RC) hipLaunchKernelGGL((prep_kernel<C, RC>), grid, block, 0, stream, p)
+  const dim3 grid((unsigned)(Mp / (16 * sp.waves)), (unsigned)sp.ks), block(64 * sp.waves);
+#define RTL_PREP(C, RC)                                                                  \
+  do {                                                                                   \
+    if (sp.waves == 8) hipLaunchKernelGGL((prep_kernel<C, RC, 8>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((prep_kernel<C, RC, 4>), grid, block, 0, stream, p);          \
+  } while (0)
   switch ((comp ? 8 : 0) + (int)(R / 32)) {
     case 0: RTL_PREP(false, 0); break;
     case 1: RTL_PREP(false, 1); break;
