@@ -53,6 +53,43 @@ struct GemmArgs {
   int tiles_m, tiles_n, n_panels;
 };
 
+// Output tile store through LDS: the accumulator layout (lane = column 16nb + r16, rows
+// 4q + j) goes 16 rows at a time into a per-wave LDS block and comes back as 16-byte row
+// chunks, so Y is written with full 16-byte stores along its rows.  `blk` is the wave's
+// block of 16 * (2 CW + 16) bytes (CW = the wave's columns; the 16-byte pad puts the four
+// row groups of a write in different banks); `val(rb, nb, j)` gives the float to store.
+template <int RB, int NBW, typename Val>
+__device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, int64_t row0, int64_t col0, uint8_t* blk,
+                                           int lane, Val val) {
+  constexpr int CW = NBW * 16, PITCH = 2 * CW + 16, CPR = CW / 8;  // 16-byte chunks per row
+  const int q = lane >> 4, r16 = lane & 15;
+  const bool vec = (N & 7) == 0;
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; nb++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *reinterpret_cast<uint16_t*>(blk + (4 * q + j) * PITCH + (nb * 16 + r16) * 2) =
+            (uint16_t)f32_to_bf16_bits(val(rb, nb, j));
+#pragma unroll
+    for (int c = 0; c < 16 * CPR / 64; c++) {
+      const int id = lane + 64 * c, rr = id / CPR, cc = id % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(blk + rr * PITCH + cc * 16);
+      const int64_t row = row0 + 16 * rb + rr, col = col0 + 8 * cc;
+      if (row >= M) continue;
+      uint16_t* y = Y + row * N + col;
+      if (vec && col + 8 <= N) {
+        *reinterpret_cast<u32x4*>(y) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          if (col + e < N) y[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
 // GEMM workgroup: 8 waves (two per SIMD) on a 256 x 256 output tile; wave w owns rows
 // 64(w % 4)..+63 and columns 128(w / 4)..+127.  Operand tiles go memory -> registers ->
 // LDS two K steps ahead of their use (double-buffered LDS), so a K step's loads have two
@@ -649,39 +686,17 @@ void gemm_kernel(const GemmArgs a) {
       }
     }
     // Store Y = s * acc (bf16, round to nearest even).
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int64_t row = m0 + 64 * wm + 16 * rb + 4 * q + j;
-        if (row >= M) continue;
-        uint16_t* yrow = a.Y + row * N;
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) {
-          const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
-          if (col < N) yrow[col] = (uint16_t)f32_to_bf16_bits(acc[rb][nb][j] * s_acc[rb][j]);
-        }
-      }
-    }
+    __syncthreads();  // the LDS rings are free
+    store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
+                      [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
     return;
   }
 
   // Dense: store Y (bf16, round to nearest even).  Lane holds column 16nb + r16 of its
   // half, rows 16rb + 4q + j of its slab.
-#pragma unroll
-  for (int rb = 0; rb < 4; rb++) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t row = m0 + 64 * wm + 16 * rb + 4 * q + j;
-      if (row >= M) continue;
-      uint16_t* yrow = a.Y + row * N;
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
-        if (col < N) yrow[col] = (uint16_t)f32_to_bf16_bits(acc[rb][nb][j]);
-      }
-    }
-  }
+  __syncthreads();  // the LDS rings are free
+  store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
+                    [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
 }
 
 // Pre-compressed GEMM with two workgroups per CU: 4 waves (one per SIMD) on a 256 x TW
@@ -854,21 +869,14 @@ void half_kernel(const GemmArgs a) {
                                                               __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
     }
   }
+  float s_acc[4][4];
 #pragma unroll
-  for (int rb = 0; rb < 4; rb++) {
+  for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const float sj = __shfl(s_row[rb], 4 * q + j, 64);
-      const int64_t row = m0 + 64 * wave + 16 * rb + 4 * q + j;
-      if (row >= M) continue;
-      uint16_t* yrow = a.Y + row * N;
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        const int64_t col = n0 + nb * 16 + r16;
-        if (col < N) yrow[col] = (uint16_t)f32_to_bf16_bits(acc[rb][nb][j] * sj);
-      }
-    }
-  }
+    for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
+  __syncthreads();  // the LDS ring is free
+  store_tile<4, NB>(a.Y, M, N, m0 + 64 * wave, n0, wl + wave * 16 * (2 * TW + 16), lane,
+                    [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
 }
 
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
