@@ -906,14 +906,16 @@ static int choose_tn(int64_t M, int64_t N) {
 }
 
 // Pre-compressed GEMM: two 256 x 128 workgroups per CU instead of one 256 x TN one, when
-// that gives the busiest CU less work (128 columns per workgroup, a little dearer per
-// column than the 256-wide kernel).
-static bool use_half_tiles(int64_t M, int64_t N) {
+// that gives the busiest CU less work.  Per output column the half-width kernel is a
+// little cheaper for short K (its two workgroups per CU hide each other's tile prologue
+// and epilogue) and dearer for long K (it moves more operand bytes per K step than the
+// 256-wide kernel, which shares the compressed rows through LDS).
+static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
   const int64_t tm = (M + kBM - 1) / kBM;
   const int tn = choose_tn(M, N);
   const int64_t full = tm * ((N + tn - 1) / tn), half = tm * ((N + 127) / 128);
   const double full_cost = (double)((full + 255) / 256) * tn * (tn == 192 ? 1.05 : 1.0);
-  const double half_cost = (double)((half + 255) / 256) * 128 * 1.08;
+  const double half_cost = (double)((half + 255) / 256) * 128 * (K <= 4096 ? 0.95 : 1.08);
   return half_cost < full_cost;
 }
 
@@ -947,7 +949,7 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     g.dbg_idx = dbg_idx;
     g.dbg_s = dbg_s;
   }
-  if (comp && use_half_tiles(M, N)) {
+  if (comp && use_half_tiles(M, N, K)) {
     GemmArgs h = g;
     h.tiles_n = (int)((N + 127) / 128);
     hipLaunchKernelGGL((half_kernel<128>), dim3((unsigned)(h.tiles_m * h.tiles_n)), dim3(kHalfThreads), 0, stream, h);
