@@ -532,11 +532,15 @@ void gemm_kernel(const GemmArgs a) {
     store_at(a0, 0);
     store_w(w0, 0);
     __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
+    // Whole periods of the ring in a loop with no exit in its body (an exit there gives
+    // the compiler a path from mid-period back to the loop head, and it then waits for
+    // every load in flight at the head); the odd step after it.
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
       step_d(kt, w1, w0, a1, a0);
-      if (kt + 1 >= KT) break;
       step_d(kt + 1, w0, w1, a0, a1);
     }
+    if (kt < KT) step_d(kt, w1, w0, a1, a0);
   } else if constexpr (CALDS) {
     AFrag f0, f1;
     AStg s0, s1;
@@ -560,19 +564,29 @@ void gemm_kernel(const GemmArgs a) {
     bp0 = read_bc(0, 0);
     bp1 = read_bc(0, 1);
     read_afrag(0, f0);
-    // LDS buffers cycle with period 3, register sets with period 2.
-    for (int kt = 0; kt < KT; kt += 6) {
+    // LDS buffers cycle with period 3, register sets with period 2: whole periods of 6
+    // steps in the loop (no exit in its body, as for the dense steps), then the rest.
+    int kt = 0;
+    for (; kt + 6 <= KT; kt += 6) {
       step_ca(kt, 0, w0, w1, s0, s1, f0, f1);
-      if (kt + 1 >= KT) break;
       step_ca(kt + 1, 1, w1, w0, s1, s0, f1, f0);
-      if (kt + 2 >= KT) break;
       step_ca(kt + 2, 2, w0, w1, s0, s1, f0, f1);
-      if (kt + 3 >= KT) break;
       step_ca(kt + 3, 0, w1, w0, s1, s0, f1, f0);
-      if (kt + 4 >= KT) break;
       step_ca(kt + 4, 1, w0, w1, s0, s1, f0, f1);
-      if (kt + 5 >= KT) break;
       step_ca(kt + 5, 2, w1, w0, s1, s0, f1, f0);
+    }
+    if (kt < KT) {
+      step_ca(kt, 0, w0, w1, s0, s1, f0, f1);
+      if (kt + 1 < KT) {
+        step_ca(kt + 1, 1, w1, w0, s1, s0, f1, f0);
+        if (kt + 2 < KT) {
+          step_ca(kt + 2, 2, w0, w1, s0, s1, f0, f1);
+          if (kt + 3 < KT) {
+            step_ca(kt + 3, 0, w1, w0, s1, s0, f1, f0);
+            if (kt + 4 < KT) step_ca(kt + 4, 1, w0, w1, s0, s1, f0, f1);
+          }
+        }
+      }
     }
   } else if constexpr (MODE == kModeComp) {
     AFrag f0, f1;
@@ -591,19 +605,29 @@ void gemm_kernel(const GemmArgs a) {
     __syncthreads();
     bp0 = read_bc(0, 0);
     bp1 = read_bc(0, 1);
-    // LDS buffers cycle with period 3, W register sets and A fragment sets with period 2.
-    for (int kt = 0; kt < KT; kt += 6) {
+    // LDS buffers cycle with period 3, W register sets and A fragment sets with period 2:
+    // whole periods of 6 steps in the loop, then the rest.
+    int kt = 0;
+    for (; kt + 6 <= KT; kt += 6) {
       step_c(kt, 0, w0, w1, f0, f1);
-      if (kt + 1 >= KT) break;
       step_c(kt + 1, 1, w1, w0, f1, f0);
-      if (kt + 2 >= KT) break;
       step_c(kt + 2, 2, w0, w1, f0, f1);
-      if (kt + 3 >= KT) break;
       step_c(kt + 3, 0, w1, w0, f1, f0);
-      if (kt + 4 >= KT) break;
       step_c(kt + 4, 1, w0, w1, f0, f1);
-      if (kt + 5 >= KT) break;
       step_c(kt + 5, 2, w1, w0, f1, f0);
+    }
+    if (kt < KT) {
+      step_c(kt, 0, w0, w1, f0, f1);
+      if (kt + 1 < KT) {
+        step_c(kt + 1, 1, w1, w0, f1, f0);
+        if (kt + 2 < KT) {
+          step_c(kt + 2, 2, w0, w1, f0, f1);
+          if (kt + 3 < KT) {
+            step_c(kt + 3, 0, w1, w0, f1, f0);
+            if (kt + 4 < KT) step_c(kt + 4, 1, w0, w1, f0, f1);
+          }
+        }
+      }
     }
   } else {
   AStage a0, a1;
@@ -825,18 +849,28 @@ void half_kernel(const GemmArgs a) {
   __syncthreads();
   bp0 = read_b(0, 0);
   bp1 = read_b(0, 1);
-  for (int kt = 0; kt < KT; kt += 6) {
+  // Whole periods of 6 steps in the loop (no exit in its body), then the rest.
+  int kt = 0;
+  for (; kt + 6 <= KT; kt += 6) {
     step(kt, 0, w0, w1, f0, f1);
-    if (kt + 1 >= KT) break;
     step(kt + 1, 1, w1, w0, f1, f0);
-    if (kt + 2 >= KT) break;
     step(kt + 2, 2, w0, w1, f0, f1);
-    if (kt + 3 >= KT) break;
     step(kt + 3, 0, w1, w0, f1, f0);
-    if (kt + 4 >= KT) break;
     step(kt + 4, 1, w0, w1, f0, f1);
-    if (kt + 5 >= KT) break;
     step(kt + 5, 2, w1, w0, f1, f0);
+  }
+  if (kt < KT) {
+    step(kt, 0, w0, w1, f0, f1);
+    if (kt + 1 < KT) {
+      step(kt + 1, 1, w1, w0, f1, f0);
+      if (kt + 2 < KT) {
+        step(kt + 2, 2, w0, w1, f0, f1);
+        if (kt + 3 < KT) {
+          step(kt + 3, 0, w1, w0, f1, f0);
+          if (kt + 4 < KT) step(kt + 4, 1, w0, w1, f0, f1);
+        }
+      }
+    }
   }
 
   // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the

@@ -116,6 +116,7 @@ FUSED_SMALL = [
     (37, 300, 128, 128, "bf16"),
     (1, 16, 64, 64, "bf16"),
     (260, 272, 64, 0, "bf16"),
+    (300, 520, 320, 64, "bf16"),    # 5 K steps: less than one turn of the GEMM's 6-step ring
     (300, 200, 1024, 64, "bf16"),   # pre-pass split over K (4 splits) with a reduction
     (1, 48, 512, 32, "bf16"),       # one row, 2 K splits
     (64, 256, 256, 8, "f32"),
@@ -190,11 +191,13 @@ def test_fused_workload_layers(name, variant):
 
 
 # Output shapes that make the library pick each GEMM tiling (ragged M and N tails in all):
-#   4000 x 4000: 16 x 16 tiles of 256 x 256, one per CU (256-wide kernels);
-#   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels; K = 320 is an
-#                odd number of 64-wide steps);
-# the small cases above get two 256 x 128 workgroups per CU (pre-compressed variant).
-WIDE = [(4000, 4000, 512), (2000, 6100, 256), (2000, 6100, 320)]
+#   4000 x 4000, K = 4160: 16 x 16 tiles of 256 x 256, one per CU (256-wide kernels; 65 K
+#                steps = ten whole turns of the 6-step ring and a 5-step tail);
+#   4000 x 4000, K = 512: two 256 x 128 workgroups per CU (pre-compressed variant);
+#   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels; K = 256 and 320
+#                are 4 and 5 K steps, shorter than one turn of the ring; K = 704 is one turn
+#                and a 5-step tail).
+WIDE = [(4000, 4000, 4160), (4000, 4000, 512), (2000, 6100, 256), (2000, 6100, 320), (2000, 6100, 704)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
