@@ -338,19 +338,28 @@ void gemm_kernel(const GemmArgs a) {
       make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 4096);
   const __amdgpu_buffer_rsrc_t cires =
       make_rsrc(MODE == kModeComp ? a.cidx + cidx_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 512);
+  // Part p < 4: kept values of row block p; part 4: the position words.
+  auto load_frag_part = [&](int kt, AFrag& f, int part) {
+    if (part < 4) {
+      f.v[part][0] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + part * 1024), kt * 4096, 0);
+    } else {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
+      f.iw[0] = w[0];
+      f.iw[1] = w[1];
+    }
+  };
   auto load_frag = [&](int kt, AFrag& f) {
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
-      f.v[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + rb * 1024), kt * 4096, 0);
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
-    f.iw[0] = w[0];
-    f.iw[1] = w[1];
+    for (int part = 0; part < 5; part++) load_frag_part(kt, f, part);
+  };
+  auto load_w_part = [&](int kt, WStage& st, int i) {
+    st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
   };
   // Pre-compressed step kt on a 3-buffer LDS ring for W (buffer kt % 3), with the memory
-  // operations spread over the MFMA loop instead of bursting at the step boundaries:
-  // column block 0 issues the A loads for step kt + 1, block 1 the W loads for step
-  // kt + 3, and the last blocks write W stage kt + 2 (loaded a step ago) to buffer
-  // (kt + 2) % 3.  The first two B fragments of the step arrive in bp0, bp1, read at the
+  // operations spread over the MFMA loop, at most two loads per column block (a burst of
+  // loads holds up the wave's next MFMAs): blocks 0-2 issue the A loads for step kt + 1,
+  // and each of the last WLD blocks writes one chunk of W stage kt + 2 (loaded a step
+  // ago) to buffer (kt + 2) % 3 and loads one chunk of stage kt + 3.  The first two B fragments of the step arrive in bp0, bp1, read at the
   // end of the previous step: with three buffers, that buffer is complete before the
   // barrier, so no LDS latency is exposed at the step boundary.
   u32x8 bp0, bp1;
@@ -386,10 +395,14 @@ void gemm_kernel(const GemmArgs a) {
   const uint32_t ai = (uint32_t)((tid >> 7) * KT * 512 + (tid & 127) * 4);
   const uint32_t lv0 = (uint32_t)((tid >> 8) * 4096 + (tid & 255) * 16), lv1 = lv0 + 2 * 4096;
   const uint32_t li = (uint32_t)(16384 + (tid >> 7) * 512 + (tid & 127) * 4);
+  auto load_ast_part = [&](int kt, AStg& st, int part) {
+    if (part == 0) st.v[0] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av0, kt * 4096, 0);
+    if (part == 1) st.v[1] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av1, kt * 4096, 0);
+    if (part == 2) st.i = __builtin_amdgcn_raw_buffer_load_b32(tires, ai, kt * 512, 0);
+  };
   auto load_ast = [&](int kt, AStg& st) {
-    st.v[0] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av0, kt * 4096, 0);
-    st.v[1] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av1, kt * 4096, 0);
-    st.i = __builtin_amdgcn_raw_buffer_load_b32(tires, ai, kt * 512, 0);
+#pragma unroll
+    for (int part = 0; part < 3; part++) load_ast_part(kt, st, part);
   };
   auto store_ast = [&](const AStg& st, int buf) {
     uint8_t* b = alc + buf * kCompStage;
@@ -405,10 +418,11 @@ void gemm_kernel(const GemmArgs a) {
     f.iw[0] = w.x;
     f.iw[1] = w.y;
   };
-  // As step_c below, with the compressed operand staged through LDS like W: stage kt + 3
-  // (A and W) is loaded in early column blocks, stage kt + 2 written to buffer
-  // (kt + 2) % 3 in the last ones, and the next step's A fragments and first B fragments
-  // are read from buffer (kt + 1) % 3 before the barrier.
+  // As step_c below, with the compressed operand staged through LDS like W: blocks 0-2
+  // load one part each of A stage kt + 3, block NB - WLD - 1 writes A stage kt + 2 to
+  // buffer (kt + 2) % 3, each of the last WLD blocks writes one chunk of W stage kt + 2
+  // and loads one of stage kt + 3, and the next step's A fragments and first B
+  // fragments are read from buffer (kt + 1) % 3 before the barrier.
   auto step_ca = [&](int kt, int buf, WStage& wst, WStage& wfree, AStg& ast, AStg& afree, const AFrag& cur,
                      AFrag& nxt) {
     const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
@@ -418,13 +432,12 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
-      // loads a few column blocks into the step, away from the burst after the barrier
-      if (nb == 2) load_ast(kp(kt + 3), afree);
-      if (nb == 4) load_w(kp(kt + 3), wfree);
+      if (nb < 3) load_ast_part(kp(kt + 3), afree, nb);
       if (nb == NB - WLD - 1) store_ast(ast, sbuf);
       if (nb >= NB - WLD) {
         const int i = nb - (NB - WLD);
         *reinterpret_cast<u32x4*>(wl + sbuf * TN * 128 + sw_off(srow + 64 * i, schunk)) = wst[i];
+        load_w_part(kp(kt + 3), wfree, i);
       }
       const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
@@ -451,11 +464,14 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
-      if (nb == 0) load_frag(kp(kt + 1), anext);
-      if (nb == 1) load_w(kp(kt + 3), wfree);
+      if (nb < 3) {
+        load_frag_part(kp(kt + 1), anext, 2 * nb);
+        if (nb < 2) load_frag_part(kp(kt + 1), anext, 2 * nb + 1);
+      }
       if (nb >= NB - WLD) {
         const int i = nb - (NB - WLD);
         *reinterpret_cast<u32x4*>(wl + sbuf * TN * 128 + sw_off(srow + 64 * i, schunk)) = wst[i];
+        load_w_part(kp(kt + 3), wfree, i);
       }
       const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
@@ -773,13 +789,22 @@ void half_kernel(const GemmArgs a) {
   const int64_t pan = min((int64_t)tm * 4 + wave, (int64_t)a.n_panels - 1);
   const __amdgpu_buffer_rsrc_t cvres = make_rsrc(a.cvals + cvals_off(pan, KT, 0), (int64_t)KT * 4096);
   const __amdgpu_buffer_rsrc_t cires = make_rsrc(a.cidx + cidx_off(pan, KT, 0), (int64_t)KT * 512);
+  // Part p < 4: kept values of row block p; part 4: the position words.
+  auto load_frag_part = [&](int kt, AF& f, int part) {
+    if (part < 4) {
+      f.v[part] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + part * 1024), kt * 4096, 0);
+    } else {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
+      f.iw[0] = w[0];
+      f.iw[1] = w[1];
+    }
+  };
   auto load_frag = [&](int kt, AF& f) {
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
-      f.v[rb] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + rb * 1024), kt * 4096, 0);
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
-    f.iw[0] = w[0];
-    f.iw[1] = w[1];
+    for (int part = 0; part < 5; part++) load_frag_part(kt, f, part);
+  };
+  auto load_w_part = [&](int kt, WStage& st, int i) {
+    st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0);
   };
   auto read_b = [&](int buf, int nb) {
     const uint8_t* base = wl + buf * TW * 128;
@@ -801,9 +826,10 @@ void half_kernel(const GemmArgs a) {
     return k >= KT ? k - KT : k;
   };
   u32x8 bp0, bp1;
-  // Step kt on LDS buffer kt % 3: A for step kt + 1 loads in column block 0, W for step
-  // kt + 3 in block 1, W stage kt + 2 goes to buffer (kt + 2) % 3 in the last blocks, and
-  // the next step's first B fragments are read before the barrier.
+  // Step kt on LDS buffer kt % 3: column blocks 0-4 load one part each of A for step
+  // kt + 1, each of the last WLD blocks writes one chunk of W stage kt + 2 to buffer
+  // (kt + 2) % 3 and loads one chunk of stage kt + 3, and the next step's first B
+  // fragments are read before the barrier.
   auto step = [&](int kt, int buf, WStage& wst, WStage& wfree, const AF& cur, AF& anext) {
     const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
     u32x8 bq[3];
@@ -812,11 +838,11 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(buf, nb + 2);
-      if (nb == 0) load_frag(kp(kt + 1), anext);
-      if (nb == 1) load_w(kp(kt + 3), wfree);
+      if (nb < 5) load_frag_part(kp(kt + 1), anext, nb);
       if (nb >= NB - WLD) {
         const int i = nb - (NB - WLD);
         *reinterpret_cast<u32x4*>(wl + sbuf * TW * 128 + sw_off(srow + 32 * i, schunk)) = wst[i];
+        load_w_part(kp(kt + 3), wfree, i);
       }
       const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0]), bv, acc[0][nb],
