@@ -90,11 +90,14 @@ __device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, in
   }
 }
 
-// GEMM workgroup: 8 waves (two per SIMD) on a 256 x 256 output tile; wave w owns rows
-// 64(w % 4)..+63 and columns 128(w / 4)..+127.  Operand tiles go memory -> registers ->
-// LDS two K steps ahead of their use (double-buffered LDS), so a K step's loads have two
-// steps of MFMA work to arrive.  Fused mode: of each row slab, the two waves that share it
-// select two 16-row blocks each and trade the compressed operand through LDS.
+// GEMM workgroup: 8 waves (two per SIMD) on a 256 x TN output tile (TN = 192 or 256); wave w
+// owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  W (and, on 256-wide pre-compressed
+// tiles, the compressed operand) goes memory -> registers -> LDS: a 3-buffer ring in the
+// pre-compressed mode (loaded a step before it is written, written two steps before it is
+// used), a 2-buffer ring in the dense and fused modes.  On 192-wide pre-compressed tiles
+// each wave loads its compressed rows straight into registers a step ahead.  Fused mode:
+// of each row slab, the two waves that share it select two 16-row blocks each and trade
+// the compressed operand through LDS.
 constexpr int kGemmThreads = 512;
 constexpr int kXBlk = 64 * 16 + 64 * 2;   // fused: one row block of the compressed operand
 constexpr int kALds = kBM * 128;          // A tile bytes per LDS buffer (dense layout, the largest)
