@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -31,11 +32,21 @@ KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_s
                   "activation_sparse_gemm_amd/csrc/rtl_device.h"]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed (string literals in
+    these kernel sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernel's code (comments and layout ignored), stored beside the
+    counter summary so that its traffic figure is used only for the code it was taken on."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
