@@ -1,6 +1,6 @@
 """Benchmark of the norm-compensated 2:4 activation-sparse + low-rank linear layer.
 
-    python bench.py [--steps K] [--warmup W] [--layer attn_proj] [--all-layers]
+    python bench.py [--steps K] [--warmup W] [--layer attn_proj] [--all-layers] [--blocks]
 
 One step = one rtl_linear_fused call (the whole hot path: the pre-pass over X that
 forms the rank-R product, the row norms and the compressed 2:4 operand, then the
@@ -146,6 +146,47 @@ def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "preco
     return d, t
 
 
+# Projections of one block of a 1024x1024 text-to-image DiT (hidden 3072, MLP 12288, 4096
+# image + 512 text tokens), with the synthetic activation recipe of each input.
+BLOCK_M = 4608
+BLOCK_LAYERS = {"attn.qkv": (3072, 9216, "qkv"), "attn.o_proj": (3072, 3072, "heavy"),
+                "mlp.up": (3072, 12288, "heavy"), "mlp.down": (12288, 3072, "gelu")}
+
+
+def bench_blocks(steps: int, warmup: int) -> dict:
+    """Per-model block time of the four projections under the layer policy of method step
+    3 (sparse layers through rtl_linear_fused, the others through rtl_linear_dense_ref),
+    against the all-dense block (in-library dense GEMM and torch.matmul)."""
+    import torch
+
+    import activation_sparse_gemm_amd as rtl
+    from activation_sparse_gemm_amd import policy
+    import synth
+    per = {}
+    for i, (kind, (K, N, x_kind)) in enumerate(BLOCK_LAYERS.items()):
+        lay = synth.Layer(kind, BLOCK_M, K, N, 64, "bf16", x_kind, 0.08)
+        d = synth.make_layer(lay, seed_base=9000 + 10 * i)
+        X, W, LA, LB = (to_dev(d[k]) for k in ("X", "W", "LA", "LB"))
+        lin = policy.Linear(W, LA, LB, sparse=True)
+        Y = torch.empty((BLOCK_M, N), dtype=torch.bfloat16, device="cuda")
+        Wt = W.t()
+        per[kind] = {"K": K, "N": N,
+                     "sparse_ms": time_loop(lambda: lin(X, Y=Y), steps, warmup) * 1e3,
+                     "dense_ms": time_loop(lambda: rtl.rtl_linear_dense_ref(X, W, Y=Y), steps, warmup) * 1e3,
+                     "torch_matmul_ms": time_loop(lambda: torch.matmul(X, Wt, out=Y), steps, warmup) * 1e3}
+        del X, W, LA, LB, Y, lin, d
+        torch.cuda.empty_cache()
+    dense = sum(v["dense_ms"] for v in per.values())
+    torch_ms = sum(v["torch_matmul_ms"] for v in per.values())
+    models = {}
+    for model, stream in (("qwen-image", "double"), ("flux", "double"), ("flux", "single"), ("z-image", "single")):
+        sp = [k for k in BLOCK_LAYERS if policy.is_sparse(model, stream, k)]
+        t = sum(per[k]["sparse_ms" if k in sp else "dense_ms"] for k in BLOCK_LAYERS)
+        models[f"{model}/{stream}"] = {"sparse_layers": sp, "block_ms": t, "speedup_vs_dense": dense / t,
+                                       "speedup_vs_torch_matmul": torch_ms / t}
+    return {"M": BLOCK_M, "layers": per, "all_dense_ms": dense, "all_torch_matmul_ms": torch_ms, "models": models}
+
+
 def prep_bytes(M: int, K: int, R: int, variant: str) -> int:
     """Algorithmic HBM bytes of the pre-pass: read X and L_B, write T (bf16) and one float
     per row; the pre-compressed variant also writes the kept values (K/2 bf16 per row) and
@@ -177,6 +218,8 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", *sorted(VARIANTS)],
                     help="entry point timed as the step (auto = rtl_linear_fused's own pick)")
     ap.add_argument("--all-layers", action="store_true", help="also time every bf16 layer (one line each, stderr)")
+    ap.add_argument("--blocks", action="store_true",
+                    help="also time a DiT block's four projections under each model's layer policy")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -255,6 +298,9 @@ def main():
             del dl
             torch.cuda.empty_cache()
         out["layers"] = layers
+    if args.blocks:
+        out["blocks"] = bench_blocks(max(5, args.steps // 5), 3)
+        print(json.dumps(out["blocks"]), file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
