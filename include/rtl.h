@@ -83,9 +83,10 @@ size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int6
  *   them with one extra K = R MFMA slice before the single bf16 store of Y.  Limits:
  *   K % 64 == 0, R % 32 == 0, R <= 128.  M and N are arbitrary.
  * fp32: same arithmetic in fp32 on the vector ALUs (no fp32 sparse MFMA exists).
- * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the GEMM
- *   writes the selection codes and s that its own prologue computed, in the layout of
- *   rtl_sparsify.
+ * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the kernels
+ *   write the selection codes and s they computed themselves (the pre-pass in the
+ *   pre-compressed variant, the GEMM's prologue in the prologue variant, the fp32
+ *   kernel in fp32), in the layout of rtl_sparsify.
  * Y must not overlap any input.  Calls that share a workspace must be serialised.
  */
 rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
