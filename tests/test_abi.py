@@ -198,3 +198,28 @@ def test_binding_rejects_cpu_tensors():
     X = torch.zeros((4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rtl.rtl_sparsify(X, vals=X, idx=X, s=X)
+
+
+def test_error_messages_are_per_thread():
+    """rtl_last_error is thread-local: each thread reads the message of its own failed
+    call, whatever the other threads did in between."""
+    import threading
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, over, want):
+        st, h = call_sparsify(**over)
+        barrier.wait()           # both threads have failed before either reads its message
+        msg = rtl.lib.rtl_last_error().decode()
+        barrier.wait()           # and both have read before either thread's buffers go away
+        seen[name] = (st == inv[want], msg, h.untouched())
+
+    t1 = threading.Thread(target=worker, args=("shape", dict(K=6), "RTL_ERR_SHAPE"))
+    t2 = threading.Thread(target=worker, args=("eps", dict(eps=-1.0), "RTL_ERR_ARG"))
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert seen["shape"][0] and seen["eps"][0]
+    assert seen["shape"][2] and seen["eps"][2]
+    assert seen["shape"][1] != seen["eps"][1]
+    assert "4" in seen["shape"][1] or "K" in seen["shape"][1]
+    assert "eps" in seen["eps"][1].lower()
