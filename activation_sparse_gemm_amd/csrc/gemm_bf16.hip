@@ -269,9 +269,6 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One main-loop step on LDS buffer kt & 1.  Every memory operation in the loop is
-  // issued unconditionally (the last steps reload the final K step), so the wait counts
-  // the compiler derives are exact and loads stay in flight across the barrier.
   // The MFMAs of one K step: B fragments from LDS buffer `buf` (read two column blocks
   // ahead), A fragments in `cur`.  Fused mode selects the next step's rows in between.
   auto mma = [&](int kt, int buf, const AFrag& cur, Raw& xsel) {
@@ -333,9 +330,10 @@ void gemm_kernel(const GemmArgs a) {
     __syncthreads();
   };
 
-  // Pre-compressed mode: the operand is stored in MFMA register order, so each wave loads
-  // its own 64 rows straight into registers (one 16-byte load per lane and row block, one
-  // 8-byte load of position words), two K steps ahead; only W goes through LDS.
+  // Pre-compressed mode on 192-wide tiles: the operand is stored in MFMA register order,
+  // so each wave loads its own 64 rows straight into registers (one 16-byte load per lane
+  // and row block, one 8-byte load of position words), one K step ahead; only W goes
+  // through LDS.
   // The wave's panel through buffer resources (wave-uniform base, scalar step offsets).
   const __amdgpu_buffer_rsrc_t cvres =
       make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 4096);
@@ -362,9 +360,10 @@ void gemm_kernel(const GemmArgs a) {
   // operations spread over the MFMA loop, at most two loads per column block (a burst of
   // loads holds up the wave's next MFMAs): blocks 0-2 issue the A loads for step kt + 1,
   // and each of the last WLD blocks writes one chunk of W stage kt + 2 (loaded a step
-  // ago) to buffer (kt + 2) % 3 and loads one chunk of stage kt + 3.  The first two B fragments of the step arrive in bp0, bp1, read at the
-  // end of the previous step: with three buffers, that buffer is complete before the
-  // barrier, so no LDS latency is exposed at the step boundary.
+  // ago) to buffer (kt + 2) % 3 and loads one chunk of stage kt + 3.  The first two B
+  // fragments of the step arrive in bp0, bp1, read at the end of the previous step: with
+  // three buffers, that buffer is complete before the barrier, so no LDS latency is
+  // exposed at the step boundary.
   u32x8 bp0, bp1;
   // K order: tile (tm, tn) starts at K step (tm + tn) % 8 and wraps around, so the
   // workgroups of an XCD that share a W column block (same tn) or a compressed row panel
