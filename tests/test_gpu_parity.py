@@ -218,6 +218,30 @@ def test_fused_wide_tiles_ragged(shape, variant):
     assert err <= TOL_Y["bf16"]
 
 
+# Irregular shapes drawn from a fixed seed (so the cases are the same on every run): M and N
+# with ragged tails, every supported R, K up to 20 steps of 64 (whole and partial turns of
+# the GEMM's register ring), both variants.  Shapes stay small enough for the full oracle.
+def _irregular_shapes(n=10, seed=20251203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        N = int(rng.integers(8, 900))
+        K = 64 * int(rng.integers(1, 21))
+        R = int(rng.choice([0, 32, 64, 96, 128]))
+        out.append((M, N, K, R))
+    return out
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
+@pytest.mark.parametrize("shape", _irregular_shapes(), ids=lambda c: "x".join(map(str, c)))
+def test_fused_irregular_shapes(shape, variant):
+    M, N, K, R = shape
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=8800 + M + N + K + R)
+    check_fused_full(d, "irregular", variant=variant)
+
+
 # ------------------------------------------------------------------ rtl_linear_dense_ref
 
 @pytest.mark.parametrize("case", [(300, 520, 192, "bf16"), (1, 16, 64, "bf16"), (64, 256, 256, "f32"),
