@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_DENSE = 2.5e15   # MI355X dense bf16 MFMA FLOP/s (published)
+PEAK_BF16_SPARSE = 5.0e15  # the same counted dense-equivalent on the 2:4 sparse MFMA (twice the dense rate)
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s (published)
 KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/bf16_common.h",
                   "activation_sparse_gemm_amd/csrc/rtl_device.h"]
@@ -271,6 +272,7 @@ def main():
         "torch_matmul_ms": t["dense_torch"] * 1e3,
         "speedup_vs_torch_matmul": t["dense_torch"] / t_step,
         "frac_dense_peak": value * 1e12 / PEAK_BF16_DENSE,
+        "frac_sparse_peak": value * 1e12 / PEAK_BF16_SPARSE,
         "variants_ms": {vn: t[vn] * 1e3 for vn in ("auto", *VARIANTS)},
         "prep": {"variant": kernel_variant, "us": t_prep * 1e6, "bound": "hbm", "bytes": pbytes,
                  "achieved_GBps": pbytes / t_prep / 1e9, "frac": pbytes / t_prep / PEAK_HBM},
