@@ -8,8 +8,8 @@ nothing from it.
 The arithmetic lives in ``rtl_oracle.c`` (plain C, fp64, OpenMP over rows); this
 module only builds it with gcc and marshals numpy arrays.  Method source: "RT-Lynx:
 Putting the GEMM Sparsity In a Right Way for Diffusion Models" (summary page, method
-overview, steps 1-2).  All functions are pinned by the CPU tests; none is
-"parity unpinned".
+overview, steps 1-2; the FP8 variant follows the reading stated in ``rtl_oracle.c``).
+All functions are pinned by the CPU tests; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -58,6 +58,14 @@ def _load():
         lib.orc_dense.restype = i32
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = i32
+        lib.orc_e4m3_value.argtypes = [i32]
+        lib.orc_e4m3_value.restype = d
+        lib.orc_e4m3_encode_array.argtypes = [i64, p, p]
+        lib.orc_e4m3_encode_array.restype = i32
+        lib.orc_quantize_rows.argtypes = [i64, i64, p, p, p]
+        lib.orc_quantize_rows.restype = i32
+        lib.orc_linear_fp8.argtypes = [i64, i64, i64, i64, p, p, p, p, p, i32, d, p, i64, p, p, p, p, p]
+        lib.orc_linear_fp8.restype = i32
         _lib = lib
     return _lib
 
@@ -158,3 +166,73 @@ def dense(X, W, rows=None):
     rc = _load().orc_dense(dt, M, N, K, _ptr(X), _ptr(W), _ptr(rows_arr), nrows, _ptr(Y))
     _check(rc)
     return Y
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an E4M3 code (OCP 8-bit format; NaN for 0x7F and 0xFF)."""
+    return _load().orc_e4m3_value(int(code))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each float32 value, ties to the even code; -1 where the
+    value is NaN or rounds past 448."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    codes = np.zeros(x.shape, np.int32)
+    _check(_load().orc_e4m3_encode_array(x.size, _ptr(x), _ptr(codes)))
+    return codes
+
+
+def quantize_rows(V) -> tuple:
+    """Row-wise E4M3 quantisation of float32 V [rows, K]: (codes [rows,K] u8, scale [rows] f32)."""
+    V = np.ascontiguousarray(np.asarray(V, dtype=np.float32))
+    rows, K = V.shape
+    codes = np.zeros((rows, K), np.uint8)
+    scale = np.zeros(rows, np.float32)
+    _check(_load().orc_quantize_rows(rows, K, _ptr(V), _ptr(codes), _ptr(scale)))
+    return codes, scale
+
+
+def bf16_to_f32(a: np.ndarray) -> np.ndarray:
+    """Exact float32 values of bf16 bit patterns."""
+    return (np.ascontiguousarray(a).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_weight(W) -> tuple:
+    """E4M3 codes [N,K] and per-output-row scales [N] of bf16 W [N,K] (uint16 bits)."""
+    return quantize_rows(bf16_to_f32(W))
+
+
+def linear_fp8(X, Wq, sw, LA, LB, rows=None, tie: int = TIE_LOWER, eps: float = EPS, want_all: bool = False):
+    """FP8 layer Y = s * sx * sw * (Xq~ Wq^T) + (X L_B^T) L_A^T in fp64 for the given rows.
+
+    X [M,K], LA [N,R], LB [R,K] bf16 bits (LA/LB may be None); Wq [N,K] u8 codes and sw [N]
+    from quantize_weight.  Returns (Y, s) or, with want_all, (Y, s, T, xq [rows,K/2], sx)."""
+    X = np.ascontiguousarray(X)
+    if _dtype_of(X) != BF16:
+        raise TypeError("the FP8 layer takes bf16 X")
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sw.shape != (N,):
+        raise ValueError("Wq must be [N, K] and sw [N]")
+    if LA is None or LB is None:
+        R = 0
+        LA = LB = None
+    else:
+        LA = np.ascontiguousarray(LA)
+        LB = np.ascontiguousarray(LB)
+        R = LB.shape[0]
+        if LA.shape != (N, R) or LB.shape != (R, K) or _dtype_of(LA) != BF16 or _dtype_of(LB) != BF16:
+            raise ValueError("LA must be [N,R] and LB [R,K], bf16")
+    rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nrows = M if rows_arr is None else rows_arr.shape[0]
+    Y = np.zeros((nrows, N))
+    s = np.zeros(nrows)
+    T = np.zeros((nrows, max(R, 1)))
+    xq = np.zeros((nrows, K // 2), np.uint8)
+    sx = np.zeros(nrows, np.float32)
+    rc = _load().orc_linear_fp8(M, N, K, R, _ptr(X), _ptr(Wq), _ptr(sw), _ptr(LA), _ptr(LB), tie, eps,
+                                _ptr(rows_arr), nrows, _ptr(Y), _ptr(s), _ptr(T), _ptr(xq), _ptr(sx))
+    _check(rc)
+    return (Y, s, T[:, :R], xq, sx) if want_all else (Y, s)

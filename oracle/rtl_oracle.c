@@ -271,3 +271,176 @@ int orc_dense(int dt, int64_t M, int64_t N, int64_t K, const void* X, const void
   free(Wd);
   return (bad & 2) ? ORC_ENOMEM : ORC_OK;
 }
+
+/*
+ * FP8 variant of the sparse product.  The summary page ("RT-Lynx: Putting the GEMM
+ * Sparsity In a Right Way for Diffusion Models", limitations and future work) names
+ * FP8 as the next step and fixes no scheme; the reading taken here:
+ *   - format E4M3 of the OCP 8-bit floating-point specification: sign, 4 exponent bits
+ *     (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; no
+ *     infinities; S.1111.111 is NaN; the largest finite magnitude is 448;
+ *   - rounding to nearest, ties to the even code;
+ *   - one scale per row of values (per token row of X~, per output row of W):
+ *     a = max |v|, inv = fl32(448 / a) (0 when a = 0), code = e4m3(fl32(v * inv)),
+ *     dequantisation scale sc = fl32(a / 448); fl32() is IEEE single rounding, the
+ *     precision in which the value that decides the 8-bit code is formed;
+ *   - the selection, s and the low-rank branch are those of the bf16 layer (computed on
+ *     the bf16 X); only X~ and W enter the product quantised:
+ *       Y[i,n] = s_i * sx_i * sw_n * sum_k dec(Xq[i,k]) dec(Wq[n,k]) + sum_q T[i,q] L_A[n,q].
+ */
+
+/* Value of an E4M3 code (NaN for the two NaN codes). */
+double orc_e4m3_value(int code) {
+  code &= 0xFF;
+  const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* Nearest E4M3 code of x, ties to the even code; -1 when x is NaN or rounds past 448
+ * (|x| > 464: the next step of the format's grid, 480, has no finite code). */
+int orc_e4m3_encode(float x) {
+  if (isnan(x)) return -1;
+  const double ax = fabs((double)x);
+  if (ax > 464.0) return -1;
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 0x7F; c++) {
+    const double d = fabs(ax - orc_e4m3_value(c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (signbit(x) ? 0x80 : 0) | best;
+}
+
+int orc_e4m3_encode_array(int64_t n, const float* x, int* codes) {
+  if (n < 0 || (n > 0 && (!x || !codes))) return ORC_EARG;
+  for (int64_t i = 0; i < n; i++) codes[i] = orc_e4m3_encode(x[i]);
+  return ORC_OK;
+}
+
+/* Row-wise quantisation of v [rows, K] (fp32 values) to codes [rows, K] and scale [rows]. */
+int orc_quantize_rows(int64_t rows, int64_t K, const float* v, uint8_t* codes, float* scale) {
+  if (rows < 0 || K <= 0 || !v || !codes || !scale) return ORC_EARG;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t i = 0; i < rows; i++) {
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; k++) {
+      const float t = fabsf(v[i * K + k]);
+      if (!isfinite(t)) bad = 1;
+      if (t > a) a = t;
+    }
+    const float inv = a > 0.0f ? 448.0f / a : 0.0f;
+    scale[i] = a / 448.0f;
+    for (int64_t k = 0; k < K; k++) {
+      const float p = v[i * K + k] * inv;
+      const int c = orc_e4m3_encode(p);
+      if (c < 0) bad = 1;
+      codes[i * K + k] = (uint8_t)(c < 0 ? 0 : c);
+    }
+  }
+  return bad ? ORC_ENONFINITE : ORC_OK;
+}
+
+/*
+ * The FP8 layer for a list of rows.  X, L_A, L_B bf16; Wq [N,K] codes and sw [N] from
+ * orc_quantize_rows on W.  Outputs Y [nrows,N] double; nullable s_out [nrows],
+ * T_out [nrows,R], xq_out [nrows,K/2] (codes of the kept values in ascending position
+ * order) and sx_out [nrows].
+ */
+int orc_linear_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const uint8_t* Wq,
+                   const float* sw, const void* LA, const void* LB, int tie, double eps,
+                   const int64_t* rows, int64_t nrows, double* Y, double* s_out, double* T_out,
+                   uint8_t* xq_out, float* sx_out) {
+  int rc = orc_check_common(ORC_BF16, M, K, tie);
+  if (rc) return rc;
+  if (tie == ORC_KEEP_ALL) return ORC_EARG;
+  if (N <= 0 || R < 0 || !X || !Wq || !sw || !Y) return ORC_EARG;
+  if (R > 0 && (!LA || !LB)) return ORC_EARG;
+  if (!rows) nrows = M;
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) return ORC_EARG;
+  }
+  double* Wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+  double* LAd = R > 0 ? (double*)malloc(sizeof(double) * (size_t)(N * R)) : NULL;
+  double* LBd = R > 0 ? (double*)malloc(sizeof(double) * (size_t)(R * K)) : NULL;
+  if (!Wd || (R > 0 && (!LAd || !LBd))) {
+    free(Wd); free(LAd); free(LBd);
+    return ORC_ENOMEM;
+  }
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t e = 0; e < N * K; e++) {
+    Wd[e] = orc_e4m3_value(Wq[e]);
+    if (isnan(Wd[e])) bad |= 1;
+  }
+  for (int64_t e = 0; e < N * R; e++) LAd[e] = orc_load(ORC_BF16, LA, e);
+  for (int64_t e = 0; e < R * K; e++) LBd[e] = orc_load(ORC_BF16, LB, e);
+#pragma omp parallel reduction(| : bad)
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)K);
+    float* kv = (float*)malloc(sizeof(float) * (size_t)(K / 2));
+    uint8_t* kq = (uint8_t*)malloc((size_t)(K / 2));
+    double* xt = (double*)malloc(sizeof(double) * (size_t)K);
+    double* T = (double*)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    if (!x || !kv || !kq || !xt || !T) bad |= 2;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; r++) {
+      if (bad & 2) continue;
+      int64_t i = rows ? rows[r] : r;
+      /* Selection and norms exactly as in the bf16 layer; kept values in position order. */
+      double sxn = 0.0, st = 0.0;
+      for (int64_t g = 0; g < K / 4; g++) {
+        double q[4];
+        for (int j = 0; j < 4; j++) {
+          q[j] = orc_load(ORC_BF16, X, i * K + 4 * g + j);
+          if (!isfinite(q[j])) bad |= 1;
+          x[4 * g + j] = q[j];
+          sxn += q[j] * q[j];
+        }
+        int m = orc_select4(q, tie), nk = 0;
+        for (int j = 0; j < 4; j++)
+          if (m & (1 << j)) {
+            st += q[j] * q[j];
+            kv[2 * g + nk++] = (float)q[j];
+          }
+      }
+      const double s = sqrt(sxn) / (sqrt(st) + eps);
+      if (s_out) s_out[r] = s;
+      /* The kept values of the row quantised with the row's own scale. */
+      float sx;
+      if (orc_quantize_rows(1, K / 2, kv, kq, &sx) != ORC_OK) bad |= 1;
+      if (xq_out) memcpy(xq_out + r * (K / 2), kq, (size_t)(K / 2));
+      if (sx_out) sx_out[r] = sx;
+      /* Dequantised X~ in dense positions (dropped positions 0). */
+      for (int64_t g = 0; g < K / 4; g++) {
+        double q[4];
+        for (int j = 0; j < 4; j++) q[j] = x[4 * g + j];
+        int m = orc_select4(q, tie), nk = 0;
+        for (int j = 0; j < 4; j++) xt[4 * g + j] = (m & (1 << j)) ? orc_e4m3_value(kq[2 * g + nk++]) : 0.0;
+      }
+      for (int64_t qq = 0; qq < R; qq++) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; k++) acc += x[k] * LBd[qq * K + k];
+        T[qq] = acc;
+        if (T_out) T_out[r * R + qq] = acc;
+      }
+      for (int64_t n = 0; n < N; n++) {
+        double ys = 0.0;
+        for (int64_t k = 0; k < K; k++) ys += xt[k] * Wd[n * K + k];
+        double yr = 0.0;
+        for (int64_t qq = 0; qq < R; qq++) yr += T[qq] * LAd[n * R + qq];
+        Y[r * N + n] = s * (double)sx * (double)sw[n] * ys + yr;
+      }
+    }
+    free(x); free(kv); free(kq); free(xt); free(T);
+  }
+  free(Wd); free(LAd); free(LBd);
+  if (bad & 2) return ORC_ENOMEM;
+  return (bad & 1) ? ORC_ENONFINITE : ORC_OK;
+}
