@@ -24,6 +24,7 @@ __all__ = [
     "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref",
     "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
     "rtl_status_string", "rtl_version",
+    "rtl_quantize_weight_fp8", "rtl_linear_fused_fp8", "rtl_linear_fused_fp8_workspace_bytes",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +39,8 @@ STATUS = {0: "RTL_OK", 1: "RTL_ERR_NULL", 2: "RTL_ERR_SHAPE", 3: "RTL_ERR_ALIGN"
 
 # Every entry point include/rtl.h declares.
 EXPORTS = ["rtl_sparsify", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused", "rtl_linear_fused_ex",
-           "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref", "rtl_status_string",
+           "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref", "rtl_quantize_weight_fp8",
+           "rtl_linear_fused_fp8_workspace_bytes", "rtl_linear_fused_fp8", "rtl_status_string",
            "rtl_last_error", "rtl_version"]
 
 
@@ -67,6 +69,12 @@ def _load() -> ctypes.CDLL:
     L.rtl_linear_fused_main.restype = i32
     L.rtl_linear_dense_ref.argtypes = [i32, i64, i64, i64, p, p, p, p]
     L.rtl_linear_dense_ref.restype = i32
+    L.rtl_quantize_weight_fp8.argtypes = [i64, i64, p, p, p, p]
+    L.rtl_quantize_weight_fp8.restype = i32
+    L.rtl_linear_fused_fp8_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.rtl_linear_fused_fp8_workspace_bytes.restype = sz
+    L.rtl_linear_fused_fp8.argtypes = [i64, i64, i64, i64, p, p, p, p, p, i32, f32, p, p, sz, p, p, p]
+    L.rtl_linear_fused_fp8.restype = i32
     L.rtl_status_string.argtypes = [i32]
     L.rtl_status_string.restype = ctypes.c_char_p
     L.rtl_last_error.argtypes = []
@@ -196,4 +204,42 @@ def rtl_linear_dense_ref(X: torch.Tensor, W: torch.Tensor, Y=None, stream=None) 
     if Y is None:
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
     _check(lib.rtl_linear_dense_ref(_dt(X), M, N, K, _ptr(X), _ptr(W), _ptr(Y), _stream(stream)))
+    return Y
+
+
+def rtl_quantize_weight_fp8(W: torch.Tensor, Wq=None, sw=None, stream=None):
+    """E4M3 codes Wq [N,K] uint8 and per-output-row scales sw [N] float32 of bf16 W [N,K]."""
+    N, K = W.shape
+    if W.dtype != torch.bfloat16:
+        raise TypeError("the FP8 layer takes bf16 weights")
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    if sw is None:
+        sw = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib.rtl_quantize_weight_fp8(N, K, _ptr(W), _ptr(Wq), _ptr(sw), _stream(stream)))
+    return Wq, sw
+
+
+def rtl_linear_fused_fp8_workspace_bytes(M: int, N: int, K: int, R: int) -> int:
+    return int(lib.rtl_linear_fused_fp8_workspace_bytes(M, N, K, R))
+
+
+def rtl_linear_fused_fp8(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, LA, LB, tie: int = RTL_TIE_LOWER_INDEX,
+                         eps: float = EPS, Y=None, workspace=None, dbg_xq=None, dbg_sx=None, stream=None) -> torch.Tensor:
+    """FP8 layer Y = s sx sw (Xq~ Wq^T) + (X L_B^T) L_A^T.  X [M,K], LA [N,R], LB [R,K] bf16
+    (LA/LB None: R = 0); Wq, sw from rtl_quantize_weight_fp8.  ``dbg_xq`` [M,K/2] uint8 and
+    ``dbg_sx`` [M] float32 receive the activation codes and scales the kernels computed."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    R = 0 if LB is None else LB.shape[0]
+    if X.dtype != torch.bfloat16:
+        raise TypeError("the FP8 layer takes bf16 activations")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    need = rtl_linear_fused_fp8_workspace_bytes(M, N, K, R)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.rtl_linear_fused_fp8(M, N, K, R, _ptr(X), _ptr(Wq), _ptr(sw), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
+                                    _ptr(workspace), ws_bytes, _ptr(dbg_xq), _ptr(dbg_sx), _stream(stream)))
     return Y

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "librtl.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["rtl_api.cpp", "sparsify.hip", "prep_bf16.hip", "gemm_bf16.hip", "fp32_path.hip"]
+SOURCES = ["rtl_api.cpp", "sparsify.hip", "prep_bf16.hip", "gemm_bf16.hip", "gemm_fp8.hip", "fp32_path.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

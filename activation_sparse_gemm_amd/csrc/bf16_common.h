@@ -83,4 +83,31 @@ inline WsLayout ws_layout(int64_t M, int64_t K, int64_t R, bool comp) {
   return L;
 }
 
+// FP8 layer.  The 8-bit sparse operand, per (64-row panel p, 128-wide K step kt): 4096
+// bytes of E4M3 codes, row block rb at +1024*rb, lane l (row 16rb + l%16, dense k
+// 32(l/16)..+31 of the step: 16 kept values, two per group in position order) at +16*l;
+// and 1024 bytes of position words, lane l at +16*l, row block rb at +4*rb (kept value i
+// of the lane at bits 2i..2i+1).
+__device__ __forceinline__ int64_t cvals8_off(int64_t p, int KT8, int kt) { return (p * KT8 + kt) * 4096; }
+__device__ __forceinline__ int64_t cidx8_off(int64_t p, int KT8, int kt) { return (p * KT8 + kt) * 1024; }
+
+// FP8 layer workspace: the bf16 pre-compressed layout, then the row absmax [Mp] f32, its
+// K-split partials [ks, Mp] f32, and the 8-bit operand (codes, then position words).
+struct Fp8WsLayout {
+  WsLayout L;
+  size_t ax, apart, cvals8, cidx8, total;
+};
+inline Fp8WsLayout fp8_ws_layout(int64_t M, int64_t K, int64_t R) {
+  const int64_t Mp = padded_rows(M);
+  const PrepSplit sp = prep_split(M, K);
+  Fp8WsLayout F;
+  F.L = ws_layout(M, K, R, true);
+  F.ax = F.L.total;
+  F.apart = F.ax + align256((size_t)Mp * 4);
+  F.cvals8 = F.apart + align256((size_t)(sp.ks > 1 ? sp.ks : 0) * Mp * 4);
+  F.cidx8 = F.cvals8 + align256((size_t)(Mp / kPanel) * (K / 128) * 4096);
+  F.total = F.cidx8 + align256((size_t)(Mp / kPanel) * (K / 128) * 1024);
+  return F;
+}
+
 }  // namespace rtl

@@ -24,6 +24,8 @@ struct PrepArgs {
   float* npart;       // [ks, Mp, 2] partial squared norms when ks > 1
   int ks;             // K splits
   int kts;            // K steps per split
+  float* ax;          // FP8 layer: [Mp] row absmax of X (written when ks == 1)
+  float* apart;       // FP8 layer: [ks, Mp] partial row absmax when ks > 1
 };
 
 // Pre-pass over X.  Workgroup (row tile, K split): PW waves, wave w the 16-row block w of
@@ -32,8 +34,9 @@ struct PrepArgs {
 // read as two 8-wide K slices, the A operand of the rank-R product; the L_B slice of each
 // step passes through LDS once per workgroup and is shared by its rows.  X and L_B
 // are loaded three steps ahead.  With several K splits the partial T and norms go to the
-// workspace and prep_reduce_kernel sums them in a fixed order.
-template <bool COMPRESS, int RC, int PW>  // RC = R / 32, PW waves = 16-row blocks per workgroup
+// workspace and prep_reduce_kernel sums them in a fixed order.  AMAX (the FP8 layer) also
+// takes each row's largest magnitude, the scale of its 8-bit quantisation.
+template <bool COMPRESS, int RC, int PW, bool AMAX>  // RC = R / 32, PW waves = 16-row blocks per workgroup
 __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   constexpr int R = 32 * RC, CB = 2 * RC;
   constexpr int NT = 64 * PW;
@@ -86,6 +89,7 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
 #pragma unroll
   for (int cb = 0; cb < (CB > 0 ? CB : 1); cb++) tacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float nx2 = 0.f, nt2 = 0.f;
+  uint32_t amax = 0;  // largest sign-cleared bf16 pattern seen (finite values order as integers)
 
   // A step past the end of the split (valid == false) reruns the last step's idempotent
   // stores and adds nothing to the sums, so every wave issues the same memory operations.
@@ -95,6 +99,10 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
 #pragma unroll
     for (int g = 0; g < 8; g++) nx2 = dot2_bf16(w8[g], w8[g], nx2);
+    if (AMAX) {
+#pragma unroll
+      for (int g = 0; g < 8; g++) amax = max(amax, max(w8[g] & 0x7FFFu, (w8[g] >> 16) & 0x7FFFu));
+    }
     if (COMPRESS) {
       u32x4 v;
       uint32_t code16 = 0, bytes = 0;
@@ -157,8 +165,14 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   nt2 += __shfl_xor(nt2, 16, 64);
   nx2 += __shfl_xor(nx2, 32, 64);
   nt2 += __shfl_xor(nt2, 32, 64);
+  if (AMAX) {
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+  }
+  const float axv = __uint_as_float(amax << 16);
   if (a.ks == 1) {
     if (q == 0) {
+      if (AMAX) a.ax[row] = axv;
       if (COMPRESS) {
         const float sv = sqrtf(nx2) / (sqrtf(nt2) + a.eps);
         a.s[row] = sv;
@@ -178,6 +192,7 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     if (q == 0) {
       a.npart[(split * Mp + row) * 2 + 0] = nx2;
       a.npart[(split * Mp + row) * 2 + 1] = nt2;
+      if (AMAX) a.apart[split * Mp + row] = axv;
     }
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
@@ -236,6 +251,52 @@ __global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepArgs a, int6
     } else {
       a.nx2[row] = x2;
     }
+    if (a.ax != nullptr) {  // FP8 layer: largest magnitude over the splits
+      float m = 0.f;
+      for (int sp = 0; sp < a.ks; sp++) m = fmaxf(m, a.apart[sp * Mp + row]);
+      a.ax[row] = m;
+    }
+  }
+}
+
+// The pre-pass launches (prep_kernel, then the split reduction when K is split).
+template <bool AMAX>
+static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const PrepSplit& sp, int64_t R,
+                                hipStream_t stream) {
+  const dim3 grid((unsigned)(Mp / (16 * sp.waves)), (unsigned)sp.ks), block(64 * sp.waves);
+#define RTL_PREP(C, RC)                                                                          \
+  do {                                                                                           \
+    if (sp.waves == 8) hipLaunchKernelGGL((prep_kernel<C, RC, 8, AMAX>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((prep_kernel<C, RC, 4, AMAX>), grid, block, 0, stream, p);          \
+  } while (0)
+  if constexpr (AMAX) {
+    switch ((int)(R / 32)) {
+      case 0: RTL_PREP(true, 0); break;
+      case 1: RTL_PREP(true, 1); break;
+      case 2: RTL_PREP(true, 2); break;
+      case 3: RTL_PREP(true, 3); break;
+      default: RTL_PREP(true, 4); break;
+    }
+  } else {
+    switch ((comp ? 8 : 0) + (int)(R / 32)) {
+      case 0: RTL_PREP(false, 0); break;
+      case 1: RTL_PREP(false, 1); break;
+      case 2: RTL_PREP(false, 2); break;
+      case 3: RTL_PREP(false, 3); break;
+      case 4: RTL_PREP(false, 4); break;
+      case 8: RTL_PREP(true, 0); break;
+      case 9: RTL_PREP(true, 1); break;
+      case 10: RTL_PREP(true, 2); break;
+      case 11: RTL_PREP(true, 3); break;
+      default: RTL_PREP(true, 4); break;
+    }
+  }
+#undef RTL_PREP
+  if (sp.ks > 1) {
+    const int64_t items = Mp * (R / 4 + 1);
+    const dim3 rgrid((unsigned)((items + 255) / 256)), rblock(256);
+    if (comp) hipLaunchKernelGGL((prep_reduce_kernel<true>), rgrid, rblock, 0, stream, p, Mp);
+    else hipLaunchKernelGGL((prep_reduce_kernel<false>), rgrid, rblock, 0, stream, p, Mp);
   }
 }
 
@@ -277,31 +338,30 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   } else {
     p.nx2 = (float*)(base + L.norm);
   }
-  const dim3 grid((unsigned)(Mp / (16 * sp.waves)), (unsigned)sp.ks), block(64 * sp.waves);
-#define RTL_PREP(C, RC)                                                                  \
-  do {                                                                                   \
-    if (sp.waves == 8) hipLaunchKernelGGL((prep_kernel<C, RC, 8>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((prep_kernel<C, RC, 4>), grid, block, 0, stream, p);          \
-  } while (0)
-  switch ((comp ? 8 : 0) + (int)(R / 32)) {
-    case 0: RTL_PREP(false, 0); break;
-    case 1: RTL_PREP(false, 1); break;
-    case 2: RTL_PREP(false, 2); break;
-    case 3: RTL_PREP(false, 3); break;
-    case 4: RTL_PREP(false, 4); break;
-    case 8: RTL_PREP(true, 0); break;
-    case 9: RTL_PREP(true, 1); break;
-    case 10: RTL_PREP(true, 2); break;
-    case 11: RTL_PREP(true, 3); break;
-    default: RTL_PREP(true, 4); break;
-  }
-#undef RTL_PREP
-  if (sp.ks > 1) {
-    const int64_t items = Mp * (R / 4 + 1);
-    const dim3 rgrid((unsigned)((items + 255) / 256)), rblock(256);
-    if (comp) hipLaunchKernelGGL((prep_reduce_kernel<true>), rgrid, rblock, 0, stream, p, Mp);
-    else hipLaunchKernelGGL((prep_reduce_kernel<false>), rgrid, rblock, 0, stream, p, Mp);
-  }
+  launch_prep_kernels<false>(p, comp, Mp, sp, R, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_fp8(int64_t M, int64_t K, int64_t R, const void* X, const void* LB, float eps, void* ws,
+                           float* dbg_s, hipStream_t stream) {
+  const Fp8WsLayout F = fp8_ws_layout(M, K, R);
+  uint8_t* base = (uint8_t*)ws;
+  PrepArgs p{};
+  p.M = M; p.K = K; p.R = R; p.X = (const uint16_t*)X; p.LB = (const uint16_t*)LB; p.eps = eps;
+  p.T = (uint16_t*)(base + F.L.t);
+  const int64_t Mp = padded_rows(M);
+  const PrepSplit sp = prep_split(M, K);
+  p.ks = sp.ks;
+  p.kts = sp.kts;
+  p.tpart = (float*)(base + F.L.tpart);
+  p.npart = (float*)(base + F.L.npart);
+  p.s = (float*)(base + F.L.norm);
+  p.cvals = base + F.L.cvals;
+  p.cidx = base + F.L.cidx;
+  p.dbg_s = dbg_s;
+  p.ax = (float*)(base + F.ax);
+  p.apart = (float*)(base + F.apart);
+  launch_prep_kernels<true>(p, true, Mp, sp, R, stream);
   return hipGetLastError();
 }
 

@@ -232,3 +232,61 @@ rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, c
 }
 
 }  // extern "C"
+
+extern "C" {
+
+rtl_status rtl_quantize_weight_fp8(int64_t N, int64_t K, const void* W, uint8_t* Wq, float* sw, void* stream) {
+  if (N <= 0 || K <= 0 || K % 8 != 0)
+    return fail(RTL_ERR_SHAPE, "need N > 0, K > 0, K %% 8 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  if (!W || !Wq || !sw) return fail(RTL_ERR_NULL, "W, Wq and sw are required");
+  if (misaligned(W) || misaligned(Wq) || misaligned(sw)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t wb = (size_t)N * K * 2, qb = (size_t)N * K, sb = (size_t)N * 4;
+  if (overlap(Wq, qb, W, wb) || overlap(sw, sb, W, wb) || overlap(Wq, qb, sw, sb))
+    return fail(RTL_ERR_ARG, "outputs overlap each other or the input");
+  return hip_status(rtl::launch_quant_w_fp8(N, K, W, Wq, sw, (hipStream_t)stream), "rtl_quantize_weight_fp8 launch");
+}
+
+size_t rtl_linear_fused_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || R < 0) return 0;
+  return rtl::fused_fp8_workspace(M, N, K, R);
+}
+
+rtl_status rtl_linear_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const uint8_t* Wq,
+                                const float* sw, const void* LA, const void* LB, rtl_tie_rule tie, float eps, void* Y,
+                                void* workspace, size_t ws_bytes, uint8_t* dbg_xq, float* dbg_sx, void* stream) {
+  rtl_status st;
+  if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
+  if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
+    return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
+                (long long)N, (long long)K, (long long)R);
+  if (!X || !Wq || !sw || !Y || (R > 0 && (!LA || !LB)))
+    return fail(RTL_ERR_NULL, "X, Wq, sw, Y (and LA, LB when R > 0) are required");
+  if (misaligned(X) || misaligned(Wq) || misaligned(sw) || misaligned(Y) || misaligned(LA) || misaligned(LB) ||
+      misaligned(workspace) || misaligned(dbg_xq) || misaligned(dbg_sx))
+    return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (K % 128 != 0) return fail(RTL_ERR_UNSUPPORTED, "fp8 path needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (R % 32 != 0 || R > 128)
+    return fail(RTL_ERR_UNSUPPORTED, "fp8 path needs R %% 32 == 0 and R <= 128 (R=%lld)", (long long)R);
+  if ((st = check_eps(eps)) != RTL_OK) return st;
+  const size_t xb = (size_t)M * K * 2, qb = (size_t)N * K, swb = (size_t)N * 4, lab = (size_t)N * R * 2,
+               lbb = (size_t)R * K * 2, yb = (size_t)M * N * 2, xqb = (size_t)M * (K / 2), sxb = (size_t)M * 4;
+  const size_t need = rtl_linear_fused_fp8_workspace_bytes(M, N, K, R);
+  const void* ins[5] = {X, Wq, sw, R > 0 ? LA : nullptr, R > 0 ? LB : nullptr};
+  const size_t inb[5] = {xb, qb, swb, lab, lbb};
+  const void* outs[4] = {Y, dbg_xq, dbg_sx, workspace};
+  const size_t outb[4] = {yb, xqb, sxb, need};
+  for (int o = 0; o < 4; o++) {
+    for (int i = 0; i < 5; i++)
+      if (overlap(outs[o], outb[o], ins[i], inb[i])) return fail(RTL_ERR_ARG, "an output or the workspace overlaps an input");
+    for (int o2 = o + 1; o2 < 4; o2++)
+      if (overlap(outs[o], outb[o], outs[o2], outb[o2]))
+        return fail(RTL_ERR_ARG, "outputs overlap each other or the workspace");
+  }
+  if (!workspace || ws_bytes < need)
+    return fail(RTL_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0);
+  return hip_status(rtl::launch_fused_fp8(M, N, K, R, X, Wq, sw, LA, LB, eps, Y, workspace, dbg_xq, dbg_sx,
+                                          (hipStream_t)stream),
+                    "rtl_linear_fused_fp8 launch");
+}
+
+}  // extern "C"

@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_DENSE = 2.5e15   # MI355X dense bf16 MFMA FLOP/s (published)
 PEAK_BF16_SPARSE = 5.0e15  # the same counted dense-equivalent on the 2:4 sparse MFMA (twice the dense rate)
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s (published)
+PEAK_FP8_DENSE = 5.0e15    # MI355X dense fp8 MFMA FLOP/s (published)
 KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/bf16_common.h",
                   "activation_sparse_gemm_amd/csrc/rtl_device.h"]
 
@@ -138,6 +139,11 @@ def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "preco
     ws = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R),), dtype=torch.uint8,
                      device="cuda")
     t["auto"] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws), steps, warmup)
+    if K % 128 == 0:
+        # FP8 variant: the weight is quantised once (a static weight), outside the timed calls
+        Wq, sw = rtl.rtl_quantize_weight_fp8(W)
+        ws8 = torch.empty((rtl.rtl_linear_fused_fp8_workspace_bytes(M, N, K, R),), dtype=torch.uint8, device="cuda")
+        t["fp8"] = time_loop(lambda: rtl.rtl_linear_fused_fp8(X, Wq, sw, LA, LB, Y=Y, workspace=ws8), steps, warmup)
     for vn in variants:
         v = VARIANTS[vn]
         t[vn] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws, variant=v), steps, warmup)
@@ -278,6 +284,11 @@ def main():
                  "achieved_GBps": pbytes / t_prep / 1e9, "frac": pbytes / t_prep / PEAK_HBM},
         "roofline": roofline,
     }
+    if "fp8" in t:
+        # FP8 (E4M3) variant of the same layer: context beside the bf16 line, not its value
+        out["fp8_variant"] = {"ms": t["fp8"] * 1e3, "tflops": flops / t["fp8"] / 1e12,
+                              "speedup_vs_dense_bf16": t["dense"] / t["fp8"], "speedup_vs_bf16_sparse": t_step / t["fp8"],
+                              "frac_fp8_dense_peak": flops / t["fp8"] / PEAK_FP8_DENSE}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     if args.all_layers:
@@ -289,6 +300,9 @@ def main():
             line = {"layer": name, "M": lay.M, "K": lay.K, "N": lay.N, "R": lay.R,
                     "dense_ms": tl["dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["dense"] / 1e12,
                     "torch_matmul_ms": tl["dense_torch"] * 1e3}
+            if "fp8" in tl:
+                line["fp8"] = {"ms": tl["fp8"] * 1e3, "tflops": lay.flops / tl["fp8"] / 1e12,
+                               "speedup": tl["dense"] / tl["fp8"], "speedup_vs_bf16_sparse": tl["auto"] / tl["fp8"]}
             for vn in ("auto", *VARIANTS):
                 if vn in tl:
                     line[vn] = {"ms": tl[vn] * 1e3, "tflops": lay.flops / tl[vn] / 1e12,

@@ -138,6 +138,46 @@ rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, i
 rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, const void* X,
                                 const void* W, void* Y, void* stream);
 
+/*
+ * FP8 (E4M3) variant.  The summary page ("RT-Lynx: Putting the GEMM Sparsity In a Right
+ * Way for Diffusion Models", limitations and future work) names FP8 as the next step
+ * without fixing a scheme.  Here only the sparse product runs in 8 bits:
+ *   Y[i,n] = s_i * sx_i * sw_n * sum_k Xq~[i,k] Wq[n,k] + (X L_B^T L_A^T)[i,n]
+ * with the selection, s and the low-rank branch of the bf16 layer.  E4M3 is the OCP
+ * 8-bit format (bias 7, largest finite 448, no infinities).  Scales are per row: a row of
+ * values v with largest magnitude a is coded as e4m3(fl32(v * fl32(448 / a))), rounded
+ * to nearest even, with dequantisation scale fl32(a / 448); a row whose 448 / a is not
+ * finite (a == 0, or a below about 1.3e-36) is coded as zeros.
+ */
+
+/*
+ * Weight quantisation (once per weight): W [N,K] bf16 -> Wq [N,K] E4M3 codes and
+ * sw [N] fp32 scales, one per output row.  Needs K % 8 == 0.  Wq and sw must not
+ * overlap W or each other.
+ */
+rtl_status rtl_quantize_weight_fp8(int64_t N, int64_t K, const void* W, uint8_t* Wq, float* sw,
+                                   void* stream);
+
+/* Workspace bytes of rtl_linear_fused_fp8 for this shape. */
+size_t rtl_linear_fused_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R);
+
+/*
+ * The FP8 layer: X [M,K], LA [N,R], LB [R,K], Y [M,N] bf16; Wq [N,K] and sw [N] from
+ * rtl_quantize_weight_fp8.  A pre-pass over X forms T = X L_B^T, s and the selection
+ * (as in the bf16 layer) and each row's largest magnitude; a pack kernel codes the kept
+ * values of each row in E4M3 with that row's scale, in the operand order of the 2:4 fp8
+ * MFMA; the GEMM runs on that MFMA and its epilogue applies sw, the rank-R slice and
+ * s * sx before the single bf16 store of Y.  Limits: K % 128 == 0, R % 32 == 0,
+ * R <= 128.  dbg_xq [M,K/2] (E4M3 codes of the kept values, two per group in position
+ * order) and dbg_sx [M] (sx) are optional; when given, the pack kernel writes the codes
+ * and scales it computed.  Y must not overlap any input; calls that share a workspace
+ * must be serialised.  Validation and errors as for rtl_linear_fused.
+ */
+rtl_status rtl_linear_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
+                                const uint8_t* Wq, const float* sw, const void* LA, const void* LB,
+                                rtl_tie_rule tie, float eps, void* Y, void* workspace, size_t ws_bytes,
+                                uint8_t* dbg_xq, float* dbg_sx, void* stream);
+
 const char* rtl_status_string(rtl_status st);
 const char* rtl_last_error(void); /* message of this thread's last failed call, or "" */
 int rtl_version(void);            /* major * 10000 + minor * 100 + patch */

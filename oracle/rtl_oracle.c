@@ -30,6 +30,7 @@
  * Parity status of every function: pinned by the CPU tests (brute force, closed forms,
  * invariants and library special cases); none is "parity unpinned".
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -281,7 +282,8 @@ int orc_dense(int dt, int64_t M, int64_t N, int64_t K, const void* X, const void
  *     infinities; S.1111.111 is NaN; the largest finite magnitude is 448;
  *   - rounding to nearest, ties to the even code;
  *   - one scale per row of values (per token row of X~, per output row of W):
- *     a = max |v|, inv = fl32(448 / a) (0 when a = 0), code = e4m3(fl32(v * inv)),
+ *     a = max |v|, inv = fl32(448 / a) (0 when that is not finite: a = 0, or a below
+ *     448 / FLT_MAX), code = e4m3(fl32(v * inv)),
  *     dequantisation scale sc = fl32(a / 448); fl32() is IEEE single rounding, the
  *     precision in which the value that decides the 8-bit code is formed;
  *   - the selection, s and the low-rank branch are those of the bf16 layer (computed on
@@ -334,7 +336,10 @@ int orc_quantize_rows(int64_t rows, int64_t K, const float* v, uint8_t* codes, f
       if (!isfinite(t)) bad = 1;
       if (t > a) a = t;
     }
-    const float inv = a > 0.0f ? 448.0f / a : 0.0f;
+    /* 448 / a is infinite for a = 0 and for a below 448 / FLT_MAX: such a row
+     * quantises to zeros (its sparse term is below 1e-60 in any case) */
+    float inv = 448.0f / a;
+    if (!(inv <= FLT_MAX)) inv = 0.0f;
     scale[i] = a / 448.0f;
     for (int64_t k = 0; k < K; k++) {
       const float p = v[i * K + k] * inv;

@@ -17,7 +17,7 @@ rtl = pytest.importorskip("activation_sparse_gemm_amd")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rtl_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rtl_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -223,3 +223,71 @@ def test_error_messages_are_per_thread():
     assert seen["shape"][1] != seen["eps"][1]
     assert "4" in seen["shape"][1] or "K" in seen["shape"][1]
     assert "eps" in seen["eps"][1].lower()
+
+
+def call_fp8(M=64, N=64, K=256, R=32, tie=0, eps=1e-8, ws_bytes=None, **over):
+    h = Host()
+    X, _ = h.buf(M * K * 2)
+    Wq, _ = h.buf(N * K)
+    sw, _ = h.buf(N * 4 + 16)
+    LA, _ = h.buf(max(N * R * 2, 16))
+    LB, _ = h.buf(max(R * K * 2, 16))
+    Y, _ = h.buf(M * N * 2)
+    need = rtl.rtl_linear_fused_fp8_workspace_bytes(max(M, 1), max(N, 1), 256 if K % 128 else max(K, 128), max(R, 0))
+    ws, _ = h.buf(max(need, 16))
+    args = dict(X=X, Wq=Wq, sw=sw, LA=LA, LB=LB, Y=Y, ws=ws)
+    args.update(over)
+    st = rtl.lib.rtl_linear_fused_fp8(M, N, K, R, args["X"], args["Wq"], args["sw"], args["LA"], args["LB"], tie, eps,
+                                      args["Y"], args["ws"], need if ws_bytes is None else ws_bytes, None, None, None)
+    return st, h
+
+
+def test_fp8_rejects_bad_calls():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    cases = [
+        (dict(K=258), "RTL_ERR_SHAPE"),
+        (dict(M=0), "RTL_ERR_SHAPE"),
+        (dict(R=-1), "RTL_ERR_SHAPE"),
+        (dict(K=192), "RTL_ERR_UNSUPPORTED"),   # needs K % 128 == 0
+        (dict(R=48), "RTL_ERR_UNSUPPORTED"),
+        (dict(R=160), "RTL_ERR_UNSUPPORTED"),
+        (dict(tie=1), "RTL_ERR_UNSUPPORTED"),
+        (dict(eps=float("nan")), "RTL_ERR_ARG"),
+        (dict(sw=None), "RTL_ERR_NULL"),
+        (dict(Wq=None), "RTL_ERR_NULL"),
+        (dict(LA=None), "RTL_ERR_NULL"),
+        (dict(ws_bytes=16), "RTL_ERR_WORKSPACE"),
+        (dict(ws=None), "RTL_ERR_WORKSPACE"),
+    ]
+    for over, want in cases:
+        st, h = call_fp8(**over)
+        assert st == inv[want], (over, rtl.STATUS.get(st))
+        assert h.untouched()
+        assert rtl.lib.rtl_last_error().decode() != ""
+    h = Host()
+    X, _ = h.buf(64 * 256 * 2)
+    assert call_fp8(X=X, Y=X)[0] == inv["RTL_ERR_ARG"]
+    assert call_fp8(X=ctypes.c_void_p(X.value + 4))[0] == inv["RTL_ERR_ALIGN"]
+
+
+def test_fp8_quantize_weight_rejects_bad_calls():
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    h = Host()
+    W, _ = h.buf(64 * 128 * 2)
+    Wq, _ = h.buf(64 * 128)
+    sw, _ = h.buf(64 * 4)
+    L = rtl.lib
+    assert L.rtl_quantize_weight_fp8(64, 100, W, Wq, sw, None) == inv["RTL_ERR_SHAPE"]
+    assert L.rtl_quantize_weight_fp8(0, 128, W, Wq, sw, None) == inv["RTL_ERR_SHAPE"]
+    assert L.rtl_quantize_weight_fp8(64, 128, W, None, sw, None) == inv["RTL_ERR_NULL"]
+    assert L.rtl_quantize_weight_fp8(64, 128, W, W, sw, None) == inv["RTL_ERR_ARG"]
+    assert L.rtl_quantize_weight_fp8(64, 128, W, ctypes.c_void_p(Wq.value + 8), sw, None) == inv["RTL_ERR_ALIGN"]
+    assert h.untouched()
+
+
+def test_fp8_workspace_bytes():
+    Wb = rtl.rtl_linear_fused_fp8_workspace_bytes
+    need = Wb(4096, 3072, 3072, 64)
+    # the bf16 layer's workspace plus row absmax and the 8-bit operand (M*K/2 codes, M*K/32 position bytes)
+    assert need >= rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, 4096, 3072, 3072, 64) + 4096 * 1536 + 4096 * 96
+    assert Wb(4096, 3072, 3000, 64) == 0 and Wb(0, 3072, 3072, 64) == 0

@@ -110,6 +110,12 @@ def test_quantize_rows_invariants():
                         2.0 ** -9)
         assert np.all(np.abs(dec[i] - y) <= step / 2 + np.abs(y) * 2.0 ** -22)
     assert dec[7, 5] == -448.0 and np.count_nonzero(codes[7]) == 1
+    # a row whose 448 / a overflows fp32 quantises to zeros (the stated rule), and one just
+    # above that limit still reaches 448
+    tiny = np.array([[1e-37, -5e-38, 0.0, 2e-38], [2e-36, 1e-36, 0.0, -2e-36]], np.float32)
+    c2, s2 = oracle.quantize_rows(tiny)
+    assert all(oracle.e4m3_value(c) == 0.0 for c in c2[0]) and s2[0] == np.float32(1e-37) / np.float32(448.0)
+    assert oracle.e4m3_value(c2[1, 0]) == 448.0 and oracle.e4m3_value(c2[1, 3]) == -448.0
 
 
 def _exact_inputs(M, K, N, R, seed):
