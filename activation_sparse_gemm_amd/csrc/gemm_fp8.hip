@@ -10,29 +10,17 @@
 // whose 448 / a is not finite quantises to zeros.
 //
 //  quant_w_kernel:   W [N,K] bf16 -> Wq [N,K] E4M3 codes and sw [N] (once per weight).
-//  fp8_pack_kernel:  the pre-pass's bf16 sparse operand and row absmax -> the 8-bit
-//                    sparse operand in the register order of the 2:4 fp8 MFMA.
+//  (the pre-pass and its pack kernel, which forms the 8-bit sparse operand, are in
+//   prep_bf16.hip)
 //  gemm_fp8_kernel:  the product on v_smfmac_f32_16x16x128_fp8_fp8, 256 x TN tiles, W
 //                    through a 3-buffer LDS ring (its [TN][128] byte tiles have the
 //                    layout of the bf16 kernel's [TN][64] element tiles), the
 //                    compressed operand straight to registers one K step ahead; the
 //                    epilogue scales by sw, adds the rank-R slice and stores s sx acc.
+#include "fp8_common.h"
 #include "gemm_common.h"
 
 namespace rtl {
-
-// Four floats -> four E4M3 codes (round to nearest even), first value in the low byte.
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, 0, false) & 0xFFFFu;
-  return lo | (hi << 16);
-}
-
-// 448 / a in fp32, or 0 where that is not finite (a = 0 or a tiny).
-__device__ __forceinline__ float fp8_inv_scale(float a) {
-  const float inv = 448.0f / a;
-  return inv <= 3.402823466e38f ? inv : 0.0f;
-}
 
 // One wave per row of W: its largest magnitude, then its codes (8 per lane and pass).
 __global__ __launch_bounds__(256) void quant_w_kernel(int64_t N, int64_t K, const uint16_t* W, uint8_t* Wq,
@@ -59,48 +47,6 @@ __global__ __launch_bounds__(256) void quant_w_kernel(int64_t N, int64_t K, cons
     o[1] = fp8x4(bf16lo(v[2]) * inv, bf16hi(v[2]) * inv, bf16lo(v[3]) * inv, bf16hi(v[3]) * inv);
     *reinterpret_cast<u32x2*>(Wq + n * K + 8 * c) = o;
   }
-}
-
-struct PackArgs {
-  int64_t M, K;
-  const uint8_t* cvals;  // bf16 sparse operand (pre-pass layout)
-  const uint8_t* cidx;
-  const float* ax;       // [Mp] row absmax
-  uint8_t* cvals8;       // 8-bit sparse operand
-  uint8_t* cidx8;
-  uint8_t* dbg_xq;       // [M, K/2] codes in row order, or null
-  float* dbg_sx;         // [M], or null
-};
-
-// Workgroup (128-wide K step kt, panel p); thread (row block rb, lane l) packs the 16 kept
-// values of row 16rb + l%16 over dense k 32(l/16)..+31 of the step: lanes 2(l/16 % 2) and
-// 2(l/16 % 2) + 1 (times 16, plus l%16) of the bf16 operand's step 2kt + (l/16) / 2.
-__global__ __launch_bounds__(256) void fp8_pack_kernel(const PackArgs a) {
-  const int tid = threadIdx.x, rb = tid >> 6, l = tid & 63, q = l >> 4, r = l & 15;
-  const int kt = blockIdx.x;
-  const int64_t p = blockIdx.y;
-  const int KT = (int)(a.K / kBK), KT8 = (int)(a.K / 128);
-  const int s = 2 * kt + (q >> 1);
-  const int l0 = 16 * (2 * (q & 1)) + r, l1 = l0 + 16;
-  const uint8_t* vb = a.cvals + cvals_off(p, KT, s) + rb * 1024;
-  const u32x4 v0 = *reinterpret_cast<const u32x4*>(vb + l0 * 16);
-  const u32x4 v1 = *reinterpret_cast<const u32x4*>(vb + l1 * 16);
-  const uint8_t* ib = a.cidx + cidx_off(p, KT, s);
-  const uint32_t c0 = *reinterpret_cast<const uint16_t*>(ib + l0 * 8 + rb * 2);
-  const uint32_t c1 = *reinterpret_cast<const uint16_t*>(ib + l1 * 8 + rb * 2);
-  const int64_t row = p * kPanel + 16 * rb + r;
-  const float ax = a.ax[row];
-  const float inv = fp8_inv_scale(ax);
-  u32x4 o;
-  o[0] = fp8x4(bf16lo(v0[0]) * inv, bf16hi(v0[0]) * inv, bf16lo(v0[1]) * inv, bf16hi(v0[1]) * inv);
-  o[1] = fp8x4(bf16lo(v0[2]) * inv, bf16hi(v0[2]) * inv, bf16lo(v0[3]) * inv, bf16hi(v0[3]) * inv);
-  o[2] = fp8x4(bf16lo(v1[0]) * inv, bf16hi(v1[0]) * inv, bf16lo(v1[1]) * inv, bf16hi(v1[1]) * inv);
-  o[3] = fp8x4(bf16lo(v1[2]) * inv, bf16hi(v1[2]) * inv, bf16lo(v1[3]) * inv, bf16hi(v1[3]) * inv);
-  *reinterpret_cast<u32x4*>(a.cvals8 + cvals8_off(p, KT8, kt) + rb * 1024 + l * 16) = o;
-  *reinterpret_cast<uint32_t*>(a.cidx8 + cidx8_off(p, KT8, kt) + l * 16 + rb * 4) = c0 | (c1 << 16);
-  if (a.dbg_xq != nullptr && row < a.M)
-    *reinterpret_cast<u32x4*>(a.dbg_xq + row * (a.K / 2) + 64 * kt + 16 * q) = o;
-  if (a.dbg_sx != nullptr && kt == 0 && q == 0 && row < a.M) a.dbg_sx[row] = ax / 448.0f;
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -323,19 +269,11 @@ hipError_t launch_quant_w_fp8(int64_t N, int64_t K, const void* W, uint8_t* Wq, 
 hipError_t launch_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const uint8_t* Wq,
                             const float* sw, const void* LA, const void* LB, float eps, void* Y, void* ws,
                             uint8_t* dbg_xq, float* dbg_sx, hipStream_t stream) {
-  hipError_t e = launch_prep_fp8(M, K, R, X, LB, eps, ws, nullptr, stream);
+  hipError_t e = launch_prep_fp8(M, K, R, X, LB, eps, ws, dbg_xq, dbg_sx, stream);
   if (e != hipSuccess) return e;
   const Fp8WsLayout F = fp8_ws_layout(M, K, R);
   uint8_t* base = (uint8_t*)ws;
   const int64_t Mp = padded_rows(M);
-  PackArgs pk{};
-  pk.M = M; pk.K = K;
-  pk.cvals = base + F.L.cvals; pk.cidx = base + F.L.cidx; pk.ax = (const float*)(base + F.ax);
-  pk.cvals8 = base + F.cvals8; pk.cidx8 = base + F.cidx8;
-  pk.dbg_xq = dbg_xq; pk.dbg_sx = dbg_sx;
-  hipLaunchKernelGGL(fp8_pack_kernel, dim3((unsigned)(K / kBK8), (unsigned)(Mp / kPanel)), dim3(256), 0, stream, pk);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int tn = choose_tn(M, N);
   GemmArgs g{};
   g.M = M; g.N = N; g.K = K; g.R = R;

@@ -5,6 +5,7 @@
 // the pre-compressed variant, the 2-of-4 selection itself: the kept values and their
 // 2-bit positions, written in the register order of the sparse MFMA's A operand, and s.
 #include "bf16_common.h"
+#include "fp8_common.h"
 
 namespace rtl {
 
@@ -201,15 +202,12 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   }
 }
 
-// Sums the K-split partials of prep_kernel in split order: T (rounded to bf16) and s (or
-// ||X||^2 for the prologue variant).  One thread per (row, 4 columns of T).
+// One item of the K-split reduction of prep_kernel's partials, summed in split order:
+// c < R/4 -> columns 4c..4c+3 of T (rounded to bf16); c == R/4 -> s (or ||X||^2 for the
+// prologue variant) and, for the FP8 layer, the row absmax.
 template <bool COMPRESS>
-__global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepArgs a, int64_t Mp) {
+__device__ __forceinline__ void reduce_item(const PrepArgs& a, int64_t Mp, int64_t row, int64_t c) {
   const int64_t R = a.R;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // row * (R/4 + 1) + c
-  const int64_t per = R / 4 + 1;
-  if (e >= Mp * per) return;
-  const int64_t row = e / per, c = e % per;
   if (c < R / 4) {
     // Loads in batches of 8 (all in flight together), sums in split order.
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
@@ -253,16 +251,90 @@ __global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepArgs a, int6
     }
     if (a.ax != nullptr) {  // FP8 layer: largest magnitude over the splits
       float m = 0.f;
-      for (int sp = 0; sp < a.ks; sp++) m = fmaxf(m, a.apart[sp * Mp + row]);
+      for (int s0 = 0; s0 < a.ks; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = a.apart[min(s0 + u, a.ks - 1) * Mp + row];
+#pragma unroll
+        for (int u = 0; u < 8; u++) m = fmaxf(m, v[u]);
+      }
       a.ax[row] = m;
     }
   }
 }
 
+// The K-split reduction: one thread per (row, 4 columns of T) plus one per row for the norms.
+template <bool COMPRESS>
+__global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepArgs a, int64_t Mp) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // row * (R/4 + 1) + c
+  const int64_t per = a.R / 4 + 1;
+  if (e >= Mp * per) return;
+  reduce_item<COMPRESS>(a, Mp, e / per, e % per);
+}
+
+// FP8 layer: the 8-bit sparse operand from the pre-pass's bf16 operand.  Workgroup
+// (128-wide K step kt, panel p); thread (row block rb, lane l) packs the 16 kept values of
+// row 16rb + l%16 over dense k 32(l/16)..+31 of the step (lanes 16 (2 (l/16 % 2)) + l%16
+// and +16 of the bf16 operand's step 2kt + (l/16) / 2), scaled by 448 / ax of the row and
+// rounded to E4M3, and joins their two 16-bit position words.  When K is split (REDUCE)
+// the row absmax comes from the split partials, and the K-step workgroups of a panel share
+// out the split reduction of its 64 rows (T, s, ax), which the GEMM reads next.
+struct PackArgs {
+  uint8_t* cvals8;  // 8-bit sparse operand (layout in bf16_common.h)
+  uint8_t* cidx8;
+  uint8_t* dbg_xq;  // [M, K/2] codes in row order, or null
+  float* dbg_sx;    // [M], or null
+};
+template <bool REDUCE>
+__global__ __launch_bounds__(256) void fp8_pack_kernel(const PrepArgs a, const PackArgs pk, int64_t Mp) {
+  const int tid = threadIdx.x, rb = tid >> 6, l = tid & 63, q = l >> 4, r = l & 15;
+  const int kt = blockIdx.x;
+  const int64_t p = blockIdx.y;
+  const int KT = (int)(a.K / kBK), KT8 = (int)(a.K / 128);
+  if (REDUCE) {
+    const int64_t per = a.R / 4 + 1, items = kPanel * per;
+    const int64_t chunk = (items + KT8 - 1) / KT8;
+    const int64_t i0 = kt * chunk, i1 = min(items, i0 + chunk);
+    for (int64_t it = i0 + tid; it < i1; it += 256) reduce_item<true>(a, Mp, p * kPanel + it / per, it % per);
+  }
+  const int s = 2 * kt + (q >> 1);
+  const int l0 = 16 * (2 * (q & 1)) + r, l1 = l0 + 16;
+  const uint8_t* vb = a.cvals + cvals_off(p, KT, s) + rb * 1024;
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(vb + l0 * 16);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(vb + l1 * 16);
+  const uint8_t* ib = a.cidx + cidx_off(p, KT, s);
+  const uint32_t c0 = *reinterpret_cast<const uint16_t*>(ib + l0 * 8 + rb * 2);
+  const uint32_t c1 = *reinterpret_cast<const uint16_t*>(ib + l1 * 8 + rb * 2);
+  const int64_t row = p * kPanel + 16 * rb + r;
+  float ax = 0.f;
+  if (REDUCE) {
+    for (int s0 = 0; s0 < a.ks; s0 += 8) {  // loads in batches of 8, all in flight together
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) v[u] = a.apart[min(s0 + u, a.ks - 1) * Mp + row];
+#pragma unroll
+      for (int u = 0; u < 8; u++) ax = fmaxf(ax, v[u]);
+    }
+  } else {
+    ax = a.ax[row];
+  }
+  const float inv = fp8_inv_scale(ax);
+  u32x4 o;
+  o[0] = fp8x4(bf16lo(v0[0]) * inv, bf16hi(v0[0]) * inv, bf16lo(v0[1]) * inv, bf16hi(v0[1]) * inv);
+  o[1] = fp8x4(bf16lo(v0[2]) * inv, bf16hi(v0[2]) * inv, bf16lo(v0[3]) * inv, bf16hi(v0[3]) * inv);
+  o[2] = fp8x4(bf16lo(v1[0]) * inv, bf16hi(v1[0]) * inv, bf16lo(v1[1]) * inv, bf16hi(v1[1]) * inv);
+  o[3] = fp8x4(bf16lo(v1[2]) * inv, bf16hi(v1[2]) * inv, bf16lo(v1[3]) * inv, bf16hi(v1[3]) * inv);
+  *reinterpret_cast<u32x4*>(pk.cvals8 + cvals8_off(p, KT8, kt) + rb * 1024 + l * 16) = o;
+  *reinterpret_cast<uint32_t*>(pk.cidx8 + cidx8_off(p, KT8, kt) + l * 16 + rb * 4) = c0 | (c1 << 16);
+  if (pk.dbg_xq != nullptr && row < a.M)
+    *reinterpret_cast<u32x4*>(pk.dbg_xq + row * (a.K / 2) + 64 * kt + 16 * q) = o;
+  if (pk.dbg_sx != nullptr && kt == 0 && q == 0 && row < a.M) pk.dbg_sx[row] = ax / 448.0f;
+}
+
 // The pre-pass launches (prep_kernel, then the split reduction when K is split).
 template <bool AMAX>
 static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const PrepSplit& sp, int64_t R,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool reduce = true) {
   const dim3 grid((unsigned)(Mp / (16 * sp.waves)), (unsigned)sp.ks), block(64 * sp.waves);
 #define RTL_PREP(C, RC)                                                                          \
   do {                                                                                           \
@@ -292,7 +364,7 @@ static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const 
     }
   }
 #undef RTL_PREP
-  if (sp.ks > 1) {
+  if (sp.ks > 1 && reduce) {
     const int64_t items = Mp * (R / 4 + 1);
     const dim3 rgrid((unsigned)((items + 255) / 256)), rblock(256);
     if (comp) hipLaunchKernelGGL((prep_reduce_kernel<true>), rgrid, rblock, 0, stream, p, Mp);
@@ -342,8 +414,10 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   return hipGetLastError();
 }
 
+// FP8 layer: the pre-pass (with row absmax, without the split reduction), then the pack
+// kernel (which also does the split reduction when K is split).
 hipError_t launch_prep_fp8(int64_t M, int64_t K, int64_t R, const void* X, const void* LB, float eps, void* ws,
-                           float* dbg_s, hipStream_t stream) {
+                           uint8_t* dbg_xq, float* dbg_sx, hipStream_t stream) {
   const Fp8WsLayout F = fp8_ws_layout(M, K, R);
   uint8_t* base = (uint8_t*)ws;
   PrepArgs p{};
@@ -358,10 +432,17 @@ hipError_t launch_prep_fp8(int64_t M, int64_t K, int64_t R, const void* X, const
   p.s = (float*)(base + F.L.norm);
   p.cvals = base + F.L.cvals;
   p.cidx = base + F.L.cidx;
-  p.dbg_s = dbg_s;
   p.ax = (float*)(base + F.ax);
   p.apart = (float*)(base + F.apart);
-  launch_prep_kernels<true>(p, true, Mp, sp, R, stream);
+  launch_prep_kernels<true>(p, true, Mp, sp, R, stream, false);
+  PackArgs pk{};
+  pk.cvals8 = base + F.cvals8;
+  pk.cidx8 = base + F.cidx8;
+  pk.dbg_xq = dbg_xq;
+  pk.dbg_sx = dbg_sx;
+  const dim3 grid((unsigned)(K / 128), (unsigned)(Mp / kPanel)), block(256);
+  if (sp.ks > 1) hipLaunchKernelGGL(fp8_pack_kernel<true>, grid, block, 0, stream, p, pk, Mp);
+  else hipLaunchKernelGGL(fp8_pack_kernel<false>, grid, block, 0, stream, p, pk, Mp);
   return hipGetLastError();
 }
 

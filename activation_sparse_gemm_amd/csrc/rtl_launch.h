@@ -33,7 +33,7 @@ hipError_t launch_dense_bf16(int64_t M, int64_t N, int64_t K, const void* X, con
 size_t fused_fp8_workspace(int64_t M, int64_t N, int64_t K, int64_t R);
 hipError_t launch_quant_w_fp8(int64_t N, int64_t K, const void* W, uint8_t* Wq, float* sw, hipStream_t stream);
 hipError_t launch_prep_fp8(int64_t M, int64_t K, int64_t R, const void* X, const void* LB, float eps, void* ws,
-                           float* dbg_s, hipStream_t stream);
+                           uint8_t* dbg_xq, float* dbg_sx, hipStream_t stream);
 hipError_t launch_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const uint8_t* Wq,
                             const float* sw, const void* LA, const void* LB, float eps, void* Y, void* ws,
                             uint8_t* dbg_xq, float* dbg_sx, hipStream_t stream);
