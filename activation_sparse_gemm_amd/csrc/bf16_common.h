@@ -25,6 +25,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier without a memory fence.  Loads into LDS that bypass the registers are
+// not waited for by a fence-free barrier, so the caller first waits (wait_vmcnt) for the
+// ones the other waves will read; the empty asm statements keep the compiler from moving
+// memory operations across the barrier.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Raw buffer resource over [base, base + bytes) (bytes clamped to 32 bits): loads at or
 // past the end return zeros, stores there are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

@@ -19,11 +19,12 @@ namespace rtl {
 constexpr int kModeDense = 0, kModeFused = 1, kModeComp = 2;
 
 // GEMM workgroup: 8 waves (two per SIMD) on a 256 x TN output tile (TN = 192 or 256); wave w
-// owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  W (and, on 256-wide pre-compressed
-// tiles, the compressed operand) goes memory -> registers -> LDS: a 3-buffer ring in the
-// pre-compressed mode (loaded a step before it is written, written two steps before it is
-// used), a 2-buffer ring in the dense and fused modes.  On 192-wide pre-compressed tiles
-// each wave loads its compressed rows straight into registers a step ahead.  Fused mode:
+// owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  On 192-wide pre-compressed tiles
+// W goes straight from memory into a 4-buffer LDS ring (three steps ahead) and each wave
+// loads its compressed rows straight into registers a step ahead.  Elsewhere W (and, on
+// 256-wide pre-compressed tiles, the compressed operand) goes memory -> registers -> LDS:
+// a 3-buffer ring in the pre-compressed mode (loaded a step before it is written, written
+// two steps before it is used), a 2-buffer ring in the dense and fused modes.  Fused mode:
 // of each row slab, the two waves that share it select two 16-row blocks each and trade
 // the compressed operand through LDS.
 constexpr int kGemmThreads = 512;
@@ -41,7 +42,10 @@ void gemm_kernel(const GemmArgs a) {
   constexpr bool SPARSE = MODE != kModeDense;
   constexpr bool FUSED = MODE == kModeFused;
   constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[(MODE == kModeComp ? 3 : 2) * TN * 128];
+  // Pre-compressed 192-wide tiles load W straight into a 4-buffer LDS ring (DTLW).
+  constexpr bool DTLW = MODE == kModeComp && TN == 192;
+  constexpr int WBUF = DTLW ? 4 : (MODE == kModeComp ? 3 : 2);
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TN * 128];
   // Pre-compressed operand through LDS on 256-wide tiles (there the smaller VMEM traffic
   // wins); straight to registers on 192-wide tiles (there the smaller LDS traffic wins).
   constexpr bool CALDS = MODE == kModeComp && TN == 256;
@@ -261,7 +265,7 @@ void gemm_kernel(const GemmArgs a) {
   // Pre-compressed mode on 192-wide tiles: the operand is stored in MFMA register order,
   // so each wave loads its own 64 rows straight into registers (one 16-byte load per lane
   // and row block, one 8-byte load of position words), one K step ahead; only W goes
-  // through LDS.
+  // through LDS (DTLW, step_dtl below).
   // The wave's panel through buffer resources (wave-uniform base, scalar step offsets).
   const __amdgpu_buffer_rsrc_t cvres =
       make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 4096);
@@ -309,6 +313,52 @@ void gemm_kernel(const GemmArgs a) {
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
     return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
+  // Direct-to-LDS W staging (DTLW): the i-th 16-byte load of lane l in wave w lands at byte
+  // (8 i + w) * 1024 + 16 l of its LDS stage (the hardware writes lane l at 16 l past the
+  // wave's LDS base), i.e. row n = 64 i + 8 w + l / 8 at swizzled position l % 8, which
+  // sw_off assigns to logical chunk (l % 8) ^ (n % 8): each lane loads that chunk.
+  const uint32_t d_voff = (uint32_t)(srow * K * 2 + 16 * ((lane & 7) ^ (srow & 7)));
+  auto dtl_w = [&](int kt, int buf, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wres, (__attribute__((address_space(3))) void*)(wl + buf * TN * 128 + (8 * i + wave) * 1024), 16, d_voff,
+        (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
+  };
+  // DTLW step kt on ring buffer kt % 4: blocks 0-2 load the A fragments of step kt + 1
+  // into registers; each of the last WLD blocks loads one chunk of W stage kt + 3 into
+  // buffer (kt + 3) % 4 (last read in step kt - 1).  Before the barrier each wave waits
+  // for its loads of stage kt + 2 (issued a step ago; 8 loads were issued after them), so
+  // the first B fragments of step kt + 1, read before the barrier, find their buffer
+  // complete.
+  auto step_dtl = [&](int kt, int buf, const AFrag& cur, AFrag& anext) {
+    const int nbuf = buf == WBUF - 1 ? 0 : buf + 1, dbuf = buf == 0 ? WBUF - 1 : buf - 1;
+    u32x8 bq[3];
+    bq[0] = bp0;
+    bq[1] = bp1;
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
+      if (nb < 3) {
+        load_frag_part(kp(kt + 1), anext, 2 * nb);
+        if (nb < 2) load_frag_part(kp(kt + 1), anext, 2 * nb + 1);
+      }
+      if (nb >= NB - WLD) dtl_w(kp(kt + 3), dbuf, nb - (NB - WLD));
+      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
+      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
+                                                             (int)cur.iw[0], 0, 0);
+      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1][0]), bv, acc[1][nb],
+                                                             (int)cur.iw[0], 0, 1);
+      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2][0]), bv, acc[2][nb],
+                                                             (int)cur.iw[1], 0, 0);
+      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3][0]), bv, acc[3][nb],
+                                                             (int)cur.iw[1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bp0 = read_bc(nbuf, 0);
+    bp1 = read_bc(nbuf, 1);
+    wait_vmcnt<WLD + 5>();
+    barrier_nofence();
+  };
+
   // Compressed operand through LDS: thread t moves value chunks t and t + 512 (panels
   // t / 256 and t / 256 + 2) and position word t (panel t / 128) of a K step; one LDS
   // stage holds the tile's four panels (values, then position words).
@@ -383,39 +433,6 @@ void gemm_kernel(const GemmArgs a) {
     bp0 = read_bc(nbuf, 0);
     bp1 = read_bc(nbuf, 1);
     read_afrag(nbuf, nxt);
-    __syncthreads();
-  };
-
-  auto step_c = [&](int kt, int buf, WStage& wst, WStage& wfree, const AFrag& cur, AFrag& anext) {
-    const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
-    u32x8 bq[3];
-    bq[0] = bp0;
-    bq[1] = bp1;
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
-      if (nb < 3) {
-        load_frag_part(kp(kt + 1), anext, 2 * nb);
-        if (nb < 2) load_frag_part(kp(kt + 1), anext, 2 * nb + 1);
-      }
-      if (nb >= NB - WLD) {
-        const int i = nb - (NB - WLD);
-        *reinterpret_cast<u32x4*>(wl + sbuf * TN * 128 + sw_off(srow + 64 * i, schunk)) = wst[i];
-        load_w_part(kp(kt + 3), wfree, i);
-      }
-      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
-      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
-                                                             (int)cur.iw[0], 0, 0);
-      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1][0]), bv, acc[1][nb],
-                                                             (int)cur.iw[0], 0, 1);
-      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2][0]), bv, acc[2][nb],
-                                                             (int)cur.iw[1], 0, 0);
-      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3][0]), bv, acc[3][nb],
-                                                             (int)cur.iw[1], 0, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bp0 = read_bc(nbuf, 0);
-    bp1 = read_bc(nbuf, 1);
     __syncthreads();
   };
 
@@ -534,47 +551,38 @@ void gemm_kernel(const GemmArgs a) {
         }
       }
     }
-  } else if constexpr (MODE == kModeComp) {
+  } else if constexpr (DTLW) {
     AFrag f0, f1;
-    // same issue order as the loop (A, then W) so the wait counts at the loop head match
-    // the steady state
+    // The A fragments of step 0, then W stages 0-2 into buffers 0-2 (A before W, as in
+    // the loop, so the wait counts at the loop head match the steady state); stages 0
+    // and 1 complete before the first B reads.
     load_frag(kp(0), f0);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(kp(0), w0);
-    load_w(kp(1), w1);
-    __builtin_amdgcn_sched_barrier(0);
-    store_w(w0, 0);
-    store_w(w1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(kp(2), w0);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 3; st++)
+#pragma unroll
+      for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+    wait_vmcnt<WLD>();
+    barrier_nofence();
     bp0 = read_bc(0, 0);
     bp1 = read_bc(0, 1);
-    // LDS buffers cycle with period 3, W register sets and A fragment sets with period 2:
-    // whole periods of 6 steps in the loop, then the rest.
+    // Ring buffers cycle with period 4, A fragment sets with period 2: whole periods of 4
+    // steps in the loop (no exit in its body), then the rest.
     int kt = 0;
-    for (; kt + 6 <= KT; kt += 6) {
-      step_c(kt, 0, w0, w1, f0, f1);
-      step_c(kt + 1, 1, w1, w0, f1, f0);
-      step_c(kt + 2, 2, w0, w1, f0, f1);
-      step_c(kt + 3, 0, w1, w0, f1, f0);
-      step_c(kt + 4, 1, w0, w1, f0, f1);
-      step_c(kt + 5, 2, w1, w0, f1, f0);
+    for (; kt + 4 <= KT; kt += 4) {
+      step_dtl(kt, 0, f0, f1);
+      step_dtl(kt + 1, 1, f1, f0);
+      step_dtl(kt + 2, 2, f0, f1);
+      step_dtl(kt + 3, 3, f1, f0);
     }
     if (kt < KT) {
-      step_c(kt, 0, w0, w1, f0, f1);
+      step_dtl(kt, 0, f0, f1);
       if (kt + 1 < KT) {
-        step_c(kt + 1, 1, w1, w0, f1, f0);
-        if (kt + 2 < KT) {
-          step_c(kt + 2, 2, w0, w1, f0, f1);
-          if (kt + 3 < KT) {
-            step_c(kt + 3, 0, w1, w0, f1, f0);
-            if (kt + 4 < KT) step_c(kt + 4, 1, w0, w1, f0, f1);
-          }
-        }
+        step_dtl(kt + 1, 1, f1, f0);
+        if (kt + 2 < KT) step_dtl(kt + 2, 2, f0, f1);
       }
     }
+    wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
   } else {
   AStage a0, a1;
   load_w(0, w0);
@@ -673,8 +681,9 @@ void gemm_kernel(const GemmArgs a) {
 // output tile, wave w owns rows 64w..64w+63 and all TW columns.  The two workgroups on a
 // CU reach their barriers at different times, so one's matrix-core work covers the
 // other's step boundary.  Per step each wave loads its own compressed rows straight into
-// registers (no sharing, no duplication) and the workgroup stages a TW x 64 W tile
-// through a 3-buffer LDS ring, with the same interleaving and K stagger as gemm_kernel.
+// registers (no sharing, no duplication) and the workgroup loads a TW x 64 W tile
+// straight into a 4-buffer LDS ring (no register staging), with the same interleaving
+// and K stagger as gemm_kernel.
 constexpr int kHalfThreads = 256;
 
 template <int TW>
@@ -683,7 +692,8 @@ void half_kernel(const GemmArgs a) {
   static_assert(TW == 128 || TW == 96, "tile widths");
   constexpr int NB = TW / 16;                   // 16-column blocks per wave
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[3 * TW * 128];
+  constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TW * 128];
 
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
@@ -694,22 +704,9 @@ void half_kernel(const GemmArgs a) {
   const int64_t M = a.M, N = a.N, K = a.K;
   const int KT = (int)(K / kBK);
 
-  // W staging: thread t moves chunks (row t/8 + 32i, k chunk t%8), i < WLD; columns past
-  // N read as zeros.
+  // W staging: thread t moves rows t/8 + 32i, i < WLD; columns past N read as zeros.
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(a.W + n0 * K, (N - n0) * K * 2);
-  const int srow = tid >> 3, schunk = tid & 7;
-  const uint32_t w_voff = (uint32_t)(srow * K * 2 + 16 * schunk);
-  typedef u32x4 WStage[WLD];
-  auto load_w = [&](int kt, WStage& st) {
-#pragma unroll
-    for (int i = 0; i < WLD; i++)
-      st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0);
-  };
-  auto store_w = [&](const WStage& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < WLD; i++)
-      *reinterpret_cast<u32x4*>(wl + buf * TW * 128 + sw_off(srow + 32 * i, schunk)) = st[i];
-  };
+  const int srow = tid >> 3;
 
   // The wave's 64-row panel of the compressed operand (register order).
   struct AF {
@@ -733,9 +730,6 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
     for (int part = 0; part < 5; part++) load_frag_part(kt, f, part);
   };
-  auto load_w_part = [&](int kt, WStage& st, int i) {
-    st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0);
-  };
   auto read_b = [&](int buf, int nb) {
     const uint8_t* base = wl + buf * TW * 128;
     const int n = nb * 16 + r16;
@@ -756,12 +750,22 @@ void half_kernel(const GemmArgs a) {
     return k >= KT ? k - KT : k;
   };
   u32x8 bp0, bp1;
-  // Step kt on LDS buffer kt % 3: column blocks 0-4 load one part each of A for step
-  // kt + 1, each of the last WLD blocks writes one chunk of W stage kt + 2 to buffer
-  // (kt + 2) % 3 and loads one chunk of stage kt + 3, and the next step's first B
-  // fragments are read before the barrier.
-  auto step = [&](int kt, int buf, WStage& wst, WStage& wfree, const AF& cur, AF& anext) {
-    const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
+  // Direct-to-LDS W staging (DTL): the i-th 16-byte load of lane l in wave w lands at
+  // byte (4 i + w) * 1024 + 16 l of its stage, row n = 32 i + 8 w + l / 8 at swizzled
+  // position l % 8, which sw_off assigns to logical chunk (l % 8) ^ (n % 8).
+  const uint32_t d_voff = (uint32_t)(srow * K * 2 + 16 * ((lane & 7) ^ (srow & 7)));
+  auto dtl_w = [&](int kt, int buf, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wres, (__attribute__((address_space(3))) void*)(wl + buf * TW * 128 + (4 * i + wave) * 1024), 16, d_voff,
+        (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
+  };
+  // DTL step kt on ring buffer kt % 4: blocks 0-4 load one part each of A for step
+  // kt + 1, each of the last WLD blocks loads one chunk of W stage kt + 3 into buffer
+  // (kt + 3) % 4 (last read in step kt - 1); before the barrier each wave waits for its
+  // loads of stage kt + 2, so the next step's first B fragments, read before the barrier,
+  // find their buffer complete.
+  auto step_dtl = [&](int kt, int buf, const AF& cur, AF& anext) {
+    const int nbuf = buf == WBUF - 1 ? 0 : buf + 1, dbuf = buf == 0 ? WBUF - 1 : buf - 1;
     u32x8 bq[3];
     bq[0] = bp0;
     bq[1] = bp1;
@@ -769,11 +773,7 @@ void half_kernel(const GemmArgs a) {
     for (int nb = 0; nb < NB; nb++) {
       if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(buf, nb + 2);
       if (nb < 5) load_frag_part(kp(kt + 1), anext, nb);
-      if (nb >= NB - WLD) {
-        const int i = nb - (NB - WLD);
-        *reinterpret_cast<u32x4*>(wl + sbuf * TW * 128 + sw_off(srow + 32 * i, schunk)) = wst[i];
-        load_w_part(kp(kt + 3), wfree, i);
-      }
+      if (nb >= NB - WLD) dtl_w(kp(kt + 3), dbuf, nb - (NB - WLD));
       const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0]), bv, acc[0][nb],
                                                              (int)cur.iw[0], 0, 0);
@@ -787,47 +787,40 @@ void half_kernel(const GemmArgs a) {
     }
     bp0 = read_b(nbuf, 0);
     bp1 = read_b(nbuf, 1);
-    __syncthreads();
+    wait_vmcnt<5 + WLD>();
+    barrier_nofence();
   };
 
-  WStage w0, w1;
   AF f0, f1;
+  // A of step 0, then W stages 0-2 (A before W, as in the loop); stages 0 and 1
+  // complete before the first B reads.
   load_frag(kp(0), f0);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(kp(0), w0);
-  load_w(kp(1), w1);
-  __builtin_amdgcn_sched_barrier(0);
-  store_w(w0, 0);
-  store_w(w1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_w(kp(2), w0);
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < 3; st++)
+#pragma unroll
+    for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+  wait_vmcnt<WLD>();
+  barrier_nofence();
   bp0 = read_b(0, 0);
   bp1 = read_b(0, 1);
-  // Whole periods of 6 steps in the loop (no exit in its body), then the rest.
+  // Ring buffers cycle with period 4, A sets with period 2: whole periods of 4 steps
+  // in the loop (no exit in its body), then the rest.
   int kt = 0;
-  for (; kt + 6 <= KT; kt += 6) {
-    step(kt, 0, w0, w1, f0, f1);
-    step(kt + 1, 1, w1, w0, f1, f0);
-    step(kt + 2, 2, w0, w1, f0, f1);
-    step(kt + 3, 0, w1, w0, f1, f0);
-    step(kt + 4, 1, w0, w1, f0, f1);
-    step(kt + 5, 2, w1, w0, f1, f0);
+  for (; kt + 4 <= KT; kt += 4) {
+    step_dtl(kt, 0, f0, f1);
+    step_dtl(kt + 1, 1, f1, f0);
+    step_dtl(kt + 2, 2, f0, f1);
+    step_dtl(kt + 3, 3, f1, f0);
   }
   if (kt < KT) {
-    step(kt, 0, w0, w1, f0, f1);
+    step_dtl(kt, 0, f0, f1);
     if (kt + 1 < KT) {
-      step(kt + 1, 1, w1, w0, f1, f0);
-      if (kt + 2 < KT) {
-        step(kt + 2, 2, w0, w1, f0, f1);
-        if (kt + 3 < KT) {
-          step(kt + 3, 0, w1, w0, f1, f0);
-          if (kt + 4 < KT) step(kt + 4, 1, w0, w1, f0, f1);
-        }
-      }
+      step_dtl(kt + 1, 1, f1, f0);
+      if (kt + 2 < KT) step_dtl(kt + 2, 2, f0, f1);
     }
   }
+  wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
 
   // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
   // accumulator rows 16rb + 4q + j (lane 4q + j); the rank-R slice acc += (T / s) L_A^T,
