@@ -45,13 +45,20 @@ void gemm_kernel(const GemmArgs a) {
   // Pre-compressed 192-wide tiles load W straight into a 4-buffer LDS ring (DTLW).
   constexpr bool DTLW = MODE == kModeComp && TN == 192;
   constexpr int WBUF = DTLW ? 4 : (MODE == kModeComp ? 3 : 2);
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TN * 128];
+  // DTLW with R <= 64 also keeps the tile's rank-R operands in LDS, past the ring (see
+  // lora below).  One array for every direct-to-LDS load: loads into a second LDS array
+  // make the compiler wait for all of them before each LDS read.
+  constexpr int kLoraT = 256 * 64 * 2, kLoraA = TN * 64 * 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TN * 128 + (DTLW ? kLoraT + kLoraA + 1024 : 0)];
   // Pre-compressed operand through LDS on 256-wide tiles (there the smaller VMEM traffic
   // wins); straight to registers on 192-wide tiles (there the smaller LDS traffic wins).
   constexpr bool CALDS = MODE == kModeComp && TN == 256;
   __shared__ __attribute__((aligned(1024))) uint8_t alc[CALDS ? 3 * kCompStage : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
   __shared__ float sred[FUSED ? 256 : 1];
+  // DTLW with R <= 64: the tile's rank-R operands in LDS, copies of their rows in memory:
+  // T [256][R] bf16, L_A [TN][R] bf16, then s [256] f32.
+  uint8_t* const lora = wl + WBUF * TN * 128;
 
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
@@ -323,6 +330,62 @@ void gemm_kernel(const GemmArgs a) {
         wres, (__attribute__((address_space(3))) void*)(wl + buf * TN * 128 + (8 * i + wave) * 1024), 16, d_voff,
         (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
   };
+  // DTLW with R <= 64 takes the rank-R branch first, from LDS: acc = (T / s)_tile
+  // L_A_tile^T (K = R in slices of 32) before the main loop accumulates X~ W^T on top, and
+  // the epilogue stores Y = s * acc.  T, L_A and s go straight into LDS ahead of the first
+  // operand loads, and the branch's MFMAs run while those are in flight.  A zero row has
+  // s = 0 and T = 0; its T / s is taken as 0.
+  const bool lfirst = DTLW && a.R <= 64;
+  auto lora_stage = [&]() {
+    const int64_t R = a.R, Mp = (int64_t)a.n_panels * kPanel;
+    uint8_t* ls = lora + kLoraT + kLoraA;
+    const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.s + m0, (Mp - m0) * 4);
+    if (lane < 8)  // 128 bytes of s per wave
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(ls + wave * 128), 16,
+                                               (uint32_t)(wave * 128 + lane * 16), 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
+    const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (N - n0) * R * 2);
+    for (int j = wave; j < (int)(R / 2); j += 8)  // 1 KB blocks of the 256 x R tile of T
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(lora + j * 1024), 16,
+                                               (uint32_t)(j * 1024 + lane * 16), 0, 0, 0);
+    for (int j = wave; j < (int)(TN * R / 512); j += 8)  // 1 KB blocks of the TN x R tile of L_A
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(lora + kLoraT + j * 1024),
+                                               16, (uint32_t)(j * 1024 + lane * 16), 0, 0, 0);
+  };
+  // s of tile row r from LDS (a 16-byte read: narrower LDS reads would make the compiler
+  // wait for every load into LDS).
+  auto lds_s = [&](int r) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(lora + kLoraT + kLoraA + (r & ~3) * 4);
+    const uint32_t e = (r & 2) ? ((r & 1) ? w[3] : w[2]) : ((r & 1) ? w[1] : w[0]);
+    return __uint_as_float(e);
+  };
+  auto lora_first = [&]() {
+    const int R = (int)a.R;
+    float inv_s[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+      const float sv = lds_s(64 * wm + 16 * rb + r16);
+      inv_s[rb] = sv > 0.f ? 1.f / sv : 0.f;
+    }
+    for (int kk = 0; kk < R / 32; kk++) {
+      u32x4 ta[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(lora + (64 * wm + 16 * rb + r16) * R * 2 + 64 * kk + 16 * q);
+#pragma unroll
+        for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        const u32x4 la = *reinterpret_cast<const u32x4*>(lora + kLoraT + ((TN / 2) * wn + nb * 16 + r16) * R * 2 +
+                                                         64 * kk + 16 * q);
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++)
+          acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
+                                                                __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
+      }
+    }
+  };
   // DTLW step kt on ring buffer kt % 4: blocks 0-2 load the A fragments of step kt + 1
   // into registers; each of the last WLD blocks loads one chunk of W stage kt + 3 into
   // buffer (kt + 3) % 4 (last read in step kt - 1).  Before the barrier each wave waits
@@ -556,12 +619,19 @@ void gemm_kernel(const GemmArgs a) {
     // The A fragments of step 0, then W stages 0-2 into buffers 0-2 (A before W, as in
     // the loop, so the wait counts at the loop head match the steady state); stages 0
     // and 1 complete before the first B reads.
+    if (lfirst) lora_stage();
+    __builtin_amdgcn_sched_barrier(0);
     load_frag(kp(0), f0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 3; st++)
 #pragma unroll
       for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+    if (lfirst) {
+      wait_vmcnt<5 + 3 * WLD>();  // the rank-R operands (issued before the 14 loads since)
+      barrier_nofence();
+      lora_first();
+    }
     wait_vmcnt<WLD>();
     barrier_nofence();
     bp0 = read_bc(0, 0);
@@ -623,6 +693,9 @@ void gemm_kernel(const GemmArgs a) {
       __syncthreads();
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) s_row[rb] = sred[64 * wm + 16 * rb + r16];
+    } else if (lfirst) {
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) s_row[rb] = lds_s(64 * wm + 16 * rb + r16);
     } else {
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
@@ -643,7 +716,7 @@ void gemm_kernel(const GemmArgs a) {
     float inv_s[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
-    for (int kk = 0; kk < (int)(R / 32); kk++) {
+    for (int kk = 0; kk < (lfirst ? 0 : (int)(R / 32)); kk++) {
       u32x4 ta[4];
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {

@@ -218,6 +218,26 @@ def test_fused_wide_tiles_ragged(shape, variant):
     assert err <= TOL_Y["bf16"]
 
 
+# 192-wide pre-compressed tiles with every supported rank: R <= 64 stages T, L_A and s in
+# LDS and adds the rank-R slice before the main loop (R = 32 splits the L_A copy unevenly
+# over the waves); R = 0 has no rank-R branch; R > 64 adds it in the epilogue.  2000 x 6100
+# is 8 x 32 tiles of 256 x 192 (one per CU), K = 320 is 5 K steps and K = 704 eleven.
+@pytest.mark.parametrize("R", [0, 32, 96, 128])
+@pytest.mark.parametrize("K", [320, 704])
+def test_fused_192_tiles_every_rank(K, R):
+    M, N = 2000, 6100
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=9190 + K + R)
+    log(f"[fused-192] M={M} N={N} K={K} R={R}")
+    Y, dbg_idx, dbg_s = run_fused(d, variant=rtl.RTL_VARIANT_PRECOMPRESSED)
+    rows = np.unique(np.concatenate([sample_rows(M, n=64), np.arange(M - 160, M, 7)]))
+    Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+    y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
+    err = row_rel_err(y, Yref)
+    log(f"  sampled {len(rows)} rows, max row rel err {err:.3e}")
+    assert err <= TOL_Y["bf16"]
+
+
 # Irregular shapes drawn from a fixed seed (so the cases are the same on every run): M and N
 # with ragged tails, every supported R, K up to 20 steps of 64 (whole and partial turns of
 # the GEMM's register ring), both variants.  Shapes stay small enough for the full oracle.
