@@ -18,47 +18,101 @@ namespace rtl {
 
 constexpr int kModeDense = 0, kModeFused = 1, kModeComp = 2;
 
-// GEMM workgroup: 8 waves (two per SIMD) on a 256 x TN output tile (TN = 192 or 256); wave w
-// owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  On 192-wide pre-compressed tiles
-// W goes straight from memory into a 4-buffer LDS ring (three steps ahead) and each wave
-// loads its compressed rows straight into registers a step ahead.  Elsewhere W (and, on
-// 256-wide pre-compressed tiles, the compressed operand) goes memory -> registers -> LDS:
-// a 3-buffer ring in the pre-compressed mode (loaded a step before it is written, written
-// two steps before it is used), a 2-buffer ring in the dense and fused modes.  Fused mode:
-// of each row slab, the two waves that share it select two 16-row blocks each and trade
-// the compressed operand through LDS.
+// GEMM workgroup: 8 waves (two per SIMD) on a 256 x TN output tile (TN = 192 or 256; the
+// pre-compressed mode only at 256, 192-wide pre-compressed tiles run in half_kernel); wave
+// w owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  W (and, in the pre-compressed
+// mode, the compressed operand) goes memory -> registers -> LDS: a 3-buffer ring in the
+// pre-compressed mode (loaded a step before it is written, written two steps before it
+// is used), a 2-buffer ring in the dense and fused modes.  Fused mode: of each row slab,
+// the two waves that share it select two 16-row blocks each and trade the compressed
+// operand through LDS.
 constexpr int kGemmThreads = 512;
 constexpr int kXBlk = 64 * 16 + 64 * 2;   // fused: one row block of the compressed operand
 constexpr int kALds = kBM * 128;          // A tile bytes per LDS buffer (dense layout, the largest)
 constexpr int kCompIdx = 16384;           // pre-compressed: offset of the position words in an A buffer
 constexpr int kCompStage = 16384 + 2048;  // pre-compressed: one K step of the tile's four panels
 
+// Rank-R operands of one output tile staged in LDS (R <= 64), as copies of their rows in
+// memory: T [256][R] bf16 at +0, L_A [TW][R] bf16 at +kLoraT, s [256] f32 at +kLoraT +
+// kLoraA.  Loaded with 16-byte direct-to-LDS loads, 1 KB blocks dealt round-robin to the
+// NW waves (s: 1024 / NW bytes per wave); the caller waits for them (vmcnt) and then
+// synchronises the workgroup.
+constexpr int kLoraT = 256 * 64 * 2;
+template <int TW, int NW>
+__device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a, int64_t m0, int64_t n0, int wave,
+                                               int lane) {
+  constexpr int kLoraA = TW * 64 * 2, SPW = 1024 / NW;
+  const int64_t R = a.R, Mp = (int64_t)a.n_panels * kPanel;
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.s + m0, (Mp - m0) * 4);
+  if (16 * lane < SPW)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(lora + kLoraT + kLoraA + wave * SPW),
+                                             16, (uint32_t)(wave * SPW + lane * 16), 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
+  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (a.N - n0) * R * 2);
+  for (int j = wave; j < (int)(R / 2); j += NW)  // 1 KB blocks of the 256 x R tile of T
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(lora + j * 1024), 16,
+                                             (uint32_t)(j * 1024 + lane * 16), 0, 0, 0);
+  for (int j = wave; j < (int)(TW * R / 512); j += NW)  // 1 KB blocks of the TW x R tile of L_A
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(lora + kLoraT + j * 1024),
+                                             16, (uint32_t)(j * 1024 + lane * 16), 0, 0, 0);
+}
+// s of tile row r from the staged copy (a 16-byte read: narrower LDS reads would make the
+// compiler wait for every load into LDS).
+template <int TW>
+__device__ __forceinline__ float lora_s_lds(const uint8_t* lora, int r) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(lora + kLoraT + TW * 128 + (r & ~3) * 4);
+  const uint32_t e = (r & 2) ? ((r & 1) ? w[3] : w[2]) : ((r & 1) ? w[1] : w[0]);
+  return __uint_as_float(e);
+}
+// acc[rb][nb] += (T / s)_rows L_A_cols^T from the staged copy, K = R in slices of 32: the
+// lane feeds tile row row0 + 16 rb + r16 and tile column col0 + 16 nb + r16.  A zero row
+// has s = 0 and T = 0; its T / s is taken as 0.
+template <int TW, int NB>
+__device__ __forceinline__ void lora_first_lds(f32x4 (&acc)[4][NB], const uint8_t* lora, int R, int row0, int col0,
+                                               int lane) {
+  const int q = lane >> 4, r16 = lane & 15;
+  float inv_s[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+    const float sv = lora_s_lds<TW>(lora, row0 + 16 * rb + r16);
+    inv_s[rb] = sv > 0.f ? 1.f / sv : 0.f;
+  }
+  for (int kk = 0; kk < R / 32; kk++) {
+    u32x4 ta[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(lora + (row0 + 16 * rb + r16) * R * 2 + 64 * kk + 16 * q);
+#pragma unroll
+      for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const u32x4 la = *reinterpret_cast<const u32x4*>(lora + kLoraT + (col0 + nb * 16 + r16) * R * 2 + 64 * kk + 16 * q);
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++)
+        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
+                                                              __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
+    }
+  }
+}
+
 template <int MODE, bool DBG, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const GemmArgs a) {
   static_assert(TN == 256 || TN == 192, "tile widths");
+  static_assert(MODE != kModeComp || TN == 256, "192-wide pre-compressed tiles run in half_kernel<192>");
   constexpr int NB = TN / 32;                     // 16-column blocks per wave (each wave: TN/2 columns)
   constexpr int WLD = TN * 8 / kGemmThreads;      // 16-byte W chunks per thread per K step
   constexpr bool SPARSE = MODE != kModeDense;
   constexpr bool FUSED = MODE == kModeFused;
   constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
-  // Pre-compressed 192-wide tiles load W straight into a 4-buffer LDS ring (DTLW).
-  constexpr bool DTLW = MODE == kModeComp && TN == 192;
-  constexpr int WBUF = DTLW ? 4 : (MODE == kModeComp ? 3 : 2);
-  // DTLW with R <= 64 also keeps the tile's rank-R operands in LDS, past the ring (see
-  // lora below).  One array for every direct-to-LDS load: loads into a second LDS array
-  // make the compiler wait for all of them before each LDS read.
-  constexpr int kLoraT = 256 * 64 * 2, kLoraA = TN * 64 * 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TN * 128 + (DTLW ? kLoraT + kLoraA + 1024 : 0)];
-  // Pre-compressed operand through LDS on 256-wide tiles (there the smaller VMEM traffic
-  // wins); straight to registers on 192-wide tiles (there the smaller LDS traffic wins).
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[(MODE == kModeComp ? 3 : 2) * TN * 128];
+  // Pre-compressed mode (256-wide tiles): the compressed operand goes through LDS too, so
+  // the two waves that share a row slab load it once.
   constexpr bool CALDS = MODE == kModeComp && TN == 256;
   __shared__ __attribute__((aligned(1024))) uint8_t alc[CALDS ? 3 * kCompStage : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
   __shared__ float sred[FUSED ? 256 : 1];
-  // DTLW with R <= 64: the tile's rank-R operands in LDS, copies of their rows in memory:
-  // T [256][R] bf16, L_A [TN][R] bf16, then s [256] f32.
-  uint8_t* const lora = wl + WBUF * TN * 128;
 
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
@@ -269,40 +323,12 @@ void gemm_kernel(const GemmArgs a) {
     __syncthreads();
   };
 
-  // Pre-compressed mode on 192-wide tiles: the operand is stored in MFMA register order,
-  // so each wave loads its own 64 rows straight into registers (one 16-byte load per lane
-  // and row block, one 8-byte load of position words), one K step ahead; only W goes
-  // through LDS (DTLW, step_dtl below).
-  // The wave's panel through buffer resources (wave-uniform base, scalar step offsets).
-  const __amdgpu_buffer_rsrc_t cvres =
-      make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 4096);
-  const __amdgpu_buffer_rsrc_t cires =
-      make_rsrc(MODE == kModeComp ? a.cidx + cidx_off(cpanel(wm), KT, 0) : nullptr, (int64_t)KT * 512);
-  // Part p < 4: kept values of row block p; part 4: the position words.
-  auto load_frag_part = [&](int kt, AFrag& f, int part) {
-    if (part < 4) {
-      f.v[part][0] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + part * 1024), kt * 4096, 0);
-    } else {
-      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
-      f.iw[0] = w[0];
-      f.iw[1] = w[1];
-    }
-  };
-  auto load_frag = [&](int kt, AFrag& f) {
-#pragma unroll
-    for (int part = 0; part < 5; part++) load_frag_part(kt, f, part);
-  };
   auto load_w_part = [&](int kt, WStage& st, int i) {
     st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
   };
-  // Pre-compressed step kt on a 3-buffer LDS ring for W (buffer kt % 3), with the memory
-  // operations spread over the MFMA loop, at most two loads per column block (a burst of
-  // loads holds up the wave's next MFMAs): blocks 0-2 issue the A loads for step kt + 1,
-  // and each of the last WLD blocks writes one chunk of W stage kt + 2 (loaded a step
-  // ago) to buffer (kt + 2) % 3 and loads one chunk of stage kt + 3.  The first two B
-  // fragments of the step arrive in bp0, bp1, read at the end of the previous step: with
-  // three buffers, that buffer is complete before the barrier, so no LDS latency is
-  // exposed at the step boundary.
+  // The first two B fragments of a pre-compressed step arrive in bp0, bp1, read at the end
+  // of the previous step: with three buffers, that buffer is complete before the barrier,
+  // so no LDS latency is exposed at the step boundary.
   u32x8 bp0, bp1;
   // K order: tile (tm, tn) starts at K step (tm + tn) % 8 and wraps around, so the
   // workgroups of an XCD that share a W column block (same tn) or a compressed row panel
@@ -320,108 +346,6 @@ void gemm_kernel(const GemmArgs a) {
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
     return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  // Direct-to-LDS W staging (DTLW): the i-th 16-byte load of lane l in wave w lands at byte
-  // (8 i + w) * 1024 + 16 l of its LDS stage (the hardware writes lane l at 16 l past the
-  // wave's LDS base), i.e. row n = 64 i + 8 w + l / 8 at swizzled position l % 8, which
-  // sw_off assigns to logical chunk (l % 8) ^ (n % 8): each lane loads that chunk.
-  const uint32_t d_voff = (uint32_t)(srow * K * 2 + 16 * ((lane & 7) ^ (srow & 7)));
-  auto dtl_w = [&](int kt, int buf, int i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        wres, (__attribute__((address_space(3))) void*)(wl + buf * TN * 128 + (8 * i + wave) * 1024), 16, d_voff,
-        (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
-  };
-  // DTLW with R <= 64 takes the rank-R branch first, from LDS: acc = (T / s)_tile
-  // L_A_tile^T (K = R in slices of 32) before the main loop accumulates X~ W^T on top, and
-  // the epilogue stores Y = s * acc.  T, L_A and s go straight into LDS ahead of the first
-  // operand loads, and the branch's MFMAs run while those are in flight.  A zero row has
-  // s = 0 and T = 0; its T / s is taken as 0.
-  const bool lfirst = DTLW && a.R <= 64;
-  auto lora_stage = [&]() {
-    const int64_t R = a.R, Mp = (int64_t)a.n_panels * kPanel;
-    uint8_t* ls = lora + kLoraT + kLoraA;
-    const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.s + m0, (Mp - m0) * 4);
-    if (lane < 8)  // 128 bytes of s per wave
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(ls + wave * 128), 16,
-                                               (uint32_t)(wave * 128 + lane * 16), 0, 0, 0);
-    const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
-    const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (N - n0) * R * 2);
-    for (int j = wave; j < (int)(R / 2); j += 8)  // 1 KB blocks of the 256 x R tile of T
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(lora + j * 1024), 16,
-                                               (uint32_t)(j * 1024 + lane * 16), 0, 0, 0);
-    for (int j = wave; j < (int)(TN * R / 512); j += 8)  // 1 KB blocks of the TN x R tile of L_A
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(lora + kLoraT + j * 1024),
-                                               16, (uint32_t)(j * 1024 + lane * 16), 0, 0, 0);
-  };
-  // s of tile row r from LDS (a 16-byte read: narrower LDS reads would make the compiler
-  // wait for every load into LDS).
-  auto lds_s = [&](int r) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(lora + kLoraT + kLoraA + (r & ~3) * 4);
-    const uint32_t e = (r & 2) ? ((r & 1) ? w[3] : w[2]) : ((r & 1) ? w[1] : w[0]);
-    return __uint_as_float(e);
-  };
-  auto lora_first = [&]() {
-    const int R = (int)a.R;
-    float inv_s[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-      const float sv = lds_s(64 * wm + 16 * rb + r16);
-      inv_s[rb] = sv > 0.f ? 1.f / sv : 0.f;
-    }
-    for (int kk = 0; kk < R / 32; kk++) {
-      u32x4 ta[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(lora + (64 * wm + 16 * rb + r16) * R * 2 + 64 * kk + 16 * q);
-#pragma unroll
-        for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        const u32x4 la = *reinterpret_cast<const u32x4*>(lora + kLoraT + ((TN / 2) * wn + nb * 16 + r16) * R * 2 +
-                                                         64 * kk + 16 * q);
-#pragma unroll
-        for (int rb = 0; rb < 4; rb++)
-          acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
-                                                                __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
-      }
-    }
-  };
-  // DTLW step kt on ring buffer kt % 4: blocks 0-2 load the A fragments of step kt + 1
-  // into registers; each of the last WLD blocks loads one chunk of W stage kt + 3 into
-  // buffer (kt + 3) % 4 (last read in step kt - 1).  Before the barrier each wave waits
-  // for its loads of stage kt + 2 (issued a step ago; 8 loads were issued after them), so
-  // the first B fragments of step kt + 1, read before the barrier, find their buffer
-  // complete.
-  auto step_dtl = [&](int kt, int buf, const AFrag& cur, AFrag& anext) {
-    const int nbuf = buf == WBUF - 1 ? 0 : buf + 1, dbuf = buf == 0 ? WBUF - 1 : buf - 1;
-    u32x8 bq[3];
-    bq[0] = bp0;
-    bq[1] = bp1;
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
-      if (nb < 3) {
-        load_frag_part(kp(kt + 1), anext, 2 * nb);
-        if (nb < 2) load_frag_part(kp(kt + 1), anext, 2 * nb + 1);
-      }
-      if (nb >= NB - WLD) dtl_w(kp(kt + 3), dbuf, nb - (NB - WLD));
-      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
-      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
-                                                             (int)cur.iw[0], 0, 0);
-      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1][0]), bv, acc[1][nb],
-                                                             (int)cur.iw[0], 0, 1);
-      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2][0]), bv, acc[2][nb],
-                                                             (int)cur.iw[1], 0, 0);
-      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3][0]), bv, acc[3][nb],
-                                                             (int)cur.iw[1], 0, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bp0 = read_bc(nbuf, 0);
-    bp1 = read_bc(nbuf, 1);
-    wait_vmcnt<WLD + 5>();
-    barrier_nofence();
-  };
-
   // Compressed operand through LDS: thread t moves value chunks t and t + 512 (panels
   // t / 256 and t / 256 + 2) and position word t (panel t / 128) of a K step; one LDS
   // stage holds the tile's four panels (values, then position words).
@@ -461,11 +385,13 @@ void gemm_kernel(const GemmArgs a) {
     f.iw[0] = w.x;
     f.iw[1] = w.y;
   };
-  // As step_c below, with the compressed operand staged through LDS like W: blocks 0-2
-  // load one part each of A stage kt + 3, block NB - WLD - 1 writes A stage kt + 2 to
-  // buffer (kt + 2) % 3, each of the last WLD blocks writes one chunk of W stage kt + 2
-  // and loads one of stage kt + 3, and the next step's A fragments and first B
-  // fragments are read from buffer (kt + 1) % 3 before the barrier.
+  // Pre-compressed step kt on the 3-buffer LDS rings (buffer kt % 3), the memory
+  // operations spread over the MFMA loop with at most two loads per column block (a burst
+  // of loads holds up the wave's next MFMAs): blocks 0-2 load one part each of A stage
+  // kt + 3, block NB - WLD - 1 writes A stage kt + 2 (loaded a step ago) to buffer
+  // (kt + 2) % 3, each of the last WLD blocks writes one chunk of W stage kt + 2 and loads
+  // one of stage kt + 3, and the next step's A fragments and first B fragments are read
+  // from buffer (kt + 1) % 3 before the barrier.
   auto step_ca = [&](int kt, int buf, WStage& wst, WStage& wfree, AStg& ast, AStg& afree, const AFrag& cur,
                      AFrag& nxt) {
     const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
@@ -614,45 +540,6 @@ void gemm_kernel(const GemmArgs a) {
         }
       }
     }
-  } else if constexpr (DTLW) {
-    AFrag f0, f1;
-    // The A fragments of step 0, then W stages 0-2 into buffers 0-2 (A before W, as in
-    // the loop, so the wait counts at the loop head match the steady state); stages 0
-    // and 1 complete before the first B reads.
-    if (lfirst) lora_stage();
-    __builtin_amdgcn_sched_barrier(0);
-    load_frag(kp(0), f0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int st = 0; st < 3; st++)
-#pragma unroll
-      for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
-    if (lfirst) {
-      wait_vmcnt<5 + 3 * WLD>();  // the rank-R operands (issued before the 14 loads since)
-      barrier_nofence();
-      lora_first();
-    }
-    wait_vmcnt<WLD>();
-    barrier_nofence();
-    bp0 = read_bc(0, 0);
-    bp1 = read_bc(0, 1);
-    // Ring buffers cycle with period 4, A fragment sets with period 2: whole periods of 4
-    // steps in the loop (no exit in its body), then the rest.
-    int kt = 0;
-    for (; kt + 4 <= KT; kt += 4) {
-      step_dtl(kt, 0, f0, f1);
-      step_dtl(kt + 1, 1, f1, f0);
-      step_dtl(kt + 2, 2, f0, f1);
-      step_dtl(kt + 3, 3, f1, f0);
-    }
-    if (kt < KT) {
-      step_dtl(kt, 0, f0, f1);
-      if (kt + 1 < KT) {
-        step_dtl(kt + 1, 1, f1, f0);
-        if (kt + 2 < KT) step_dtl(kt + 2, 2, f0, f1);
-      }
-    }
-    wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
   } else {
   AStage a0, a1;
   load_w(0, w0);
@@ -693,9 +580,6 @@ void gemm_kernel(const GemmArgs a) {
       __syncthreads();
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) s_row[rb] = sred[64 * wm + 16 * rb + r16];
-    } else if (lfirst) {
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++) s_row[rb] = lds_s(64 * wm + 16 * rb + r16);
     } else {
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
@@ -716,7 +600,7 @@ void gemm_kernel(const GemmArgs a) {
     float inv_s[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
-    for (int kk = 0; kk < (lfirst ? 0 : (int)(R / 32)); kk++) {
+    for (int kk = 0; kk < (int)(R / 32); kk++) {
       u32x4 ta[4];
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
@@ -750,23 +634,30 @@ void gemm_kernel(const GemmArgs a) {
                     [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
 }
 
-// Pre-compressed GEMM with two workgroups per CU: 4 waves (one per SIMD) on a 256 x TW
-// output tile, wave w owns rows 64w..64w+63 and all TW columns.  The two workgroups on a
-// CU reach their barriers at different times, so one's matrix-core work covers the
-// other's step boundary.  Per step each wave loads its own compressed rows straight into
-// registers (no sharing, no duplication) and the workgroup loads a TW x 64 W tile
-// straight into a 4-buffer LDS ring (no register staging), with the same interleaving
-// and K stagger as gemm_kernel.
+// Pre-compressed GEMM with 4 waves (one per SIMD) on a 256 x TW output tile, wave w owns
+// rows 64w..64w+63 and all TW columns.  TW = 96 or 128: two workgroups per CU, which reach
+// their barriers at different times, so one's matrix-core work covers the other's step
+// boundary.  TW = 192: one workgroup per CU (192 accumulators per lane); against the
+// 8-wave layout it moves 30% fewer bytes through the vector-memory path per K step (no
+// compressed row is loaded twice).  Per step each wave loads its own compressed rows
+// straight into registers (no sharing, no duplication) and the workgroup loads a TW x 64
+// W tile straight into a 4-buffer LDS ring (no register staging), with the same
+// interleaving and K stagger as gemm_kernel.
 constexpr int kHalfThreads = 256;
 
 template <int TW>
-__global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads),
+                          amdgpu_waves_per_eu(TW == 192 ? 1 : 2, TW == 192 ? 1 : 2)))
 void half_kernel(const GemmArgs a) {
-  static_assert(TW == 128 || TW == 96, "tile widths");
+  static_assert(TW == 128 || TW == 96 || TW == 192, "tile widths");
   constexpr int NB = TW / 16;                   // 16-column blocks per wave
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TW * 128];
+  // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
+  // take the rank-R branch first from operands staged in LDS past the ring.
+  constexpr bool ONE = TW == 192;
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TW * 128 + (ONE ? kLoraT + TW * 128 + 1024 : 0)];
+  uint8_t* const lora = wl + WBUF * TW * 128;
 
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
@@ -865,14 +756,22 @@ void half_kernel(const GemmArgs a) {
   };
 
   AF f0, f1;
-  // A of step 0, then W stages 0-2 (A before W, as in the loop); stages 0 and 1
-  // complete before the first B reads.
+  // (192-wide, R <= 64: the rank-R operands into LDS, then) A of step 0, then W stages 0-2
+  // (A before W, as in the loop); stages 0 and 1 complete before the first B reads.
+  const bool lfirst = ONE && a.R <= 64;
+  if (lfirst) lora_stage_lds<TW, 4>(lora, a, m0, n0, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
   load_frag(kp(0), f0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < 3; st++)
 #pragma unroll
     for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+  if (lfirst) {
+    wait_vmcnt<5 + 3 * WLD>();  // the rank-R operands (issued before the loads since)
+    barrier_nofence();
+    lora_first_lds<TW, NB>(acc, lora, (int)a.R, 64 * wave, 0, lane);
+  }
   wait_vmcnt<WLD>();
   barrier_nofence();
   bp0 = read_b(0, 0);
@@ -896,17 +795,18 @@ void half_kernel(const GemmArgs a) {
   wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
 
   // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
-  // accumulator rows 16rb + 4q + j (lane 4q + j); the rank-R slice acc += (T / s) L_A^T,
-  // then Y = s * acc (a zero row has s = 0 and T = 0; its T / s is taken as 0).
+  // accumulator rows 16rb + 4q + j (lane 4q + j); unless taken first, the rank-R slice
+  // acc += (T / s) L_A^T; then Y = s * acc (a zero row has s = 0 and T = 0; its T / s is
+  // taken as 0).
   float s_row[4], inv_s[4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
     const int64_t row = m0 + 64 * wave + 16 * rb + r16;
-    s_row[rb] = a.s[row < M ? row : M - 1];
+    s_row[rb] = lfirst ? lora_s_lds<TW>(lora, 64 * wave + 16 * rb + r16) : a.s[row < M ? row : M - 1];
     inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
   }
   const int64_t R = a.R;
-  for (int kk = 0; kk < (int)(R / 32); kk++) {
+  for (int kk = 0; kk < (lfirst ? 0 : (int)(R / 32)); kk++) {
     u32x4 ta[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
@@ -948,9 +848,9 @@ static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void
 }
 
 // Pre-compressed GEMM: two 256 x 128 workgroups per CU instead of one 256 x TN one, when
-// that gives the busiest CU less work.  Per output column the half-width kernel is a
-// little cheaper for short K (its two workgroups per CU hide each other's tile prologue
-// and epilogue) and dearer for long K (it moves more operand bytes per K step than the
+// that gives the busiest CU less work.  Per output column the 128-wide kernel is a little
+// cheaper for short K (its two workgroups per CU hide each other's tile prologue and
+// epilogue) and dearer for long K (it moves more operand bytes per K step than the
 // 256-wide kernel, which shares the compressed rows through LDS).
 static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
   const int64_t tm = (M + kBM - 1) / kBM;
@@ -964,9 +864,13 @@ static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
 template <int TN>
 static void launch_main_tn(bool comp, GemmArgs g, uint8_t* dbg_idx, hipStream_t stream) {
   const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(kGemmThreads);
-  if (comp) {
-    hipLaunchKernelGGL((gemm_kernel<kModeComp, false, TN>), grid, block, 0, stream, g);
-  } else if (dbg_idx != nullptr) {
+  if constexpr (TN == 256) {
+    if (comp) {
+      hipLaunchKernelGGL((gemm_kernel<kModeComp, false, TN>), grid, block, 0, stream, g);
+      return;
+    }
+  }
+  if (dbg_idx != nullptr) {
     hipLaunchKernelGGL((gemm_kernel<kModeFused, true, TN>), grid, block, 0, stream, g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<kModeFused, false, TN>), grid, block, 0, stream, g);
@@ -995,6 +899,10 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     GemmArgs h = g;
     h.tiles_n = (int)((N + 127) / 128);
     hipLaunchKernelGGL((half_kernel<128>), dim3((unsigned)(h.tiles_m * h.tiles_n)), dim3(kHalfThreads), 0, stream, h);
+    return hipGetLastError();
+  }
+  if (comp && tn == 192) {
+    hipLaunchKernelGGL((half_kernel<192>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream, g);
     return hipGetLastError();
   }
   if (tn == 192) launch_main_tn<192>(comp, g, dbg_idx, stream);
