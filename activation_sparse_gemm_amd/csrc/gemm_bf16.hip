@@ -637,9 +637,10 @@ void gemm_kernel(const GemmArgs a) {
 // Pre-compressed GEMM with 4 waves (one per SIMD) on a 256 x TW output tile, wave w owns
 // rows 64w..64w+63 and all TW columns.  TW = 96 or 128: two workgroups per CU, which reach
 // their barriers at different times, so one's matrix-core work covers the other's step
-// boundary.  TW = 192: one workgroup per CU (192 accumulators per lane); against the
-// 8-wave layout it moves 30% fewer bytes through the vector-memory path per K step (no
-// compressed row is loaded twice).  Per step each wave loads its own compressed rows
+// boundary.  TW = 192 and 256: one workgroup per CU (TW accumulators per lane); against
+// the 8-wave layout at 192 columns it moves 30% fewer bytes through the vector-memory path
+// per K step (no compressed row is loaded twice), at 256 columns 25% fewer bytes through
+// LDS (the compressed rows skip it).  Per step each wave loads its own compressed rows
 // straight into registers (no sharing, no duplication) and the workgroup loads a TW x 64
 // W tile straight into a 4-buffer LDS ring (no register staging), with the same
 // interleaving and K stagger as gemm_kernel.
@@ -647,16 +648,16 @@ constexpr int kHalfThreads = 256;
 
 template <int TW>
 __global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads),
-                          amdgpu_waves_per_eu(TW == 192 ? 1 : 2, TW == 192 ? 1 : 2)))
+                          amdgpu_waves_per_eu(TW >= 192 ? 1 : 2, TW >= 192 ? 1 : 2)))
 void half_kernel(const GemmArgs a) {
-  static_assert(TW == 128 || TW == 96 || TW == 192, "tile widths");
+  static_assert(TW == 128 || TW == 96 || TW == 192 || TW == 256, "tile widths");
   constexpr int NB = TW / 16;                   // 16-column blocks per wave
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
   // take the rank-R branch first from operands staged in LDS past the ring.
-  constexpr bool ONE = TW == 192;
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TW * 128 + (ONE ? kLoraT + TW * 128 + 1024 : 0)];
+  constexpr bool ONE = TW >= 192, LSTG = TW == 192;
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : 0)];
   uint8_t* const lora = wl + WBUF * TW * 128;
 
   int tm, tn;
@@ -724,21 +725,25 @@ void half_kernel(const GemmArgs a) {
         (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
   };
   // DTL step kt on ring buffer kt % 4: blocks 0-4 load one part each of A for step
-  // kt + 1, each of the last WLD blocks loads one chunk of W stage kt + 3 into buffer
+  // kt + AAH, each of the last WLD blocks loads one chunk of W stage kt + 3 into buffer
   // (kt + 3) % 4 (last read in step kt - 1); before the barrier each wave waits for its
   // loads of stage kt + 2, so the next step's first B fragments, read before the barrier,
   // find their buffer complete.
+  // A fragments are loaded AAH steps ahead (two workgroups per CU: two steps, measured 2%
+  // faster; one workgroup per CU: one), B fragments read BQ column blocks ahead.
+  constexpr int AAH = ONE ? 1 : 2, BQ = 2, NSET = AAH + 1, PER = AAH == 1 ? 4 : 12;
+  u32x8 bp[BQ];
   auto step_dtl = [&](int kt, int buf, const AF& cur, AF& anext) {
     const int nbuf = buf == WBUF - 1 ? 0 : buf + 1, dbuf = buf == 0 ? WBUF - 1 : buf - 1;
-    u32x8 bq[3];
-    bq[0] = bp0;
-    bq[1] = bp1;
+    u32x8 bq[BQ + 1];
+#pragma unroll
+    for (int j = 0; j < BQ; j++) bq[j] = bp[j];
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
-      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_b(buf, nb + 2);
-      if (nb < 5) load_frag_part(kp(kt + 1), anext, nb);
+      if (nb + BQ < NB) bq[(nb + BQ) % (BQ + 1)] = read_b(buf, nb + BQ);
+      if (nb < 5) load_frag_part(kp(kt + AAH), anext, nb);
       if (nb >= NB - WLD) dtl_w(kp(kt + 3), dbuf, nb - (NB - WLD));
-      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
+      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % (BQ + 1)]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0]), bv, acc[0][nb],
                                                              (int)cur.iw[0], 0, 0);
       acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1]), bv, acc[1][nb],
@@ -749,49 +754,45 @@ void half_kernel(const GemmArgs a) {
                                                              (int)cur.iw[1], 0, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    bp0 = read_b(nbuf, 0);
-    bp1 = read_b(nbuf, 1);
+#pragma unroll
+    for (int j = 0; j < BQ; j++) bp[j] = read_b(nbuf, j);
     wait_vmcnt<5 + WLD>();
     barrier_nofence();
   };
 
-  AF f0, f1;
-  // (192-wide, R <= 64: the rank-R operands into LDS, then) A of step 0, then W stages 0-2
-  // (A before W, as in the loop); stages 0 and 1 complete before the first B reads.
-  const bool lfirst = ONE && a.R <= 64;
+  AF fa[NSET];
+  // (192-wide, R <= 64: the rank-R operands into LDS, then) A of the first steps, then W
+  // stages 0-2 (A before W, as in the loop); stages 0 and 1 complete before the first B
+  // reads.
+  const bool lfirst = LSTG && a.R <= 64;
   if (lfirst) lora_stage_lds<TW, 4>(lora, a, m0, n0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_frag(kp(0), f0);
+#pragma unroll
+  for (int j = 0; j < AAH; j++) load_frag(kp(j), fa[j]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < 3; st++)
 #pragma unroll
     for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
   if (lfirst) {
-    wait_vmcnt<5 + 3 * WLD>();  // the rank-R operands (issued before the loads since)
+    wait_vmcnt<5 * AAH + 3 * WLD>();  // the rank-R operands (issued before the loads since)
     barrier_nofence();
     lora_first_lds<TW, NB>(acc, lora, (int)a.R, 64 * wave, 0, lane);
   }
   wait_vmcnt<WLD>();
   barrier_nofence();
-  bp0 = read_b(0, 0);
-  bp1 = read_b(0, 1);
-  // Ring buffers cycle with period 4, A sets with period 2: whole periods of 4 steps
-  // in the loop (no exit in its body), then the rest.
+#pragma unroll
+  for (int j = 0; j < BQ; j++) bp[j] = read_b(0, j);
+  // Ring buffers cycle with period 4, A sets with period AAH + 1: whole periods in the
+  // loop (no exit in its body), then the rest.
   int kt = 0;
-  for (; kt + 4 <= KT; kt += 4) {
-    step_dtl(kt, 0, f0, f1);
-    step_dtl(kt + 1, 1, f1, f0);
-    step_dtl(kt + 2, 2, f0, f1);
-    step_dtl(kt + 3, 3, f1, f0);
+  for (; kt + PER <= KT; kt += PER) {
+#pragma unroll
+    for (int j = 0; j < PER; j++) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
   }
-  if (kt < KT) {
-    step_dtl(kt, 0, f0, f1);
-    if (kt + 1 < KT) {
-      step_dtl(kt + 1, 1, f1, f0);
-      if (kt + 2 < KT) step_dtl(kt + 2, 2, f0, f1);
-    }
-  }
+#pragma unroll
+  for (int j = 0; j < PER - 1; j++)
+    if (kt + j < KT) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
   wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
 
   // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
@@ -903,6 +904,14 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   }
   if (comp && tn == 192) {
     hipLaunchKernelGGL((half_kernel<192>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream, g);
+    return hipGetLastError();
+  }
+  // 256-wide pre-compressed tiles: the 4-wave kernel (less LDS traffic per K step) for
+  // long K, the 8-wave one (lower fixed cost per tile) otherwise; measured on the
+  // workload layers: K = 12288 and 13824 6-7% faster in the 4-wave kernel, K = 5120 3%
+  // slower.
+  if (comp && tn == 256 && K > 8192) {
+    hipLaunchKernelGGL((half_kernel<256>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream, g);
     return hipGetLastError();
   }
   if (tn == 192) launch_main_tn<192>(comp, g, dbg_idx, stream);

@@ -196,8 +196,11 @@ def test_fused_workload_layers(name, variant):
 #   4000 x 4000, K = 512: two 256 x 128 workgroups per CU (pre-compressed variant);
 #   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels; K = 256 and 320
 #                are 4 and 5 K steps, shorter than one turn of the ring; K = 704 is one turn
-#                and a 5-step tail).
-WIDE = [(4000, 4000, 4160), (4000, 4000, 512), (2000, 6100, 256), (2000, 6100, 320), (2000, 6100, 704)]
+#                and a 5-step tail);
+#   4000 x 4000, K = 8256: 256 x 256 tiles in the 4-wave kernel (pre-compressed variant,
+#                K > 8192; 129 K steps, 32 whole turns of its 4-step ring and one step).
+WIDE = [(4000, 4000, 4160), (4000, 4000, 512), (2000, 6100, 256), (2000, 6100, 320), (2000, 6100, 704),
+        (4000, 4000, 8256)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: VNAME[v])
@@ -231,6 +234,23 @@ def test_fused_192_tiles_every_rank(K, R):
     log(f"[fused-192] M={M} N={N} K={K} R={R}")
     Y, dbg_idx, dbg_s = run_fused(d, variant=rtl.RTL_VARIANT_PRECOMPRESSED)
     rows = np.unique(np.concatenate([sample_rows(M, n=64), np.arange(M - 160, M, 7)]))
+    Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+    y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
+    err = row_rel_err(y, Yref)
+    log(f"  sampled {len(rows)} rows, max row rel err {err:.3e}")
+    assert err <= TOL_Y["bf16"]
+
+
+# 256-wide pre-compressed tiles with long K (the 4-wave kernel) without and with the
+# largest rank.
+@pytest.mark.parametrize("R", [0, 128])
+def test_fused_256_tiles_long_k(R):
+    M, N, K = 4000, 4000, 8256
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=9290 + R)
+    log(f"[fused-256] M={M} N={N} K={K} R={R}")
+    Y, dbg_idx, dbg_s = run_fused(d, variant=rtl.RTL_VARIANT_PRECOMPRESSED)
+    rows = np.unique(np.concatenate([sample_rows(M, n=48), np.arange(M - 160, M, 9)]))
     Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
     y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
     err = row_rel_err(y, Yref)
