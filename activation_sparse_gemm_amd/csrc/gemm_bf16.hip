@@ -588,10 +588,21 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) s_row[rb] = sred[64 * wm + 16 * rb + r16];
     } else {
+      // Pre-compressed (256-wide): for R <= 64 the rank-R operands are copied into the (now
+      // free) W ring once per workgroup and the slice is taken from there (loaded by every
+      // wave straight from memory they are a 192 KB burst per workgroup through L2).
+      if (a.R <= 64) {
+        wait_vmcnt<0>();
+        __syncthreads();  // every wave is done with the ring
+        lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
+        wait_vmcnt<0>();
+        __syncthreads();
+        lora_first_lds<TN, NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
+      }
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
         const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-        s_row[rb] = a.s[row < M ? row : M - 1];
+        s_row[rb] = a.R <= 64 ? lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16) : a.s[row < M ? row : M - 1];
       }
     }
     // ... and of the accumulator rows 16rb + 4q + j, held by lane 4q + j.
@@ -607,7 +618,7 @@ void gemm_kernel(const GemmArgs a) {
     float inv_s[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
-    for (int kk = 0; kk < (int)(R / 32); kk++) {
+    for (int kk = 0; kk < (FUSED || R > 64 ? (int)(R / 32) : 0); kk++) {
       u32x4 ta[4];
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {

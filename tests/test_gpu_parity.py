@@ -241,13 +241,15 @@ def test_fused_192_tiles_every_rank(K, R):
     assert err <= TOL_Y["bf16"]
 
 
-# 256-wide pre-compressed tiles with long K (the 4-wave kernel) without and with the
-# largest rank.
-@pytest.mark.parametrize("R", [0, 128])
-def test_fused_256_tiles_long_k(R):
-    M, N, K = 4000, 4000, 8256
+# 256-wide pre-compressed tiles in both kernels (K = 4160: the 8-wave kernel, which copies
+# the rank-R operands into LDS for R <= 64; K = 8256: the 4-wave kernel) with every
+# other supported rank.
+@pytest.mark.parametrize("R", [0, 32, 128])
+@pytest.mark.parametrize("K", [4160, 8256])
+def test_fused_256_tiles_every_rank(K, R):
+    M, N = 4000, 4000
     lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
-    d = synth.make_layer(lay, seed_base=9290 + R)
+    d = synth.make_layer(lay, seed_base=9290 + R + K)
     log(f"[fused-256] M={M} N={N} K={K} R={R}")
     Y, dbg_idx, dbg_s = run_fused(d, variant=rtl.RTL_VARIANT_PRECOMPRESSED)
     rows = np.unique(np.concatenate([sample_rows(M, n=48), np.arange(M - 160, M, 9)]))
