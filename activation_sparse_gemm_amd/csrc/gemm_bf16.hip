@@ -12,7 +12,7 @@
 //  Sparse modes run v_smfmac_f32_16x16x64_bf16; their epilogue adds (T / s) L_A^T into the
 //  accumulators with an extra K = R MFMA slice and stores s * acc, so the M x N low-rank
 //  product never reaches device memory.
-#include "gemm_common.h"
+#include "lora_lds.h"
 
 namespace rtl {
 
@@ -31,77 +31,6 @@ constexpr int kXBlk = 64 * 16 + 64 * 2;   // fused: one row block of the compres
 constexpr int kALds = kBM * 128;          // A tile bytes per LDS buffer (dense layout, the largest)
 constexpr int kCompIdx = 16384;           // pre-compressed: offset of the position words in an A buffer
 constexpr int kCompStage = 16384 + 2048;  // pre-compressed: one K step of the tile's four panels
-
-// Rank-R operands of one output tile staged in LDS (R <= 64): T [256][R] bf16 at +0, L_A
-// [TW][R] bf16 at +kLoraT, s [256] f32 at +kLoraT + kLoraA.  Rows of T and L_A keep their
-// R / 8 16-byte chunks, chunk c of row r at position c ^ (r mod R / 8) (so the 16 rows that
-// a fragment read touches fall in different banks).  Loaded with 16-byte direct-to-LDS
-// loads, 1 KB blocks dealt round-robin to the NW waves (lane l of a block writes position
-// l mod R / 8 of row l / (R / 8) and so loads the chunk stored there; s: 1024 / NW bytes
-// per wave); the caller waits for them (vmcnt) and then synchronises the workgroup.
-constexpr int kLoraT = 256 * 64 * 2;
-template <int TW, int NW>
-__device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a, int64_t m0, int64_t n0, int wave,
-                                               int lane) {
-  constexpr int kLoraA = TW * 64 * 2, SPW = 1024 / NW;
-  const int64_t R = a.R, Mp = (int64_t)a.n_panels * kPanel;
-  const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.s + m0, (Mp - m0) * 4);
-  if (16 * lane < SPW)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(lora + kLoraT + kLoraA + wave * SPW),
-                                             16, (uint32_t)(wave * SPW + lane * 16), 0, 0, 0);
-  const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
-  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (a.N - n0) * R * 2);
-  const int ch = (int)(R / 8);                               // 16-byte chunks per row
-  const int src = (lane & ~(ch - 1)) | ((lane ^ (lane / ch)) & (ch - 1));  // chunk this lane loads
-  for (int j = wave; j < (int)(R / 2); j += NW)  // 1 KB blocks of the 256 x R tile of T
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(lora + j * 1024), 16,
-                                             (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
-  for (int j = wave; j < (int)(TW * R / 512); j += NW)  // 1 KB blocks of the TW x R tile of L_A
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(lora + kLoraT + j * 1024),
-                                             16, (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
-}
-// s of tile row r from the staged copy (a 16-byte read: narrower LDS reads would make the
-// compiler wait for every load into LDS).
-template <int TW>
-__device__ __forceinline__ float lora_s_lds(const uint8_t* lora, int r) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(lora + kLoraT + TW * 128 + (r & ~3) * 4);
-  const uint32_t e = (r & 2) ? ((r & 1) ? w[3] : w[2]) : ((r & 1) ? w[1] : w[0]);
-  return __uint_as_float(e);
-}
-// acc[rb][nb] += (T / s)_rows L_A_cols^T from the staged copy, K = R in slices of 32: the
-// lane feeds tile row row0 + 16 rb + r16 and tile column col0 + 16 nb + r16.  A zero row
-// has s = 0 and T = 0; its T / s is taken as 0.
-template <int TW, int NB>
-__device__ __forceinline__ void lora_first_lds(f32x4 (&acc)[4][NB], const uint8_t* lora, int R, int row0, int col0,
-                                               int lane) {
-  const int q = lane >> 4, r16 = lane & 15;
-  float inv_s[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; rb++) {
-    const float sv = lora_s_lds<TW>(lora, row0 + 16 * rb + r16);
-    inv_s[rb] = sv > 0.f ? 1.f / sv : 0.f;
-  }
-  const int cm = R / 8 - 1;  // chunk swizzle mask
-  for (int kk = 0; kk < R / 32; kk++) {
-    u32x4 ta[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-      const int r = row0 + 16 * rb + r16;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(lora + r * R * 2 + 16 * ((4 * kk + q) ^ (r & cm)));
-#pragma unroll
-      for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-      const int c = col0 + nb * 16 + r16;
-      const u32x4 la = *reinterpret_cast<const u32x4*>(lora + kLoraT + c * R * 2 + 16 * ((4 * kk + q) ^ (c & cm)));
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++)
-        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
-                                                              __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
-    }
-  }
-}
 
 template <int MODE, bool DBG, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(2, 2)))

@@ -18,7 +18,7 @@
 //                    compressed operand straight to registers one K step ahead; the
 //                    epilogue scales by sw, adds the rank-R slice and stores s sx acc.
 #include "fp8_common.h"
-#include "gemm_common.h"
+#include "lora_lds.h"
 
 namespace rtl {
 
@@ -68,6 +68,7 @@ void gemm_fp8_kernel(const GemmArgs a) {
   constexpr int NB = TN / 32;                 // 16-column blocks per wave
   constexpr int WLD = TN * 8 / kFp8Threads;   // 16-byte W chunks per thread per K step
   __shared__ __attribute__((aligned(1024))) uint8_t wl[3 * TN * 128];
+  static_assert(3 * TN * 128 >= kLoraT + TN * 128 + 1024, "the ring holds the staged rank-R operands");
 
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
@@ -226,7 +227,17 @@ void gemm_fp8_kernel(const GemmArgs a) {
     for (int rb = 0; rb < 4; rb++) acc[rb][nb] *= swc;
   }
   const int64_t R = a.R;
-  for (int kk = 0; kk < (int)(R / 32); kk++) {
+  if (R > 0 && R <= 64) {
+    // T, L_A (and s) of the tile into the free ring, once per workgroup, then the slice
+    // from there.
+    wait_vmcnt<0>();
+    __syncthreads();
+    lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
+    wait_vmcnt<0>();
+    __syncthreads();
+    lora_slice_lds<NB>(acc, wl, (int)R, 64 * wm, (TN / 2) * wn, lane, inv_s);
+  }
+  for (int kk = 0; kk < (R > 64 ? (int)(R / 32) : 0); kk++) {
     u32x4 ta[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {

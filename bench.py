@@ -31,7 +31,8 @@ PEAK_BF16_SPARSE = 5.0e15  # the same counted dense-equivalent on the 2:4 sparse
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s (published)
 PEAK_FP8_DENSE = 5.0e15    # MI355X dense fp8 MFMA FLOP/s (published)
 KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/gemm_common.h",
-                  "activation_sparse_gemm_amd/csrc/bf16_common.h", "activation_sparse_gemm_amd/csrc/rtl_device.h"]
+                  "activation_sparse_gemm_amd/csrc/bf16_common.h", "activation_sparse_gemm_amd/csrc/rtl_device.h",
+                  "activation_sparse_gemm_amd/csrc/lora_lds.h"]
 
 
 def _code_only(text: str) -> str:
