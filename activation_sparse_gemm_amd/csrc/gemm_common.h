@@ -71,7 +71,7 @@ __device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, in
       if (row >= M) continue;
       uint16_t* y = Y + row * N + col;
       if (vec && col + 8 <= N) {
-        *reinterpret_cast<u32x4*>(y) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y));  // Y is not read again here
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++)

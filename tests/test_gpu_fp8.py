@@ -62,7 +62,8 @@ def check_fp8(d, tag, rows=None, y_rows=None):
     return Yg, Yref
 
 
-SMALL = [(64, 256, 256, 32), (300, 384, 520, 64), (1000, 1408, 1000, 32), (257, 768, 200, 0), (513, 2048, 1100, 128)]
+SMALL = [(64, 256, 256, 32), (300, 384, 520, 64), (1000, 1408, 1000, 32), (257, 768, 200, 0), (513, 2048, 1100, 128),
+         (700, 1024, 640, 96)]
 
 
 @pytest.mark.parametrize("shape", SMALL)
