@@ -602,9 +602,12 @@ void half_kernel(const GemmArgs a) {
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
-  // take the rank-R branch first from operands staged in LDS past the ring.
-  constexpr bool ONE = TW >= 192, LSTG = TW == 192;
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : 0)];
+  // take the rank-R branch first from operands staged in LDS past the ring.  The narrow
+  // tiles (two workgroups per CU) stage only L_A there, at the start, and take the branch
+  // at the end with T from memory.
+  constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = TW <= 128;
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : LAST ? TW * 128 : 0)];
   uint8_t* const lora = wl + WBUF * TW * 128;
 
   int tm, tn;
@@ -712,7 +715,9 @@ void half_kernel(const GemmArgs a) {
   // stages 0-2 (A before W, as in the loop); stages 0 and 1 complete before the first B
   // reads.
   const bool lfirst = LSTG && a.R <= 64;
+  const bool lalds = LAST && a.R > 0 && a.R <= 64;
   if (lfirst) lora_stage_lds<TW, 4>(lora, a, m0, n0, wave, lane);
+  if (lalds) lora_stage_la<TW, 4>(lora, a, n0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < AAH; j++) load_frag(kp(j), fa[j]);
@@ -766,7 +771,8 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       const int64_t col = n0 + nb * 16 + r16;
-      const u32x4 la = *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
+      const u32x4 la = lalds ? lora_la_lds(lora, (int)R, nb * 16 + r16, kk, q)
+                             : *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
 #pragma unroll
       for (int rb = 0; rb < 4; rb++)
         acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),

@@ -14,6 +14,18 @@ namespace rtl {
 // l mod R / 8 of row l / (R / 8) and so loads the chunk stored there; s: 1024 / NW bytes
 // per wave); the caller waits for them (vmcnt) and then synchronises the workgroup.
 constexpr int kLoraT = 256 * 64 * 2;
+// The tile's L_A rows (columns n0..n0 + TW - 1 of the output) into dst, swizzled as above.
+template <int TW, int NW>
+__device__ __forceinline__ void lora_stage_la(uint8_t* dst, const GemmArgs& a, int64_t n0, int wave, int lane) {
+  const int64_t R = a.R;
+  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (a.N - n0) * R * 2);
+  const int ch = R >= 8 ? (int)(R / 8) : 1;                  // 16-byte chunks per row
+  const int src = (lane & ~(ch - 1)) | ((lane ^ (lane / ch)) & (ch - 1));  // chunk this lane loads
+  for (int j = wave; j < (int)(TW * R / 512); j += NW)  // 1 KB blocks of the TW x R tile of L_A
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                             (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
+}
+// T, L_A and s of the tile (layout above).
 template <int TW, int NW>
 __device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a, int64_t m0, int64_t n0, int wave,
                                                int lane) {
@@ -24,15 +36,16 @@ __device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(lora + kLoraT + kLoraA + wave * SPW),
                                              16, (uint32_t)(wave * SPW + lane * 16), 0, 0, 0);
   const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
-  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (a.N - n0) * R * 2);
-  const int ch = R >= 8 ? (int)(R / 8) : 1;                 // 16-byte chunks per row
+  const int ch = R >= 8 ? (int)(R / 8) : 1;                  // 16-byte chunks per row
   const int src = (lane & ~(ch - 1)) | ((lane ^ (lane / ch)) & (ch - 1));  // chunk this lane loads
   for (int j = wave; j < (int)(R / 2); j += NW)  // 1 KB blocks of the 256 x R tile of T
     __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(lora + j * 1024), 16,
                                              (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
-  for (int j = wave; j < (int)(TW * R / 512); j += NW)  // 1 KB blocks of the TW x R tile of L_A
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(lora + kLoraT + j * 1024),
-                                             16, (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
+  lora_stage_la<TW, NW>(lora + kLoraT, a, n0, wave, lane);
+}
+// Fragment of staged L_A for tile column c, K = R slice kk: chunk 4 kk + q of row c.
+__device__ __forceinline__ u32x4 lora_la_lds(const uint8_t* la, int R, int c, int kk, int q) {
+  return *reinterpret_cast<const u32x4*>(la + c * R * 2 + 16 * ((4 * kk + q) ^ (c & (R / 8 - 1))));
 }
 // s of tile row r from the staged copy (a 16-byte read: narrower LDS reads would make the
 // compiler wait for every load into LDS).
@@ -62,7 +75,7 @@ __device__ __forceinline__ void lora_slice_lds(f32x4 (&acc)[4][NB], const uint8_
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       const int c = col0 + nb * 16 + r16;
-      const u32x4 la = *reinterpret_cast<const u32x4*>(lora + kLoraT + c * R * 2 + 16 * ((4 * kk + q) ^ (c & cm)));
+      const u32x4 la = lora_la_lds(lora + kLoraT, R, c, kk, q);
 #pragma unroll
       for (int rb = 0; rb < 4; rb++)
         acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
