@@ -602,10 +602,10 @@ void half_kernel(const GemmArgs a) {
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
-  // take the rank-R branch first from operands staged in LDS past the ring.  The narrow
-  // tiles (two workgroups per CU) stage only L_A there, at the start, and take the branch
-  // at the end with T from memory.
-  constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = TW <= 128;
+  // take the rank-R branch first from operands staged in LDS past the ring.  The other
+  // widths stage only L_A there, at the start, and take the branch at the end with T from
+  // memory (two 128-wide workgroups, or one 256-wide one, then fill the 160 KB of LDS).
+  constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = !LSTG;
   __shared__ __attribute__((aligned(1024)))
   uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : LAST ? TW * 128 : 0)];
   uint8_t* const lora = wl + WBUF * TW * 128;
