@@ -241,6 +241,26 @@ def test_fused_192_tiles_every_rank(K, R):
     assert err <= TOL_Y["bf16"]
 
 
+# 128-wide pre-compressed tiles (two workgroups per CU) with every supported rank: R <= 64
+# copies the tile's L_A into LDS at the start (R = 32 and 64: four and eight 1 KB blocks
+# per wave); R = 0 has no rank-R branch; R > 64 reads L_A from memory.  2000 x 4000 is 8 x 32
+# tiles of 256 x 128 with ragged M and N tails (208 rows, 32 columns).
+@pytest.mark.parametrize("R", [0, 32, 64, 96, 128])
+@pytest.mark.parametrize("K", [320, 704])
+def test_fused_128_tiles_every_rank(K, R):
+    M, N = 2000, 4000
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=9390 + K + R)
+    log(f"[fused-128] M={M} N={N} K={K} R={R}")
+    Y, dbg_idx, dbg_s = run_fused(d, variant=rtl.RTL_VARIANT_PRECOMPRESSED)
+    rows = np.unique(np.concatenate([sample_rows(M, n=64), np.arange(M - 160, M, 7)]))
+    Yref, sref = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+    y = f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16")
+    err = row_rel_err(y, Yref)
+    log(f"  sampled {len(rows)} rows, max row rel err {err:.3e}")
+    assert err <= TOL_Y["bf16"]
+
+
 # 256-wide pre-compressed tiles in both kernels (K = 4160: the 8-wave kernel, which copies
 # the rank-R operands into LDS for R <= 64; K = 8256: the 4-wave kernel) with every
 # other supported rank.
