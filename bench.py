@@ -66,6 +66,16 @@ def stored_traffic(layer: str, variant: str):
     return t.get("bytes_per_launch")
 
 
+def stored_kernel_name(layer: str, variant: str) -> str:
+    """Name of the GEMM kernel the committed counter summary was taken on (the kernel
+    the launcher picks for this layer), or a generic name when there is none."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{variant}_{layer}.json")
+    if not os.path.exists(path):
+        return "gemm_kernel"
+    with open(path) as f:
+        return str(json.load(f).get("kernel", "gemm_kernel"))
+
+
 def to_dev(a):
     import torch
     if a is None:
@@ -262,7 +272,8 @@ def main():
     achieved = alg_flops / t_main
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_DENSE / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_DENSE, "traffic": stored_traffic(args.layer, kernel_variant),
-                "kernel": f"gemm_kernel ({kernel_variant} operand), {t_main * 1e6:.1f} us per launch",
+                "kernel": f"{stored_kernel_name(args.layer, kernel_variant)} (GEMM, {kernel_variant} operand), "
+                          f"{t_main * 1e6:.1f} us per launch",
                 "flop_per_launch": alg_flops}
     pbytes = prep_bytes(M, K, R, kernel_variant)
     t_prep = t[kernel_variant + "_prep"]
