@@ -73,8 +73,8 @@ inline PrepSplit prep_split(int64_t M, int64_t K) {
   return PrepSplit{4, (int)((KT + kts - 1) / kts), (int)kts};
 }
 
-// Workspace: T [Mp,R] bf16 | nx2 or s [Mp] f32 | (pre-compressed) values, position words
-// | (K split) partial T [ks,Mp,R] f32, partial squared norms [ks,Mp,2] f32.
+// Workspace: T (or T / s) [Mp,R] bf16 | s [Mp] f32 | (pre-compressed) values, position
+// words | (K split) partial T [ks,Mp,R] f32, partial squared norms [ks,Mp,2] f64.
 struct WsLayout {
   size_t t, norm, cvals, cidx, tpart, npart, total;
 };
@@ -89,7 +89,7 @@ inline WsLayout ws_layout(int64_t M, int64_t K, int64_t R, bool comp) {
   L.cidx = L.cvals + (comp ? align256((size_t)Mp * (K / 2) * 2) : 0);
   L.tpart = L.cidx + (comp ? align256((size_t)(Mp / kPanel) * (K / kBK) * 512) : 0);
   L.npart = L.tpart + align256((size_t)(parts * Mp * R * 4));
-  L.total = L.npart + align256((size_t)(parts * Mp * 2 * 4));
+  L.total = L.npart + align256((size_t)(parts * Mp * 2 * 8));
   return L;
 }
 

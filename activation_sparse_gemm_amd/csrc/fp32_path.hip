@@ -1,7 +1,8 @@
 // fp32_path.hip -- fp32 mode of the layer on the vector ALUs (the matrix cores have no
 // fp32 2:4-sparse instruction).  Same arithmetic as the bf16 path ("RT-Lynx: Putting the
 // GEMM Sparsity In a Right Way for Diffusion Models", summary page, method steps 1-2):
-// selection in the tile prologue, row norms accumulated across the K loop, rank-R
+// selection in the tile prologue, row norms accumulated across the K loop (in double
+// precision, so no finite row underflows or overflows them), rank-R
 // down projection of the dense rows in the same loop, s and the rank-R up projection in
 // the epilogue.  Sized for small latency-bound layers.
 #include "rtl_device.h"
@@ -24,7 +25,7 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
   __shared__ float Ws[kFT][kFK + 1];
   __shared__ float Bs[kFMaxR][kFK + 1];  // L_B tile
   __shared__ float Ts[kFT][kFMaxR];
-  __shared__ float red[2][kFT][kFK / 4];
+  __shared__ double red[2][kFT][kFK / 4];
   __shared__ float srow[kFT];
 
   const int tid = threadIdx.x;
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
   float tacc[kFT * kFMaxR / 256];
 #pragma unroll
   for (int i = 0; i < kFT * kFMaxR / 256; i++) tacc[i] = 0.f;
-  float nx2 = 0.f, nt2 = 0.f;
+  double nx2 = 0.0, nt2 = 0.0;
 
   for (int64_t k0 = 0; k0 < K; k0 += kFK) {
     // X group: selection (tile prologue)
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         Xs[lr][4 * lg + j] = kept[j];
-        nx2 = fmaf(kept[j], kept[j], nx2);
+        nx2 = fma((double)kept[j], (double)kept[j], nx2);
       }
       if (SPARSE) {
         int lo, hi;
@@ -66,8 +67,8 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
         for (int j = 0; j < 4; j++)
           if (j != lo && j != hi) kept[j] = 0.f;
         const float vlo = __uint_as_float(x[lo]), vhi = __uint_as_float(x[hi]);
-        nt2 = fmaf(vlo, vlo, nt2);
-        nt2 = fmaf(vhi, vhi, nt2);
+        nt2 = fma((double)vlo, (double)vlo, nt2);
+        nt2 = fma((double)vhi, (double)vhi, nt2);
         if (dbg_idx != nullptr && blockIdx.x == 0 && m0 + lr < M && k < K)
           dbg_idx[(m0 + lr) * (K / 4) + k / 4] = (uint8_t)(lo | (hi << 2));
       }
@@ -124,12 +125,12 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
     }
     __syncthreads();
     if (tid < kFT) {
-      float a = 0.f, t = 0.f;
+      double a = 0.0, t = 0.0;
       for (int g = 0; g < kFK / 4; g++) {
         a += red[0][tid][g];
         t += red[1][tid][g];
       }
-      const float s = sqrtf(a) / (sqrtf(t) + eps);
+      const float s = scale_from_norms(a, t, eps);
       srow[tid] = s;
       if (dbg_s != nullptr && blockIdx.x == 0 && m0 + tid < M) dbg_s[m0 + tid] = s;
     }

@@ -6,12 +6,12 @@
 //    kModeComp:  the A operand arrives compressed from the pre-pass (kept values and
 //                2-bit positions in sparse-MFMA register order).
 //    kModeFused: the 2-of-4 selection and compression run in the GEMM's own A-operand
-//                prologue, one K step ahead of the sparse MFMAs; the kept-value norm is
-//                accumulated across the K loop.
+//                prologue, one K step ahead of the sparse MFMAs (s comes from the
+//                pre-pass, which also selects to form ||X~||).
 //    kModeDense: the dense product X W^T (v_mfma_f32_16x16x32_bf16), same tiling.
-//  Sparse modes run v_smfmac_f32_16x16x64_bf16; their epilogue adds (T / s) L_A^T into the
-//  accumulators with an extra K = R MFMA slice and stores s * acc, so the M x N low-rank
-//  product never reaches device memory.
+//  Sparse modes run v_smfmac_f32_16x16x64_bf16; their epilogue scales the accumulators by
+//  s and then adds T L_A^T into them with an extra K = R MFMA slice before the single
+//  store, so the M x N low-rank product never reaches device memory.
 #include "lora_lds.h"
 
 namespace rtl {
@@ -48,7 +48,6 @@ void gemm_kernel(const GemmArgs a) {
   constexpr bool CALDS = MODE == kModeComp && TN == 256;
   __shared__ __attribute__((aligned(1024))) uint8_t alc[CALDS ? 3 * kCompStage : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
-  __shared__ float sred[FUSED ? 256 : 1];
 
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
@@ -150,14 +149,13 @@ void gemm_kernel(const GemmArgs a) {
       x[j][1] = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff + 16, so, 0);
     }
   };
-  float nt2[2] = {0.f, 0.f};
   // Selection codes of this tile's rows (first tile column only); rows past M fall outside
   // the buffer and their stores are dropped.
   const __amdgpu_buffer_rsrc_t dres =
       make_rsrc(DBG ? a.dbg_idx + m0 * (K / 4) : nullptr, (DBG && tn == 0) ? (M - m0) * (K / 4) : 0);
-  // Fused prologue for row block 2wn + j: 2-of-4 selection, compression into the sparse
-  // operand (to LDS for both waves of the slab), kept-value norm.
-  auto select_rb = [&](int kt, const Raw& x, int j, int buf, bool valid) {
+  // Fused prologue for row block 2wn + j: 2-of-4 selection and compression into the sparse
+  // operand (to LDS for both waves of the slab).
+  auto select_rb = [&](int kt, const Raw& x, int j, int buf) {
     const int rb = 2 * wn + j;
     const uint32_t w8[8] = {x[j][0][0], x[j][0][1], x[j][0][2], x[j][0][3],
                             x[j][1][0], x[j][1][1], x[j][1][2], x[j][1][3]};
@@ -170,8 +168,6 @@ void gemm_kernel(const GemmArgs a) {
       v[g] = vv;
       code16 |= cc << (4 * g);
       bytes |= cc << (8 * g);
-      const float t = dot2_bf16(vv, vv, nt2[j]);
-      nt2[j] = valid ? t : nt2[j];
     }
     uint8_t* blk = al + ((buf * 4 + wm) * 4 + rb) * kXBlk;
     *reinterpret_cast<u32x4*>(blk + lane * 16) = v;
@@ -237,7 +233,7 @@ void gemm_kernel(const GemmArgs a) {
         }
       }
       if (FUSED && (nb == 0 || nb == NB / 2))
-        select_rb(min(kt + 1, KT - 1), xsel, nb == 0 ? 0 : 1, buf ^ 1, kt + 1 < KT);
+        select_rb(min(kt + 1, KT - 1), xsel, nb == 0 ? 0 : 1, buf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -483,8 +479,8 @@ void gemm_kernel(const GemmArgs a) {
   if (FUSED) {
     load_raw(0, xr0);
     load_raw(min(1, KT - 1), xr1);
-    select_rb(0, xr0, 0, 0, true);
-    select_rb(0, xr0, 1, 0, true);
+    select_rb(0, xr0, 0, 0);
+    select_rb(0, xr0, 1, 0);
   } else {
     load_at(0, a0);
     load_at(min(1, KT - 1), a1);
@@ -499,63 +495,35 @@ void gemm_kernel(const GemmArgs a) {
   }
 
   if (SPARSE) {
-    // s of row 16rb + r16 (the row this lane feeds as A operand) ...
-    float s_row[4];
-    if (FUSED) {
-#pragma unroll
-      for (int j = 0; j < 2; j++) {
-        float t = nt2[j];
-        t += __shfl_xor(t, 16, 64);
-        t += __shfl_xor(t, 32, 64);
-        const int rb = 2 * wn + j;
-        const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-        const float sv = sqrtf(a.nx2[row < M ? row : M - 1]) / (sqrtf(t) + a.eps);
-        if (q == 0) sred[64 * wm + 16 * rb + r16] = sv;
-        if (a.dbg_s != nullptr && tn == 0 && q == 0 && row < M) a.dbg_s[row] = sv;
-      }
+    // Epilogue: acc *= s (row scale of the sparse product), then acc += T_tile L_A_tile^T
+    // (K = R in slices of 32), then one bf16 store.  s_row[rb] is the s of row 16rb + r16,
+    // the row this lane feeds as A operand.  Pre-compressed mode with R <= 64 first copies
+    // the tile's T, L_A and s into the (now free) W ring once per workgroup and takes the
+    // slice from there (loaded by every wave straight from memory they are a 192 KB burst
+    // per workgroup through L2).
+    const bool lds_slice = MODE == kModeComp && a.R <= 64;
+    if (lds_slice) {
+      wait_vmcnt<0>();
+      __syncthreads();  // every wave is done with the ring
+      lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
+      wait_vmcnt<0>();
       __syncthreads();
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++) s_row[rb] = sred[64 * wm + 16 * rb + r16];
-    } else {
-      // Pre-compressed (256-wide): for R <= 64 the rank-R operands are copied into the (now
-      // free) W ring once per workgroup and the slice is taken from there (loaded by every
-      // wave straight from memory they are a 192 KB burst per workgroup through L2).
-      if (a.R <= 64) {
-        wait_vmcnt<0>();
-        __syncthreads();  // every wave is done with the ring
-        lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
-        wait_vmcnt<0>();
-        __syncthreads();
-        lora_first_lds<TN, NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++) {
-        const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-        s_row[rb] = a.R <= 64 ? lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16) : a.s[row < M ? row : M - 1];
-      }
     }
-    // ... and of the accumulator rows 16rb + 4q + j, held by lane 4q + j.
-    float s_acc[4][4];
+    float s_row[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
-    // Rank-R branch, accumulated before the rescale so the accumulators stay with the
-    // matrix cores: acc += (T / s)_tile L_A_tile^T, K = R in slices of 32; Y = s * acc.
-    // A zero row has s = 0 and T = 0; its T / s is taken as 0.
+    for (int rb = 0; rb < 4; rb++) {
+      const int64_t row = m0 + 64 * wm + 16 * rb + r16;
+      s_row[rb] = lds_slice ? lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16) : a.s[row < M ? row : M - 1];
+    }
+    scale_rows<NB>(acc, s_row, lane);
+    if (lds_slice) lora_slice_lds<NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
     const int64_t R = a.R;
-    float inv_s[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++) inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
-    for (int kk = 0; kk < (FUSED || R > 64 ? (int)(R / 32) : 0); kk++) {
+    for (int kk = 0; kk < (lds_slice ? 0 : (int)(R / 32)); kk++) {
       u32x4 ta[4];
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
         const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-        const u32x4 t = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-          ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+        ta[rb] = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) {
@@ -567,15 +535,10 @@ void gemm_kernel(const GemmArgs a) {
               __builtin_bit_cast(bf16x8, ta[rb]), __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
       }
     }
-    // Store Y = s * acc (bf16, round to nearest even).
-    __syncthreads();  // the LDS rings are free
-    store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
-                      [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
-    return;
   }
 
-  // Dense: store Y (bf16, round to nearest even).  Lane holds column 16nb + r16 of its
-  // half, rows 16rb + 4q + j of its slab.
+  // Store Y (bf16, round to nearest even).  Lane holds column 16nb + r16 of its half, rows
+  // 16rb + 4q + j of its slab.
   __syncthreads();  // the LDS rings are free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
                     [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
@@ -602,9 +565,11 @@ void half_kernel(const GemmArgs a) {
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
-  // take the rank-R branch first from operands staged in LDS past the ring.  The other
-  // widths stage only L_A there, at the start, and take the branch at the end with T from
-  // memory (two 128-wide workgroups, or one 256-wide one, then fill the 160 KB of LDS).
+  // take the rank-R branch first, from T / s (formed by the pre-pass), L_A and s staged in
+  // LDS past the ring; the final store multiplies by s.  The other widths stage only L_A
+  // there, at the start, and at the end scale the accumulators by s and then add T L_A^T
+  // with T from memory (two 128-wide workgroups, or one 256-wide one, then fill the 160 KB
+  // of LDS).
   constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = !LSTG;
   __shared__ __attribute__((aligned(1024)))
   uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : LAST ? TW * 128 : 0)];
@@ -729,7 +694,7 @@ void half_kernel(const GemmArgs a) {
   if (lfirst) {
     wait_vmcnt<5 * AAH + 3 * WLD>();  // the rank-R operands (issued before the loads since)
     barrier_nofence();
-    lora_first_lds<TW, NB>(acc, lora, (int)a.R, 64 * wave, 0, lane);
+    lora_slice_lds<NB>(acc, lora, (int)a.R, 64 * wave, 0, lane);
   }
   wait_vmcnt<WLD>();
   barrier_nofence();
@@ -747,26 +712,23 @@ void half_kernel(const GemmArgs a) {
     if (kt + j < KT) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
   wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
 
-  // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
-  // accumulator rows 16rb + 4q + j (lane 4q + j); unless taken first, the rank-R slice
-  // acc += (T / s) L_A^T; then Y = s * acc (a zero row has s = 0 and T = 0; its T / s is
-  // taken as 0).
-  float s_row[4], inv_s[4];
+  // Epilogue: s_row[rb] is the s of row 16rb + r16 (the row this lane feeds as A operand).
+  // Unless the rank-R slice was taken first (its T / s term then makes Y = s * acc), the
+  // accumulators are scaled by s and T L_A^T is added; then the single bf16 store.
+  float s_row[4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
     const int64_t row = m0 + 64 * wave + 16 * rb + r16;
     s_row[rb] = lfirst ? lora_s_lds<TW>(lora, 64 * wave + 16 * rb + r16) : a.s[row < M ? row : M - 1];
-    inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
   }
+  scale_rows<NB>(acc, s_row, lane);
   const int64_t R = a.R;
   for (int kk = 0; kk < (lfirst ? 0 : (int)(R / 32)); kk++) {
     u32x4 ta[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       const int64_t row = m0 + 64 * wave + 16 * rb + r16;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
-#pragma unroll
-      for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+      ta[rb] = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
@@ -779,14 +741,9 @@ void half_kernel(const GemmArgs a) {
                                                               __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
     }
   }
-  float s_acc[4][4];
-#pragma unroll
-  for (int rb = 0; rb < 4; rb++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
   __syncthreads();  // the LDS ring is free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wave, n0, wl + wave * 16 * (2 * TW + 16), lane,
-                    [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
+                    [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
 }
 
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
@@ -815,6 +772,12 @@ static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
   return half_cost < full_cost;
 }
 
+bool lowrank_first_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R) {
+  // half_kernel<192> (192-wide pre-compressed tiles) takes the slice first for R <= 64
+  const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
+  return comp && R > 0 && R <= 64 && !use_half_tiles(M, N, K) && choose_tn(M, N) == 192;
+}
+
 template <int TN>
 static void launch_main_tn(bool comp, GemmArgs g, uint8_t* dbg_idx, hipStream_t stream) {
   const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(kGemmThreads);
@@ -840,14 +803,12 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   const int tn = choose_tn(M, N);
   GemmArgs g = gemm_args(M, N, K, R, X, W, LA, Y, eps, tn);
   g.T = (const uint16_t*)(base + L.t);
+  g.s = (const float*)(base + L.norm);
   if (comp) {
-    g.s = (const float*)(base + L.norm);
     g.cvals = base + L.cvals;
     g.cidx = base + L.cidx;
   } else {
-    g.nx2 = (const float*)(base + L.norm);
     g.dbg_idx = dbg_idx;
-    g.dbg_s = dbg_s;
   }
   if (comp && use_half_tiles(M, N, K)) {
     GemmArgs h = g;

@@ -30,15 +30,13 @@ struct GemmArgs {
   const uint16_t* X;
   const uint16_t* W;
   const uint16_t* LA;
-  const uint16_t* T;      // [Mp, R] bf16
-  const float* nx2;       // [Mp] (fused mode)
-  const float* s;         // [Mp] (pre-compressed mode)
+  const uint16_t* T;      // [Mp, R] bf16: T, or T / s for a slice taken before the main loop
+  const float* s;         // [Mp]
   const uint8_t* cvals;   // pre-compressed mode
   const uint8_t* cidx;
   float eps;
   uint16_t* Y;
   uint8_t* dbg_idx;       // fused mode, [M, K/4] or null
-  float* dbg_s;           // fused mode, [M] or null
   int tiles_m, tiles_n, n_panels;
   const float* ax;        // FP8 layer: [Mp] row absmax of X
   const float* sw;        // FP8 layer: [N] weight dequantisation scales

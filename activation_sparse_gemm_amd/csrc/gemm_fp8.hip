@@ -16,7 +16,8 @@
 //                    through a 3-buffer LDS ring (its [TN][128] byte tiles have the
 //                    layout of the bf16 kernel's [TN][64] element tiles), the
 //                    compressed operand straight to registers one K step ahead; the
-//                    epilogue scales by sw, adds the rank-R slice and stores s sx acc.
+//                    epilogue scales by sw and s sx, then adds the rank-R slice
+//                    T L_A^T before the single store of Y.
 #include "fp8_common.h"
 #include "lora_lds.h"
 
@@ -207,17 +208,15 @@ void gemm_fp8_kernel(const GemmArgs a) {
     }
   }
 
-  // Epilogue.  Row scale s * sx of row 16rb + r16 (the row this lane feeds as A operand)
-  // and of the accumulator rows 16rb + 4q + j (lane 4q + j); column scale sw of the
-  // lane's column 16nb + r16.  acc *= sw; acc += (T / (s sx)) L_A^T (K = R slices of 32);
-  // Y = s sx acc.  A row with s sx = 0 takes T / (s sx) as 0.
-  float s_row[4], inv_s[4];
+  // Epilogue: acc *= sw (column scale of the lane's column 16nb + r16) and s * sx (row
+  // scale; s_row[rb] belongs to row 16rb + r16, the row this lane feeds as A operand), then
+  // acc += T L_A^T (K = R in slices of 32), then the single bf16 store.
+  float s_row[4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
     const int64_t row = m0 + 64 * wm + 16 * rb + r16;
     const int64_t rr = row < M ? row : M - 1;
     s_row[rb] = a.s[rr] * (a.ax[rr] / 448.0f);
-    inv_s[rb] = s_row[rb] > 0.f ? 1.f / s_row[rb] : 0.f;
   }
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) {
@@ -226,6 +225,7 @@ void gemm_fp8_kernel(const GemmArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) acc[rb][nb] *= swc;
   }
+  scale_rows<NB>(acc, s_row, lane);
   const int64_t R = a.R;
   if (R > 0 && R <= 64) {
     // T, L_A (and s) of the tile into the free ring, once per workgroup, then the slice
@@ -235,16 +235,14 @@ void gemm_fp8_kernel(const GemmArgs a) {
     lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
     wait_vmcnt<0>();
     __syncthreads();
-    lora_slice_lds<NB>(acc, wl, (int)R, 64 * wm, (TN / 2) * wn, lane, inv_s);
+    lora_slice_lds<NB>(acc, wl, (int)R, 64 * wm, (TN / 2) * wn, lane);
   }
   for (int kk = 0; kk < (R > 64 ? (int)(R / 32) : 0); kk++) {
     u32x4 ta[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
-#pragma unroll
-      for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+      ta[rb] = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
@@ -256,14 +254,9 @@ void gemm_fp8_kernel(const GemmArgs a) {
                                                               __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
     }
   }
-  float s_acc[4][4];
-#pragma unroll
-  for (int rb = 0; rb < 4; rb++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
   __syncthreads();  // the LDS ring is free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
-                    [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
+                    [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
 }
 
 size_t fused_fp8_workspace(int64_t M, int64_t N, int64_t K, int64_t R) {

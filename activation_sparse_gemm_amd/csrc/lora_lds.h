@@ -55,12 +55,13 @@ __device__ __forceinline__ float lora_s_lds(const uint8_t* lora, int r) {
   const uint32_t e = (r & 2) ? ((r & 1) ? w[3] : w[2]) : ((r & 1) ? w[1] : w[0]);
   return __uint_as_float(e);
 }
-// acc[rb][nb] += (T * inv_s)_rows L_A_cols^T from the staged copy, K = R in slices of 32:
-// the lane feeds tile row row0 + 16 rb + r16 (scaled by inv_s[rb]) and tile column
-// col0 + 16 nb + r16.
+// acc[rb][nb] += T_rows L_A_cols^T from the staged copy, K = R in slices of 32: the lane
+// feeds tile row row0 + 16 rb + r16 and tile column col0 + 16 nb + r16.  The staged rows
+// hold T itself when the accumulators were already scaled by s, or T / s (formed by the
+// pre-pass in double precision) when the slice comes before the main loop.
 template <int NB>
 __device__ __forceinline__ void lora_slice_lds(f32x4 (&acc)[4][NB], const uint8_t* lora, int R, int row0, int col0,
-                                               int lane, const float (&inv_s)[4]) {
+                                               int lane) {
   const int q = lane >> 4, r16 = lane & 15;
   const int cm = R / 8 - 1;  // chunk swizzle mask
   for (int kk = 0; kk < R / 32; kk++) {
@@ -68,9 +69,7 @@ __device__ __forceinline__ void lora_slice_lds(f32x4 (&acc)[4][NB], const uint8_
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       const int r = row0 + 16 * rb + r16;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(lora + r * R * 2 + 16 * ((4 * kk + q) ^ (r & cm)));
-#pragma unroll
-      for (int e = 0; e < 4; e++) ta[rb][e] = pack_bf16x2(bf16lo(t[e]) * inv_s[rb], bf16hi(t[e]) * inv_s[rb]);
+      ta[rb] = *reinterpret_cast<const u32x4*>(lora + r * R * 2 + 16 * ((4 * kk + q) ^ (r & cm)));
     }
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
@@ -83,19 +82,20 @@ __device__ __forceinline__ void lora_slice_lds(f32x4 (&acc)[4][NB], const uint8_
     }
   }
 }
-// The same with inv_s = 1 / s from the staged s (the bf16 layer).  A zero row has s = 0 and
-// T = 0; its T / s is taken as 0.
-template <int TW, int NB>
-__device__ __forceinline__ void lora_first_lds(f32x4 (&acc)[4][NB], const uint8_t* lora, int R, int row0, int col0,
-                                               int lane) {
-  const int r16 = lane & 15;
-  float inv_s[4];
+
+// acc[rb][nb][j] *= s of accumulator row 16 rb + 4q + j (s_row[rb] is the s of row
+// 16 rb + r16, the row this lane feeds as A operand; lane 4q + j holds row 4q + j's).
+template <int NB>
+__device__ __forceinline__ void scale_rows(f32x4 (&acc)[4][NB], const float (&s_row)[4], int lane) {
+  const int q = lane >> 4;
 #pragma unroll
-  for (int rb = 0; rb < 4; rb++) {
-    const float sv = lora_s_lds<TW>(lora, row0 + 16 * rb + r16);
-    inv_s[rb] = sv > 0.f ? 1.f / sv : 0.f;
-  }
-  lora_slice_lds<NB>(acc, lora, R, row0, col0, lane, inv_s);
+  for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float sv = __shfl(s_row[rb], 4 * q + j, 64);
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) acc[rb][nb][j] *= sv;
+    }
 }
 
 }  // namespace rtl

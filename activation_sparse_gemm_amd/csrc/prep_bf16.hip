@@ -1,9 +1,10 @@
 // prep_bf16.hip -- the bf16 pre-pass over X for the norm-compensated 2:4 activation-
 // sparse linear layer ("RT-Lynx: Putting the GEMM Sparsity In a Right Way for Diffusion
 // Models", summary page, method steps 1 and 2).  One read of the dense X forms the
-// rank-R down projection T = X L_B^T on the matrix cores, the squared row norms and, for
-// the pre-compressed variant, the 2-of-4 selection itself: the kept values and their
-// 2-bit positions, written in the register order of the sparse MFMA's A operand, and s.
+// rank-R down projection T = X L_B^T on the matrix cores, the squared row norms (in
+// double precision), the 2-of-4 selection and s; for the pre-compressed variant it also
+// writes the kept values and their 2-bit positions in the register order of the sparse
+// MFMA's A operand.
 #include "bf16_common.h"
 #include "fp8_common.h"
 
@@ -14,17 +15,17 @@ struct PrepArgs {
   const uint16_t* X;
   const uint16_t* LB;
   float eps;
-  uint16_t* T;        // [Mp, R] bf16
-  float* nx2;         // [Mp] (fused mode)
-  float* s;           // [Mp] (pre-compressed mode)
+  uint16_t* T;        // [Mp, R] bf16: T, or T / s when `fold` is set
+  float* s;           // [Mp]
   uint8_t* cvals;     // pre-compressed mode
   uint8_t* cidx;
   uint8_t* dbg_idx;   // [M, K/4] or null (pre-compressed mode)
-  float* dbg_s;       // [M] or null (pre-compressed mode)
+  float* dbg_s;       // [M] or null
   float* tpart;       // [ks, Mp, R] partial T when ks > 1
-  float* npart;       // [ks, Mp, 2] partial squared norms when ks > 1
+  double* npart;      // [ks, Mp, 2] partial squared norms when ks > 1
   int ks;             // K splits
   int kts;            // K steps per split
+  int fold;           // write T / s (formed in double precision) instead of T
   float* ax;          // FP8 layer: [Mp] row absmax of X (written when ks == 1)
   float* apart;       // FP8 layer: [ks, Mp] partial row absmax when ks > 1
 };
@@ -34,9 +35,11 @@ struct PrepArgs {
 // row (k = 16q..16q+15 of a step), which serve both the selection (four groups of 4) and,
 // read as two 8-wide K slices, the A operand of the rank-R product; the L_B slice of each
 // step passes through LDS once per workgroup and is shared by its rows.  X and L_B
-// are loaded three steps ahead.  With several K splits the partial T and norms go to the
-// workspace and prep_reduce_kernel sums them in a fixed order.  AMAX (the FP8 layer) also
-// takes each row's largest magnitude, the scale of its 8-bit quantisation.
+// are loaded three steps ahead.  The squared norms ||X||^2 and ||X~||^2 are summed in
+// double precision.  With several K splits the partial T and norms go to the workspace and
+// prep_reduce_kernel sums them in a fixed order.  COMPRESS writes the compressed operand;
+// without it (the prologue variant) the selection still runs, for ||X~||^2.  AMAX (the
+// FP8 layer) also takes each row's largest magnitude, the scale of its 8-bit quantisation.
 template <bool COMPRESS, int RC, int PW, bool AMAX>  // RC = R / 32, PW waves = 16-row blocks per workgroup
 __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   constexpr int R = 32 * RC, CB = 2 * RC;
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   f32x4 tacc[CB > 0 ? CB : 1];
 #pragma unroll
   for (int cb = 0; cb < (CB > 0 ? CB : 1); cb++) tacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float nx2 = 0.f, nt2 = 0.f;
+  double nx2 = 0.0, nt2 = 0.0;
   uint32_t amax = 0;  // largest sign-cleared bf16 pattern seen (finite values order as integers)
 
   // A step past the end of the split (valid == false) reruns the last step's idempotent
@@ -99,12 +102,12 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     const u32x4 xv0 = valid ? st.x[0] : z, xv1 = valid ? st.x[1] : z;
     const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
 #pragma unroll
-    for (int g = 0; g < 8; g++) nx2 = dot2_bf16(w8[g], w8[g], nx2);
+    for (int g = 0; g < 8; g++) nx2 = sq2_f64(w8[g], nx2);
     if (AMAX) {
 #pragma unroll
       for (int g = 0; g < 8; g++) amax = max(amax, max(w8[g] & 0x7FFFu, (w8[g] >> 16) & 0x7FFFu));
     }
-    if (COMPRESS) {
+    {
       u32x4 v;
       uint32_t code16 = 0, bytes = 0;
       const uint32_t r8[8] = {st.x[0][0], st.x[0][1], st.x[0][2], st.x[0][3],
@@ -116,12 +119,14 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
         v[g] = vv;
         code16 |= cc << (4 * g);
         bytes |= cc << (8 * g);
-        const float t = dot2_bf16(vv, vv, nt2);
+        const double t = sq2_f64(vv, nt2);
         nt2 = valid ? t : nt2;
       }
+      if (COMPRESS) {
       *reinterpret_cast<u32x4*>(a.cvals + cvals_off(p, KT, kt) + rb * 1024 + lane * 16) = v;
       *reinterpret_cast<uint16_t*>(a.cidx + cidx_off(p, KT, kt) + lane * 8 + rb * 2) = (uint16_t)code16;
       __builtin_amdgcn_raw_buffer_store_b32(bytes, dres, (uint32_t)(r16 * (K / 4) + 4 * q), kt * 16, 0);
+      }
     }
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
@@ -174,20 +179,25 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   if (a.ks == 1) {
     if (q == 0) {
       if (AMAX) a.ax[row] = axv;
-      if (COMPRESS) {
-        const float sv = sqrtf(nx2) / (sqrtf(nt2) + a.eps);
-        a.s[row] = sv;
-        if (a.dbg_s != nullptr && row_ok) a.dbg_s[row] = sv;
-      } else {
-        a.nx2[row] = nx2;
-      }
+      const float sv = scale_from_norms(nx2, nt2, a.eps);
+      a.s[row] = sv;
+      if (a.dbg_s != nullptr && row_ok) a.dbg_s[row] = sv;
     }
-    // T rows 4q + j of the block, column cb*16 + r16 (accumulator layout), rounded to bf16.
+    // T rows 4q + j of the block, column cb*16 + r16 (accumulator layout), rounded to bf16;
+    // with `fold`, T / s, the factor 1 / s of row 4q + j taken from lane 4q + j in double.
+    double inv[4] = {1.0, 1.0, 1.0, 1.0};
+    if (a.fold) {
+      const double iv = inv_scale_from_norms(nx2, nt2, a.eps);
+#pragma unroll
+      for (int j = 0; j < 4; j++) inv[j] = __shfl(iv, 4 * q + j, 64);
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(tacc[cb][j]);
+      for (int j = 0; j < 4; j++) {
+        const float t = a.fold ? (float)((double)tacc[cb][j] * inv[j]) : tacc[cb][j];
+        a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(t);
+      }
   } else {
     const int64_t Mp = (int64_t)gridDim.x * 16 * PW;
     if (q == 0) {
@@ -203,52 +213,30 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
 }
 
 // One item of the K-split reduction of prep_kernel's partials, summed in split order:
-// c < R/4 -> columns 4c..4c+3 of T (rounded to bf16); c == R/4 -> s (or ||X||^2 for the
-// prologue variant) and, for the FP8 layer, the row absmax.
-template <bool COMPRESS>
+// the row's squared norms (double) and, for c < R / 4, columns 4c..4c+3 of T (or of T / s
+// with `fold`), rounded to bf16; item c == 0 also writes s and, for the FP8 layer, the row
+// absmax.  A row has max(R / 4, 1) items.
 __device__ __forceinline__ void reduce_item(const PrepArgs& a, int64_t Mp, int64_t row, int64_t c) {
   const int64_t R = a.R;
-  if (c < R / 4) {
-    // Loads in batches of 8 (all in flight together), sums in split order.
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.ks; s0 += 8) {
-      f32x4 v[8];
+  double x2 = 0.0, t2 = 0.0;
+  for (int s0 = 0; s0 < a.ks; s0 += 8) {  // loads in batches of 8 (all in flight together)
+    double2 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const int sp = min(s0 + u, a.ks - 1);
-        v[u] = *reinterpret_cast<const f32x4*>(a.tpart + (sp * Mp + row) * R + 4 * c);
+    for (int u = 0; u < 8; u++) {
+      const int sp = min(s0 + u, a.ks - 1);
+      v[u] = *reinterpret_cast<const double2*>(a.npart + (sp * Mp + row) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (s0 + u < a.ks) {
+        x2 += v[u].x;
+        t2 += v[u].y;
       }
-#pragma unroll
-      for (int u = 0; u < 8; u++)
-        if (s0 + u < a.ks) t += v[u];
-    }
-    uint2 o;
-    o.x = pack_bf16x2(t[0], t[1]);
-    o.y = pack_bf16x2(t[2], t[3]);
-    *reinterpret_cast<uint2*>(a.T + row * R + 4 * c) = o;
-  } else {
-    float x2 = 0.f, t2 = 0.f;
-    for (int s0 = 0; s0 < a.ks; s0 += 8) {
-      float2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const int sp = min(s0 + u, a.ks - 1);
-        v[u] = *reinterpret_cast<const float2*>(a.npart + (sp * Mp + row) * 2);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; u++)
-        if (s0 + u < a.ks) {
-          x2 += v[u].x;
-          t2 += v[u].y;
-        }
-    }
-    if (COMPRESS) {
-      const float sv = sqrtf(x2) / (sqrtf(t2) + a.eps);
-      a.s[row] = sv;
-      if (a.dbg_s != nullptr && row < a.M) a.dbg_s[row] = sv;
-    } else {
-      a.nx2[row] = x2;
-    }
+  }
+  if (c == 0) {
+    const float sv = scale_from_norms(x2, t2, a.eps);
+    a.s[row] = sv;
+    if (a.dbg_s != nullptr && row < a.M) a.dbg_s[row] = sv;
     if (a.ax != nullptr) {  // FP8 layer: largest magnitude over the splits
       float m = 0.f;
       for (int s0 = 0; s0 < a.ks; s0 += 8) {
@@ -261,15 +249,37 @@ __device__ __forceinline__ void reduce_item(const PrepArgs& a, int64_t Mp, int64
       a.ax[row] = m;
     }
   }
+  if (c < R / 4) {
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.ks; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int sp = min(s0 + u, a.ks - 1);
+        v[u] = *reinterpret_cast<const f32x4*>(a.tpart + (sp * Mp + row) * R + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        if (s0 + u < a.ks) t += v[u];
+    }
+    if (a.fold) {
+      const double iv = inv_scale_from_norms(x2, t2, a.eps);
+#pragma unroll
+      for (int e = 0; e < 4; e++) t[e] = (float)((double)t[e] * iv);
+    }
+    uint2 o;
+    o.x = pack_bf16x2(t[0], t[1]);
+    o.y = pack_bf16x2(t[2], t[3]);
+    *reinterpret_cast<uint2*>(a.T + row * R + 4 * c) = o;
+  }
 }
 
-// The K-split reduction: one thread per (row, 4 columns of T) plus one per row for the norms.
-template <bool COMPRESS>
+// The K-split reduction: one thread per (row, 4 columns of T), or one per row when R == 0.
 __global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepArgs a, int64_t Mp) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // row * (R/4 + 1) + c
-  const int64_t per = a.R / 4 + 1;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // row * per + c
+  const int64_t per = a.R >= 4 ? a.R / 4 : 1;
   if (e >= Mp * per) return;
-  reduce_item<COMPRESS>(a, Mp, e / per, e % per);
+  reduce_item(a, Mp, e / per, e % per);
 }
 
 // FP8 layer: the 8-bit sparse operand from the pre-pass's bf16 operand.  Workgroup
@@ -292,10 +302,10 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const PrepArgs a, const P
   const int64_t p = blockIdx.y;
   const int KT = (int)(a.K / kBK), KT8 = (int)(a.K / 128);
   if (REDUCE) {
-    const int64_t per = a.R / 4 + 1, items = kPanel * per;
+    const int64_t per = a.R >= 4 ? a.R / 4 : 1, items = kPanel * per;
     const int64_t chunk = (items + KT8 - 1) / KT8;
     const int64_t i0 = kt * chunk, i1 = min(items, i0 + chunk);
-    for (int64_t it = i0 + tid; it < i1; it += 256) reduce_item<true>(a, Mp, p * kPanel + it / per, it % per);
+    for (int64_t it = i0 + tid; it < i1; it += 256) reduce_item(a, Mp, p * kPanel + it / per, it % per);
   }
   const int s = 2 * kt + (q >> 1);
   const int l0 = 16 * (2 * (q & 1)) + r, l1 = l0 + 16;
@@ -365,10 +375,9 @@ static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const 
   }
 #undef RTL_PREP
   if (sp.ks > 1 && reduce) {
-    const int64_t items = Mp * (R / 4 + 1);
+    const int64_t items = Mp * (R >= 4 ? R / 4 : 1);
     const dim3 rgrid((unsigned)((items + 255) / 256)), rblock(256);
-    if (comp) hipLaunchKernelGGL((prep_reduce_kernel<true>), rgrid, rblock, 0, stream, p, Mp);
-    else hipLaunchKernelGGL((prep_reduce_kernel<false>), rgrid, rblock, 0, stream, p, Mp);
+    hipLaunchKernelGGL(prep_reduce_kernel, rgrid, rblock, 0, stream, p, Mp);
   }
 }
 
@@ -400,15 +409,14 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   p.ks = sp.ks;
   p.kts = sp.kts;
   p.tpart = (float*)(base + L.tpart);
-  p.npart = (float*)(base + L.npart);
+  p.npart = (double*)(base + L.npart);
+  p.s = (float*)(base + L.norm);
+  p.dbg_s = dbg_s;
+  p.fold = lowrank_first_bf16(variant, M, N, K, R) ? 1 : 0;
   if (comp) {
-    p.s = (float*)(base + L.norm);
     p.cvals = base + L.cvals;
     p.cidx = base + L.cidx;
     p.dbg_idx = dbg_idx;
-    p.dbg_s = dbg_s;
-  } else {
-    p.nx2 = (float*)(base + L.norm);
   }
   launch_prep_kernels<false>(p, comp, Mp, sp, R, stream);
   return hipGetLastError();
@@ -428,7 +436,7 @@ hipError_t launch_prep_fp8(int64_t M, int64_t K, int64_t R, const void* X, const
   p.ks = sp.ks;
   p.kts = sp.kts;
   p.tpart = (float*)(base + F.L.tpart);
-  p.npart = (float*)(base + F.L.npart);
+  p.npart = (double*)(base + F.L.npart);
   p.s = (float*)(base + F.L.norm);
   p.cvals = base + F.L.cvals;
   p.cidx = base + F.L.cidx;

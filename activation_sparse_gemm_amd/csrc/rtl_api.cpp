@@ -45,8 +45,10 @@ rtl_status check_dtype(rtl_dtype dt) {
   return RTL_OK;
 }
 
+// eps guards the division by ||X~||; it is kept in [0, 1] so that s of any nonzero row whose
+// output is in the normal floating-point range is itself a normal fp32 number.
 rtl_status check_eps(float eps) {
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(RTL_ERR_ARG, "eps must be finite and >= 0");
+  if (!(eps >= 0.f && eps <= 1.f)) return fail(RTL_ERR_ARG, "eps must lie in [0, 1] (got %g)", (double)eps);
   return RTL_OK;
 }
 

@@ -87,14 +87,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// Squared-norm accumulation of two packed bf16 values.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
+// Squared-norm accumulation of the two bf16 values packed in d, in double precision: the
+// square of any finite bf16 (or fp32) value and sums of up to 2^40 of them stay inside the
+// double range, so no row norm underflows or overflows.
+__device__ __forceinline__ double sq2_f64(uint32_t d, double acc) {
+  const double lo = (double)bf16lo(d), hi = (double)bf16hi(d);
+  return fma(hi, hi, fma(lo, lo, acc));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// s = ||X|| / (||X~|| + eps) from the squared norms, in double precision, rounded to fp32;
+// an all-zero row (nx2 == 0, hence nt2 == 0) has s = 0.  For a nonzero row nt2 > 0
+// (the two largest magnitudes of some group are kept), so eps == 0 is allowed.
+__device__ __forceinline__ float scale_from_norms(double nx2, double nt2, float eps) {
+  return nx2 > 0.0 ? (float)(sqrt(nx2) / (sqrt(nt2) + (double)eps)) : 0.f;
+}
+// 1 / s in double precision (0 for an all-zero row): T / s stays in range for any row.
+__device__ __forceinline__ double inv_scale_from_norms(double nx2, double nt2, float eps) {
+  return nx2 > 0.0 ? (sqrt(nt2) + (double)eps) / sqrt(nx2) : 0.0;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;

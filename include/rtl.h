@@ -27,6 +27,11 @@
  *  - Selection compares magnitudes exactly (as integers on the sign-cleared bit
  *    patterns); ties go to the lower channel index; exactly two positions are kept in
  *    every group even when it holds fewer than two nonzeros.  Inputs must be finite.
+ *  - The squared row norms ||X||^2 and ||X~||^2 are summed in double precision and s is
+ *    formed in double precision and rounded to fp32, so no finite row underflows or
+ *    overflows them (s > 0 for every nonzero row).  The products (X~ W^T, X L_B^T and Y)
+ *    accumulate in fp32 and must lie in its range.
+ *  - eps must lie in [0, 1] (RTL_ERR_ARG otherwise); the method uses 1e-8.
  *  - Thread-safe: no global mutable state apart from the thread-local error message.
  */
 #ifndef RTL_H
@@ -45,7 +50,7 @@ typedef enum {
   RTL_ERR_SHAPE = 2,       /* M, N or K <= 0, K % 4 != 0, R < 0 */
   RTL_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned */
   RTL_ERR_UNSUPPORTED = 4, /* tie rule, dtype, or a shape limit of the bf16 kernels */
-  RTL_ERR_ARG = 5,         /* eps negative or not finite; an output overlaps an input */
+  RTL_ERR_ARG = 5,         /* eps outside [0, 1] or NaN; an output overlaps an input */
   RTL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   RTL_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
 } rtl_status;
@@ -76,17 +81,20 @@ size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int6
  *   X [M,K], W [N,K], LA [N,R], LB [R,K], Y [M,N]; R == 0 drops the low-rank branch
  *   (LA and LB may then be NULL).
  * bf16: a pre-pass over X forms the rank-R product T = X L_B^T (rounded to bf16), the
- *   row norms and (default variant) the 2-of-4 selection, packed as the compressed
+ *   row norms, s and (default variant) the 2-of-4 selection, packed as the compressed
  *   sparse-MFMA operand, in `workspace`; the sparse-MFMA GEMM then reads that operand
  *   (or, in the prologue variant, selects in its own A-operand prologue, see
- *   rtl_variant), and its epilogue scales the accumulators by s and adds T L_A^T into
- *   them with one extra K = R MFMA slice before the single bf16 store of Y.  Limits:
- *   K % 64 == 0, R % 32 == 0, R <= 128.  M and N are arbitrary.
+ *   rtl_variant), and its epilogue scales the accumulators by s and then adds T L_A^T
+ *   into them with one extra K = R MFMA slice before the single bf16 store of Y.  (GEMM
+ *   tilings that add the slice before their main loop read T / s, formed by the pre-pass
+ *   in double precision, and store s * acc: the same value in exact arithmetic.)
+ *   Limits: K % 64 == 0, R % 32 == 0, R <= 128.  M and N are arbitrary.
  * fp32: same arithmetic in fp32 on the vector ALUs (no fp32 sparse MFMA exists).
  * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the kernels
- *   write the selection codes and s they computed themselves (the pre-pass in the
- *   pre-compressed variant, the GEMM's prologue in the prologue variant, the fp32
- *   kernel in fp32), in the layout of rtl_sparsify.
+ *   write the selection codes and s they computed themselves, in the layout of
+ *   rtl_sparsify: the codes from the pre-pass in the pre-compressed variant, from the
+ *   GEMM's A-operand prologue in the prologue variant; s from the pre-pass in both;
+ *   both from the single kernel in fp32.
  * Y must not overlap any input.  Calls that share a workspace must be serialised.
  */
 rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
@@ -118,8 +126,9 @@ rtl_status rtl_linear_fused_ex(rtl_variant variant, rtl_dtype dt, int64_t M, int
  *   rtl_linear_fused_prep: the pre-pass over X into `workspace`;
  *   rtl_linear_fused_main: the GEMM with the epilogue, reading `workspace`.
  * Call them in this order on the same stream with the same variant, shape and workspace.
- * Each writes the optional dbg outputs it computes (the prologue variant's main launch,
- * the pre-compressed variant's prep launch).  Validation as for rtl_linear_fused.
+ * Each writes the optional dbg outputs it computes (s: the prep launch; selection codes:
+ * the prologue variant's main launch, the pre-compressed variant's prep launch).
+ * Validation as for rtl_linear_fused.
  */
 rtl_status rtl_linear_fused_prep(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K,
                                  int64_t R, const void* X, const void* LB, rtl_tie_rule tie, float eps,

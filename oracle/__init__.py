@@ -58,6 +58,8 @@ def _load():
         lib.orc_dense.restype = i32
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = i32
+        lib.orc_set_num_threads.argtypes = [i32]
+        lib.orc_set_num_threads.restype = None
         lib.orc_e4m3_value.argtypes = [i32]
         lib.orc_e4m3_value.restype = d
         lib.orc_e4m3_encode_array.argtypes = [i64, p, p]
@@ -89,6 +91,11 @@ def _check(rc: int):
 
 def num_threads() -> int:
     return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (for timing; the results do not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def select4(x, tie: int = TIE_LOWER) -> int:

@@ -90,6 +90,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads of the following parallel regions (timing only; results do not depend on it). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 static int orc_check_common(int dt, int64_t M, int64_t K, int tie) {
   if (dt != ORC_F32 && dt != ORC_BF16) return ORC_EARG;
   if (M < 0 || K <= 0 || K % 4 != 0) return ORC_EARG;

@@ -86,6 +86,7 @@ def test_sparsify_rejects_bad_calls():
         (dict(eps=-1.0), "RTL_ERR_ARG"),
         (dict(eps=float("nan")), "RTL_ERR_ARG"),
         (dict(eps=float("inf")), "RTL_ERR_ARG"),
+        (dict(eps=2.0), "RTL_ERR_ARG"),
         (dict(X=None), "RTL_ERR_NULL"),
         (dict(s=None), "RTL_ERR_NULL"),
     ]

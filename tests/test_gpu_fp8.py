@@ -3,11 +3,12 @@
 Weight codes and scales, and the activation codes and scales the pack kernel computes,
 are compared bit for bit: both sides form the value that decides each code in fp32 and
 round it to nearest even.  Y is compared against the oracle's fp64 FP8 layer within the
-bf16 contract tolerance (max row relative error 2e-2): in full on small shapes that span
-several tiles with ragged M and N tails (K from one 128-wide step to several loop
-periods, R = 0 to 128), and at the workload layers' full sizes on sampled rows, in the
-launch configuration of the default call (256 x 192 tiles on the attention shape,
-256 x 256 on the video layers).
+bf16 contract tolerance (2e-2 on the per-row relative L2 error and on the element-wise
+error max|Y - Yref| / max|Yref|): in full on small shapes that span several tiles with
+ragged M and N tails (K from one 128-wide step to several loop periods, R = 0 to 128),
+and at the workload layers' full sizes on rows of every 256-row output tile plus the
+whole last tile, in the launch configuration of the default call (256 x 192 tiles on the
+attention shape, 256 x 256 on the video layers).
 """
 import numpy as np
 import pytest
@@ -15,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from _gpu import TOL_Y, layer, log, row_rel_err, sample_rows, to_dev, to_host
+from _gpu import TOL_Y, check_y, layer, log, tile_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -56,9 +57,7 @@ def check_fp8(d, tag, rows=None, y_rows=None):
     assert np.array_equal(to_host(sx)[sel], sx_ref), "activation scale mismatch"
     Yg = synth.bf16_to_f32(to_host(Y))[sel].astype(np.float64)
     keep = np.ones(len(sel), bool) if y_rows is None else np.isin(sel, y_rows)
-    err = row_rel_err(Yg[keep], Yref[keep])
-    log(f"[fp8] {tag} max row rel err {err:.3e}")
-    assert err <= TOL_Y["bf16"], err
+    check_y(Yg[keep], Yref[keep], "bf16", f"fp8 {tag}")
     return Yg, Yref
 
 
@@ -76,7 +75,9 @@ def test_fp8_small_shapes(shape):
 
 def test_fp8_zero_tiny_and_tied_rows():
     """All-zero rows (sx = 0, Y = 0), rows whose largest magnitude is too small for an
-    fp32 448 / a (coded as zeros on both sides), and rows with exact magnitude ties."""
+    fp32 448 / a (coded as zeros on both sides: only the rank-R branch remains), rows far
+    below the usual scale (their fp32 squared norms would underflow; the kernels sum them
+    in double precision) and rows with exact magnitude ties."""
     M, K, N, R = 64, 256, 192, 32
     lay = synth.Layer("fp8t", M, K, N, R, "bf16", "heavy", 0.08)
     d = dict(synth.make_layer(lay, seed_base=7100))
@@ -88,10 +89,15 @@ def test_fp8_zero_tiny_and_tied_rows():
     X[20, :8] = [t, t, t, t, t, -t, t, -t]
     X[21, :8] = [t, -t, -t, t, 2 * t, t, t, 2 * t]
     d["X"] = synth.to_bf16(X)
-    # rows 10 and 11 are compared by their codes and scales only: their squared norms
-    # underflow fp32 (a limit of the bf16 layer's s as well), so s differs from fp64
-    Yg, Yref = check_fp8(d, "special rows", y_rows=[i for i in range(M) if i not in (10, 11)])
+    # Row 10's exact outputs (about 1e-40) lie below the smallest normal bf16 (1.2e-38),
+    # where bf16 resolves only multiples of 2^-133 (9.2e-41), so it cannot meet a relative
+    # bound; it is compared on its own with an absolute bound of a few such steps and is
+    # part of the element metric with the other rows.
+    Yg, Yref = check_fp8(d, "special rows", y_rows=[i for i in range(M) if i != 10])
     assert np.all(Yg[3] == 0)
+    assert np.max(np.abs(Yg - Yref)) <= TOL_Y["bf16"] * np.max(np.abs(Yref))
+    assert np.max(np.abs(Yg[10] - Yref[10])) <= 4 * 2.0 ** -133 + 2.0 ** -8 * np.max(np.abs(Yref[10]))
+    assert np.max(np.abs(Yref[10])) > 0 and np.max(np.abs(Yg[10])) > 0
 
 
 def test_fp8_exactly_quantisable_equals_bf16_layer():
@@ -128,8 +134,7 @@ def test_fp8_exactly_quantisable_equals_bf16_layer():
 @pytest.mark.parametrize("name", ["attn_proj", "fused_qkv", "mlp_down", "video_up"])
 def test_fp8_workload_layers(name):
     d = layer(name)
-    rows = sample_rows(d["M"], n=16 if d["M"] > 10000 else 24)
-    check_fp8(d, name, rows=rows)
+    check_fp8(d, name, rows=tile_rows(d["M"]))
 
 
 def test_fp8_workspace_reuse_and_streams():
@@ -148,6 +153,5 @@ def test_fp8_workspace_reuse_and_streams():
         Y2 = rtl.rtl_linear_fused_fp8(Xs, Wq, sw, LA, LB, workspace=ws, stream=side)
     side.synchronize()
     Yref, _ = oracle.linear_fp8(d["X"], Wq_ref, sw_ref, d["LA"], d["LB"])
-    e1 = row_rel_err(synth.bf16_to_f32(to_host(Y1)).astype(np.float64), Yref)
-    e2 = row_rel_err(synth.bf16_to_f32(to_host(Y2)).astype(np.float64), Yref[:300])
-    assert e1 <= TOL_Y["bf16"] and e2 <= TOL_Y["bf16"], (e1, e2)
+    check_y(synth.bf16_to_f32(to_host(Y1)).astype(np.float64), Yref, "bf16", "fp8 first call")
+    check_y(synth.bf16_to_f32(to_host(Y2)).astype(np.float64), Yref[:300], "bf16", "fp8 second call, side stream")

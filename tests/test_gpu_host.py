@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from _gpu import TOL_Y, f64, log, row_rel_err, sample_rows, to_dev, to_host
+from _gpu import TOL_Y, check_y, f64, log, sample_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +47,7 @@ def test_block_dispatch_matches_direct_calls():
             Yref, _ = oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
         else:
             Yref = f64(d["X"], "bf16")[rows] @ f64(d["W"], "bf16").T
-        err = row_rel_err(f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16"), Yref)
-        assert err <= TOL_Y["bf16"], (kind, err)
+        check_y(f64(to_host(Y[torch.from_numpy(rows).cuda()]), "bf16"), Yref, "bf16", kind)
     assert not block["attn.o_proj"].sparse and not block["mlp.down"].sparse
     assert block["attn.qkv"].sparse and block["mlp.up"].sparse
 
