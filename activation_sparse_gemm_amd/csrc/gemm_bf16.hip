@@ -9,9 +9,10 @@
 //                prologue, one K step ahead of the sparse MFMAs (s comes from the
 //                pre-pass, which also selects to form ||X~||).
 //    kModeDense: the dense product X W^T (v_mfma_f32_16x16x32_bf16), same tiling.
-//  Sparse modes run v_smfmac_f32_16x16x64_bf16; their epilogue scales the accumulators by
-//  s and then adds T L_A^T into them with an extra K = R MFMA slice before the single
-//  store, so the M x N low-rank product never reaches device memory.
+//  Sparse modes run v_smfmac_f32_16x16x64_bf16.  The rank-R branch goes into the same
+//  accumulators as one extra K = R MFMA slice with T / s (formed by the pre-pass in double
+//  precision) as its A operand, and the single store writes Y = s * acc; so the M x N
+//  low-rank product never reaches device memory, and s * (T / s) L_A^T = T L_A^T.
 #include "lora_lds.h"
 
 namespace rtl {
@@ -495,12 +496,10 @@ void gemm_kernel(const GemmArgs a) {
   }
 
   if (SPARSE) {
-    // Epilogue: acc *= s (row scale of the sparse product), then acc += T_tile L_A_tile^T
-    // (K = R in slices of 32), then one bf16 store.  s_row[rb] is the s of row 16rb + r16,
-    // the row this lane feeds as A operand.  Pre-compressed mode with R <= 64 first copies
-    // the tile's T, L_A and s into the (now free) W ring once per workgroup and takes the
-    // slice from there (loaded by every wave straight from memory they are a 192 KB burst
-    // per workgroup through L2).
+    // Epilogue: acc += (T / s)_tile L_A_tile^T (K = R in slices of 32), then Y = s * acc.
+    // Pre-compressed mode with R <= 64 first copies the tile's T / s, L_A and s into the
+    // (now free) W ring once per workgroup and takes the slice from there (loaded by every
+    // wave straight from memory they are a 192 KB burst per workgroup through L2).
     const bool lds_slice = MODE == kModeComp && a.R <= 64;
     if (lds_slice) {
       wait_vmcnt<0>();
@@ -508,15 +507,21 @@ void gemm_kernel(const GemmArgs a) {
       lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
       wait_vmcnt<0>();
       __syncthreads();
+      lora_slice_lds<NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
     }
+    // s of row 16rb + r16 (the row this lane feeds as A operand), then of the accumulator
+    // rows 16rb + 4q + j, held by lane 4q + j.
     float s_row[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       const int64_t row = m0 + 64 * wm + 16 * rb + r16;
       s_row[rb] = lds_slice ? lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16) : a.s[row < M ? row : M - 1];
     }
-    scale_rows<NB>(acc, s_row, lane);
-    if (lds_slice) lora_slice_lds<NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
+    float s_acc[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
     const int64_t R = a.R;
     for (int kk = 0; kk < (lds_slice ? 0 : (int)(R / 32)); kk++) {
       u32x4 ta[4];
@@ -535,10 +540,14 @@ void gemm_kernel(const GemmArgs a) {
               __builtin_bit_cast(bf16x8, ta[rb]), __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
       }
     }
+    __syncthreads();  // the LDS rings are free
+    store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
+                      [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
+    return;
   }
 
-  // Store Y (bf16, round to nearest even).  Lane holds column 16nb + r16 of its half, rows
-  // 16rb + 4q + j of its slab.
+  // Dense: store Y (bf16, round to nearest even).  Lane holds column 16nb + r16 of its
+  // half, rows 16rb + 4q + j of its slab.
   __syncthreads();  // the LDS rings are free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
                     [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
@@ -565,11 +574,10 @@ void half_kernel(const GemmArgs a) {
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
-  // take the rank-R branch first, from T / s (formed by the pre-pass), L_A and s staged in
-  // LDS past the ring; the final store multiplies by s.  The other widths stage only L_A
-  // there, at the start, and at the end scale the accumulators by s and then add T L_A^T
-  // with T from memory (two 128-wide workgroups, or one 256-wide one, then fill the 160 KB
-  // of LDS).
+  // take the rank-R branch first, from T / s, L_A and s staged in LDS past the ring.  The
+  // other widths stage only L_A there, at the start, and take the branch at the end with
+  // T / s from memory (two 128-wide workgroups, or one 256-wide one, then fill the 160 KB
+  // of LDS).  The single store writes Y = s * acc.
   constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = !LSTG;
   __shared__ __attribute__((aligned(1024)))
   uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : LAST ? TW * 128 : 0)];
@@ -712,16 +720,15 @@ void half_kernel(const GemmArgs a) {
     if (kt + j < KT) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
   wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
 
-  // Epilogue: s_row[rb] is the s of row 16rb + r16 (the row this lane feeds as A operand).
-  // Unless the rank-R slice was taken first (its T / s term then makes Y = s * acc), the
-  // accumulators are scaled by s and T L_A^T is added; then the single bf16 store.
+  // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
+  // accumulator rows 16rb + 4q + j (lane 4q + j); unless taken first, the rank-R slice
+  // acc += (T / s) L_A^T; then Y = s * acc.
   float s_row[4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
     const int64_t row = m0 + 64 * wave + 16 * rb + r16;
     s_row[rb] = lfirst ? lora_s_lds<TW>(lora, 64 * wave + 16 * rb + r16) : a.s[row < M ? row : M - 1];
   }
-  scale_rows<NB>(acc, s_row, lane);
   const int64_t R = a.R;
   for (int kk = 0; kk < (lfirst ? 0 : (int)(R / 32)); kk++) {
     u32x4 ta[4];
@@ -741,9 +748,14 @@ void half_kernel(const GemmArgs a) {
                                                               __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
     }
   }
+  float s_acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
   __syncthreads();  // the LDS ring is free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wave, n0, wl + wave * 16 * (2 * TW + 16), lane,
-                    [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
+                    [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
 }
 
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
@@ -770,12 +782,6 @@ static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
   const double full_cost = (double)((full + 255) / 256) * tn * (tn == 192 ? 1.05 : 1.0);
   const double half_cost = (double)((half + 255) / 256) * 128 * (K <= 4096 ? 0.95 : 1.08);
   return half_cost < full_cost;
-}
-
-bool lowrank_first_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R) {
-  // half_kernel<192> (192-wide pre-compressed tiles) takes the slice first for R <= 64
-  const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
-  return comp && R > 0 && R <= 64 && !use_half_tiles(M, N, K) && choose_tn(M, N) == 192;
 }
 
 template <int TN>

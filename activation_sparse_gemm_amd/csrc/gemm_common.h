@@ -30,7 +30,7 @@ struct GemmArgs {
   const uint16_t* X;
   const uint16_t* W;
   const uint16_t* LA;
-  const uint16_t* T;      // [Mp, R] bf16: T, or T / s for a slice taken before the main loop
+  const uint16_t* T;      // [Mp, R] bf16: T / s (bf16 layer) or T (FP8 layer)
   const float* s;         // [Mp]
   const uint8_t* cvals;   // pre-compressed mode
   const uint8_t* cidx;

@@ -6,7 +6,7 @@
 #include "gemm_common.h"
 
 namespace rtl {
-// Rank-R operands of one output tile staged in LDS (R <= 64): T [256][R] bf16 at +0, L_A
+// Rank-R operands of one output tile staged in LDS (R <= 64): T (or T / s) [256][R] bf16 at +0, L_A
 // [TW][R] bf16 at +kLoraT, s [256] f32 at +kLoraT + kLoraA.  Rows of T and L_A keep their
 // R / 8 16-byte chunks, chunk c of row r at position c ^ (r mod R / 8) (so the 16 rows that
 // a fragment read touches fall in different banks).  Loaded with 16-byte direct-to-LDS
@@ -57,8 +57,8 @@ __device__ __forceinline__ float lora_s_lds(const uint8_t* lora, int r) {
 }
 // acc[rb][nb] += T_rows L_A_cols^T from the staged copy, K = R in slices of 32: the lane
 // feeds tile row row0 + 16 rb + r16 and tile column col0 + 16 nb + r16.  The staged rows
-// hold T itself when the accumulators were already scaled by s, or T / s (formed by the
-// pre-pass in double precision) when the slice comes before the main loop.
+// hold T / s in the bf16 layer (formed by the pre-pass in double precision; the store then
+// writes s * acc) and T in the FP8 layer (whose accumulators are scaled first).
 template <int NB>
 __device__ __forceinline__ void lora_slice_lds(f32x4 (&acc)[4][NB], const uint8_t* lora, int R, int row0, int col0,
                                                int lane) {

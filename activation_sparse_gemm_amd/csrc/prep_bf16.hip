@@ -412,7 +412,7 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   p.npart = (double*)(base + L.npart);
   p.s = (float*)(base + L.norm);
   p.dbg_s = dbg_s;
-  p.fold = lowrank_first_bf16(variant, M, N, K, R) ? 1 : 0;
+  p.fold = 1;  // the bf16 GEMMs add (T / s) L_A^T and store s * acc
   if (comp) {
     p.cvals = base + L.cvals;
     p.cidx = base + L.cidx;

@@ -17,9 +17,6 @@ hipError_t launch_sparsify(int dt, int64_t M, int64_t K, const void* X, float ep
 // prologue, or in the pre-pass over X with the GEMM reading the compressed operand.
 constexpr int kVariantAuto = 0, kVariantPrologue = 1, kVariantPrecompressed = 2;
 int resolve_variant_bf16(int variant, int64_t M, int64_t N, int64_t K);
-// True when the GEMM that runs for this shape adds the rank-R slice before its main loop
-// and so reads T / s (formed by the pre-pass) instead of T.
-bool lowrank_first_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R);
 size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R);
 hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
                             float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream);

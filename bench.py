@@ -1,23 +1,29 @@
 """Benchmark of the norm-compensated 2:4 activation-sparse + low-rank linear layer.
 
-    python bench.py [--steps K] [--warmup W] [--layer attn_proj] [--all-layers] [--blocks]
+    python bench.py [--steps K] [--warmup W] [--workload video_block|<layer>] [--no-layers] [--blocks]
 
-One step = one rtl_linear_fused call (the whole hot path: the pre-pass over X that
-forms the rank-R product, the row norms and the compressed 2:4 operand, then the
-sparse-MFMA GEMM with the rescale + low-rank epilogue) on one batch of synthetic inputs
-already resident in HBM.  Prints ONE JSON line with the effective throughput
-(dense-equivalent 2MNK plus rank-R FLOPs per second), the speedup over the in-library
-dense GEMM of the same shape, the roofline position of the dominant kernel (timed alone
-with HIP events on the stream it runs on) and the CPU oracle timed on a bounded sample.
-Runs on one GPU only.
+Default step: one pass of the long-sequence video-DiT block, M = 32760 tokens: the up
+projection 5120 -> 13824 and the down projection 13824 -> 5120 through rtl_linear_fused
+(the whole hot path: the pre-pass over X that forms the rank-R product, the row norms,
+s and the compressed 2:4 operand, then the sparse-MFMA GEMM with the rescale + rank-R
+epilogue; R = 64), and the attention output projection 5120 -> 5120, a layer the method
+leaves dense, through rtl_linear_dense_ref.  Each layer has its own synthetic input
+(heavy-tailed rows, 5% large channels), resident in HBM before the timed region.
+
+Prints ONE JSON line: the block's effective throughput (dense-equivalent 2MNK plus the
+rank-R FLOPs per second), its speedup over the all-dense block (in-library dense GEMM,
+and the faster of that and torch.matmul per layer), the roofline position of the block's
+dominant kernel (timed alone with HIP events on the stream it runs on), the per-layer
+figures of every workload configuration, the fp32 Tiny layer's latency, and the CPU
+oracle timed on a bounded sample of the block.  Runs on one GPU only.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import re
 import os
+import re
 import sys
 import time
 
@@ -33,6 +39,12 @@ PEAK_FP8_DENSE = 5.0e15    # MI355X dense fp8 MFMA FLOP/s (published)
 KERNEL_SOURCES = ["activation_sparse_gemm_amd/csrc/gemm_bf16.hip", "activation_sparse_gemm_amd/csrc/gemm_common.h",
                   "activation_sparse_gemm_amd/csrc/bf16_common.h", "activation_sparse_gemm_amd/csrc/rtl_device.h",
                   "activation_sparse_gemm_amd/csrc/lora_lds.h"]
+METRIC = "effective TFLOP/s of fused 2:4 act-sparse+LoRA linear; speedup vs dense bf16"
+BLOCK = ("video_up", "video_down", "video_oproj")     # configuration 5
+OTHER_LAYERS = ("attn_proj", "fused_qkv", "mlp_up", "mlp_down")  # configurations 2-4
+# The summary page's own figures (NVIDIA H20, shapes and precision not stated): context only.
+PAGES_CONTEXT = {"hardware": "NVIDIA H20", "linear_layer_speedup_avg": 1.55, "sparsify_overhead_max_frac": 0.10,
+                 "end_to_end_speedup": [1.20, 1.24]}
 
 
 def _code_only(text: str) -> str:
@@ -53,27 +65,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(layer: str, variant: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{variant}_{layer}.json")
+def _traffic_record(layer: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_precompressed_{layer}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+        return json.load(f)
+
+
+def stored_traffic(layer: str):
+    """HBM bytes per launch of the layer's GEMM from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    t = _traffic_record(layer)
+    if t is None or t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
-
-
-def stored_kernel_name(layer: str, variant: str) -> str:
-    """Name of the GEMM kernel the committed counter summary was taken on (the kernel
-    the launcher picks for this layer), or a generic name when there is none."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{variant}_{layer}.json")
-    if not os.path.exists(path):
-        return "gemm_kernel"
-    with open(path) as f:
-        return str(json.load(f).get("kernel", "gemm_kernel"))
 
 
 def to_dev(a):
@@ -88,7 +94,7 @@ def to_dev(a):
 def time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.05) -> float:
     """Mean seconds per call of fn over `steps` calls after `warmup` calls (and at least
     `min_warm_s` seconds of them, so the clocks have settled), timed with events on the
-    current stream (the stream the library launches on)."""
+    current stream (the stream the library launches on), synchronised on both sides."""
     import torch
     t0 = time.perf_counter()
     n = 0
@@ -107,61 +113,175 @@ def time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.05) -> float:
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def cpu_baseline(d, target_s: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def layer_flops(lay) -> int:
+    """Metric FLOPs of one layer call: 2MNK (dense-equivalent) plus 2MR(K+N) of the rank-R
+    branch (R = 0 for a layer kept dense)."""
+    return lay.flops
+
+
+class LayerRun:
+    """One workload layer's inputs on the GPU and the calls the benchmark times."""
+
+    def __init__(self, name: str):
+        import torch
+
+        import activation_sparse_gemm_amd as rtl
+        import synth
+        self.name = name
+        self.lay = synth.LAYERS[name]
+        d = synth.make_layer(name)
+        self.M, self.K, self.N, self.R = d["M"], d["K"], d["N"], d["R"]
+        self.X, self.W, self.LA, self.LB = (to_dev(d[k]) for k in ("X", "W", "LA", "LB"))
+        self.host = d
+        self.Y = torch.empty((self.M, self.N), dtype=self.X.dtype, device="cuda")
+        self.dense_only = self.lay.dense_only
+        self.ws = None
+        if not self.dense_only:
+            dt = rtl.RTL_BF16 if self.lay.dtype == "bf16" else rtl.RTL_F32
+            need = rtl.rtl_linear_fused_workspace_bytes(dt, self.M, self.N, self.K, self.R)
+            self.ws = torch.empty((max(need, 1),), dtype=torch.uint8, device="cuda")
+        self.Wt = self.W.t()
+
+    def fused(self, variant=0):
+        import activation_sparse_gemm_amd as rtl
+        rtl.rtl_linear_fused(self.X, self.W, self.LA, self.LB, Y=self.Y, workspace=self.ws, variant=variant)
+
+    def prep(self):
+        import activation_sparse_gemm_amd as rtl
+        rtl.rtl_linear_fused_prep(self.X, self.LB, self.N, self.ws)
+
+    def main(self):
+        import activation_sparse_gemm_amd as rtl
+        rtl.rtl_linear_fused_main(self.X, self.W, self.LA, self.R, self.ws, Y=self.Y)
+
+    def dense(self):
+        import activation_sparse_gemm_amd as rtl
+        rtl.rtl_linear_dense_ref(self.X, self.W, Y=self.Y)
+
+    def torch_dense(self):
+        import torch
+        torch.matmul(self.X, self.Wt, out=self.Y)
+
+    def step(self):
+        """The layer as the method runs it: dense layers through the dense GEMM."""
+        self.dense() if self.dense_only else self.fused()
+
+    def times(self, steps: int, warmup: int, fp8: bool = False) -> dict:
+        """Seconds per call: the layer (default entry point), its two launches alone, the
+        in-library dense GEMM and torch.matmul of the same shape (and the FP8 layer)."""
+        import activation_sparse_gemm_amd as rtl
+        t = {"dense": time_loop(self.dense, steps, warmup), "torch": time_loop(self.torch_dense, steps, warmup)}
+        if not self.dense_only:
+            t["layer"] = time_loop(self.fused, steps, warmup)
+            t["prep"] = time_loop(self.prep, steps, warmup)
+            t["main"] = time_loop(self.main, steps, warmup)
+            t["prologue_variant"] = time_loop(lambda: self.fused(rtl.RTL_VARIANT_PROLOGUE), max(3, steps // 4), 2)
+            if fp8 and self.K % 128 == 0:
+                import torch
+                Wq, sw = rtl.rtl_quantize_weight_fp8(self.W)  # a static weight, quantised once
+                ws8 = torch.empty((rtl.rtl_linear_fused_fp8_workspace_bytes(self.M, self.N, self.K, self.R),),
+                                  dtype=torch.uint8, device="cuda")
+                t["fp8"] = time_loop(lambda: rtl.rtl_linear_fused_fp8(self.X, Wq, sw, self.LA, self.LB, Y=self.Y,
+                                                                      workspace=ws8), steps, warmup)
+                del Wq, sw, ws8
+        return t
+
+
+def prep_bytes(M: int, K: int, R: int) -> int:
+    """Algorithmic HBM bytes of the pre-pass (pre-compressed variant): read X and L_B; write
+    T (bf16), s, the kept values (K/2 bf16 per row) and their positions (K/16 bytes per row)."""
+    return M * K * 2 + R * K * 2 + M * R * 2 + M * 4 + M * (K // 2) * 2 + M * K // 16
+
+
+def gemm_alg_flops(M: int, N: int, K: int, R: int) -> int:
+    """Work of one sparse GEMM launch: the multiply-adds the 2:4 instruction really performs
+    (M N K / 2 of them, M N K FLOP) plus the rank-R slice 2 M R N, priced against the dense
+    bf16 MFMA peak: the 2:4 instruction retires real multiply-adds at the dense rate."""
+    return M * N * K + 2 * M * R * N
+
+
+def layer_line(run: LayerRun, t: dict) -> dict:
+    lay = run.lay
+    f = layer_flops(lay)
+    best = min(t["dense"], t["torch"])
+    line = {"M": run.M, "K": run.K, "N": run.N, "R": run.R,
+            "dense_ms": t["dense"] * 1e3, "torch_matmul_ms": t["torch"] * 1e3,
+            "dense_tflops": 2 * run.M * run.N * run.K / t["dense"] / 1e12}
+    if "layer" in t:
+        line.update(ms=t["layer"] * 1e3, tflops=f / t["layer"] / 1e12, frac_dense_peak=f / t["layer"] / PEAK_BF16_DENSE,
+                    speedup_vs_dense=t["dense"] / t["layer"], speedup_vs_best_dense=best / t["layer"],
+                    prep_us=t["prep"] * 1e6, gemm_us=t["main"] * 1e6, sparsify_overhead_frac=t["prep"] / t["layer"],
+                    prep_frac_hbm=prep_bytes(run.M, run.K, run.R) / t["prep"] / PEAK_HBM,
+                    gemm_frac_mfma=gemm_alg_flops(run.M, run.N, run.K, run.R) / t["main"] / PEAK_BF16_DENSE,
+                    prologue_variant_ms=t["prologue_variant"] * 1e3)
+        if "fp8" in t:
+            line["fp8"] = {"ms": t["fp8"] * 1e3, "tflops": f / t["fp8"] / 1e12,
+                           "speedup_vs_dense_bf16": t["dense"] / t["fp8"], "speedup_vs_bf16_layer": t["layer"] / t["fp8"],
+                           "frac_fp8_dense_peak": f / t["fp8"] / PEAK_FP8_DENSE}
+    return line
+
+
+def cpu_baseline(hosts, target_s: float) -> dict:
+    """The oracle (fp64, OpenMP over rows, all host threads) on an evenly spaced row sample
+    of every layer of the workload (`hosts`: (name, layer, host inputs) per layer), scaled
+    to TFLOP/s of the same metric; plus a single-thread time of a smaller sample for scale."""
     import oracle
-    M, K, N, R = d["M"], d["K"], d["N"], d["R"]
-    rows_per_probe = 16
+
+    def run_rows(rows):
+        for _, lay, d in hosts:
+            if lay.dense_only:
+                oracle.dense(d["X"], d["W"], rows=rows)
+            else:
+                oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+
+    M = hosts[0][2]["M"]
+    per_row = sum(layer_flops(lay) for _, lay, _ in hosts) / M
+    probe_rows = np.arange(16)
     t0 = time.perf_counter()
-    oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=np.arange(rows_per_probe))
+    run_rows(probe_rows)
     probe = time.perf_counter() - t0
-    nrows = int(min(M, max(rows_per_probe, rows_per_probe * target_s / max(probe, 1e-6))))
+    nrows = int(min(M, max(16, 16 * target_s / max(probe, 1e-6))))
     rows = np.linspace(0, M - 1, nrows).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.linear(d["X"], d["W"], d["LA"], d["LB"], rows=rows)
+    run_rows(rows)
     dt = time.perf_counter() - t0
-    flops = 2 * nrows * N * K + 2 * nrows * R * (K + N)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{nrows} of {M} rows (evenly spaced), full N={N} and K={K}, fp64, {dt:.1f} s"}
+    cores = oracle.num_threads()
+    out = {"value": per_row * nrows / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{nrows} of {M} evenly spaced rows of each of {', '.join(n for n, _, _ in hosts)} "
+                     f"(full N and K), fp64, {dt:.1f} s on {cores} threads"}
+    oracle.set_num_threads(1)
+    try:
+        rows1 = np.arange(4)
+        t0 = time.perf_counter()
+        run_rows(rows1)
+        dt1 = time.perf_counter() - t0
+        out["single_thread"] = {"value": per_row * len(rows1) / dt1 / 1e12, "unit": "TFLOP/s",
+                                "sample": f"{len(rows1)} rows of each layer, {dt1:.1f} s"}
+    finally:
+        oracle.set_num_threads(cores)
+    return out
 
 
-VARIANTS = {"prologue": 1, "precompressed": 2}
-AUTO_RESOLVES_TO = "precompressed"   # what RTL_VARIANT_AUTO runs on gfx950 (include/rtl.h)
-
-
-def bench_layer(name: str, steps: int, warmup: int, variants=("prologue", "precompressed")):
-    """Times (seconds per call) of the whole layer through the default entry point
-    (rtl_linear_fused, variant AUTO), of each explicit variant whole and of its two
-    launches alone, and of the dense GEMM of the same shape."""
-    import torch
-
-    import activation_sparse_gemm_amd as rtl
-    import synth
-    d = synth.make_layer(name)
-    M, K, N, R = d["M"], d["K"], d["N"], d["R"]
-    X, W, LA, LB = (to_dev(d[k]) for k in ("X", "W", "LA", "LB"))
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    t = {"dense": time_loop(lambda: rtl.rtl_linear_dense_ref(X, W, Y=Yd), steps, warmup)}
-    # the vendor library's dense GEMM of the same shape (torch.matmul -> hipBLASLt), for context
-    Wt = W.t()
-    t["dense_torch"] = time_loop(lambda: torch.matmul(X, Wt, out=Yd), steps, warmup)
-    if synth.LAYERS[name].dense_only:
-        return d, t
-    ws = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R),), dtype=torch.uint8,
-                     device="cuda")
-    t["auto"] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws), steps, warmup)
-    if K % 128 == 0:
-        # FP8 variant: the weight is quantised once (a static weight), outside the timed calls
-        Wq, sw = rtl.rtl_quantize_weight_fp8(W)
-        ws8 = torch.empty((rtl.rtl_linear_fused_fp8_workspace_bytes(M, N, K, R),), dtype=torch.uint8, device="cuda")
-        t["fp8"] = time_loop(lambda: rtl.rtl_linear_fused_fp8(X, Wq, sw, LA, LB, Y=Y, workspace=ws8), steps, warmup)
-    for vn in variants:
-        v = VARIANTS[vn]
-        t[vn] = time_loop(lambda: rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws, variant=v), steps, warmup)
-        t[vn + "_prep"] = time_loop(lambda: rtl.rtl_linear_fused_prep(X, LB, N, ws, variant=v), steps, warmup)
-        t[vn + "_main"] = time_loop(lambda: rtl.rtl_linear_fused_main(X, W, LA, R, ws, variant=v, Y=Y), steps,
-                                    warmup)
-    return d, t
+def tiny_latency(steps: int, warmup: int) -> dict:
+    """The fp32 Tiny layer (latency-bound): microseconds per call of the fused layer and of
+    the dense product."""
+    run = LayerRun("tiny")
+    t_f = time_loop(run.fused, max(steps, 50), warmup)
+    t_d = time_loop(run.dense, max(steps, 50), warmup)
+    return {"workload": f"tiny: M={run.M} K={run.K} N={run.N} R={run.R}, fp32", "us": t_f * 1e6,
+            "dense_us": t_d * 1e6, "tflops": layer_flops(run.lay) / t_f / 1e12}
 
 
 # Projections of one block of a 1024x1024 text-to-image DiT (hidden 3072, MLP 12288, 4096
@@ -205,16 +325,6 @@ def bench_blocks(steps: int, warmup: int) -> dict:
     return {"M": BLOCK_M, "layers": per, "all_dense_ms": dense, "all_torch_matmul_ms": torch_ms, "models": models}
 
 
-def prep_bytes(M: int, K: int, R: int, variant: str) -> int:
-    """Algorithmic HBM bytes of the pre-pass: read X and L_B, write T (bf16) and one float
-    per row; the pre-compressed variant also writes the kept values (K/2 bf16 per row) and
-    their positions (K/16 bytes per row)."""
-    b = M * K * 2 + R * K * 2 + M * R * 2 + M * 4
-    if variant == "precompressed":
-        b += M * (K // 2) * 2 + M * K // 16
-    return b
-
-
 def copy_calibration(mib: int):
     """A plain device copy of known size, for scaling the HBM byte counters of a profile
     run: each launch reads and writes exactly `mib` MiB."""
@@ -230,14 +340,13 @@ def copy_calibration(mib: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layer", default="attn_proj")
-    ap.add_argument("--variant", default="auto", choices=["auto", *sorted(VARIANTS)],
-                    help="entry point timed as the step (auto = rtl_linear_fused's own pick)")
-    ap.add_argument("--all-layers", action="store_true", help="also time every bf16 layer (one line each, stderr)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_block",
+                    help="video_block (default: configuration 5) or one layer name, timed alone as the step")
+    ap.add_argument("--no-layers", action="store_true", help="skip the per-layer figures of configurations 1-4")
     ap.add_argument("--blocks", action="store_true",
-                    help="also time a DiT block's four projections under each model's layer policy")
+                    help="also time a text-to-image DiT block's four projections under each model's layer policy")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -251,84 +360,86 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
-    import synth
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
-    d, t = bench_layer(args.layer, args.steps, args.warmup)
-    M, K, N, R = d["M"], d["K"], d["N"], d["R"]
-    variant = args.variant
-    kernel_variant = AUTO_RESOLVES_TO if variant == "auto" else variant
-    flops = synth.LAYERS[args.layer].flops
-    t_step = t[variant]
-    value = flops / t_step / 1e12
-    # Dominant kernel = the GEMM launch of the variant that runs.  Algorithmic work per
-    # launch: the multiply-adds the sparse instruction really performs (M N K / 2 of them,
-    # i.e. M N K FLOP) plus the rank-R slice 2 M R N, priced against the dense bf16 MFMA
-    # peak: the 2:4 instruction retires real multiply-adds at the dense instruction's rate
-    # (twice the dense-equivalent rate).
-    t_main = t[kernel_variant + "_main"]
-    alg_flops = M * N * K + 2 * M * R * N
-    achieved = alg_flops / t_main
-    roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_DENSE / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_DENSE, "traffic": stored_traffic(args.layer, kernel_variant),
-                "kernel": f"{stored_kernel_name(args.layer, kernel_variant)} (GEMM, {kernel_variant} operand), "
-                          f"{t_main * 1e6:.1f} us per launch",
-                "flop_per_launch": alg_flops}
-    pbytes = prep_bytes(M, K, R, kernel_variant)
-    t_prep = t[kernel_variant + "_prep"]
+    names = BLOCK if args.workload == "video_block" else (args.workload,)
+    runs = [LayerRun(n) for n in names]
+    M = runs[0].M
+
+    def step():
+        for r in runs:
+            r.step()
+
+    def dense_step():
+        for r in runs:
+            r.dense()
+
+    def torch_step():
+        for r in runs:
+            r.torch_dense()
+
+    # the timed step: exactly `warmup` untimed passes, then exactly `steps` passes
+    t_step = time_loop(step, args.steps, args.warmup, min_warm_s=0.0)
+    t_dense = time_loop(dense_step, args.steps, args.warmup)
+    t_torch = time_loop(torch_step, args.steps, args.warmup)
+    per = {r.name: r.times(max(5, args.steps // 2), 3, fp8=True) for r in runs}
+    best_dense = sum(min(per[r.name]["dense"], per[r.name]["torch"]) for r in runs)
+    flops = sum(layer_flops(r.lay) for r in runs)
+    value = flops / t_step
+
+    # dominant kernel: the slowest GEMM launch of the step's sparse layers
+    sparse_runs = [r for r in runs if not r.dense_only]
+    dom = max(sparse_runs, key=lambda r: per[r.name]["main"])
+    t_main = per[dom.name]["main"]
+    alg = gemm_alg_flops(dom.M, dom.N, dom.K, dom.R)
+    rec = _traffic_record(dom.name) or {}
+    roofline = {"bound": "mfma", "achieved": alg / t_main / 1e12, "peak": PEAK_BF16_DENSE / 1e12, "unit": "TFLOP/s",
+                "frac": alg / t_main / PEAK_BF16_DENSE, "traffic": stored_traffic(dom.name),
+                "kernel": f"{rec.get('kernel', 'sparse GEMM')} ({dom.name} GEMM launch), {t_main * 1e6:.1f} us",
+                "flop_per_launch": alg}
+    pb = prep_bytes(dom.M, dom.K, dom.R)
+    t_prep = per[dom.name]["prep"]
+    wl = ("video-DiT block (configuration 5): M=32760 tokens; up 5120->13824 and down 13824->5120 through the "
+          "fused 2:4 + rank-64 layer, o_proj 5120->5120 dense; bf16, heavy-tailed activations (5% large channels)"
+          if args.workload == "video_block" else
+          f"{dom.name}: M={dom.M} K={dom.K} N={dom.N} R={dom.R}, bf16")
     out = {
-        "metric": "effective TFLOP/s of fused 2:4 act-sparse+LoRA linear; speedup vs dense bf16",
-        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.layer}: M={M} K={K} N={N} R={R}, bf16, heavy-tailed activations",
-                   "M": M, "K": K, "N": N, "R": R, "variant": variant},
-        "speedup_vs_dense": t["dense"] / t_step,
-        "dense_tflops": 2 * M * N * K / t["dense"] / 1e12,
-        "dense_ms": t["dense"] * 1e3,
-        "torch_matmul_ms": t["dense_torch"] * 1e3,
-        "speedup_vs_torch_matmul": t["dense_torch"] / t_step,
-        "frac_dense_peak": value * 1e12 / PEAK_BF16_DENSE,
-        "frac_sparse_peak": value * 1e12 / PEAK_BF16_SPARSE,
-        "variants_ms": {vn: t[vn] * 1e3 for vn in ("auto", *VARIANTS)},
-        "prep": {"variant": kernel_variant, "us": t_prep * 1e6, "bound": "hbm", "bytes": pbytes,
-                 "achieved_GBps": pbytes / t_prep / 1e9, "frac": pbytes / t_prep / PEAK_HBM},
+        "metric": METRIC, "value": value / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "M": M, "layers": {r.name: {"K": r.K, "N": r.N, "R": r.R,
+                                                               "path": "dense" if r.dense_only else "fused"}
+                                                      for r in runs}},
+        "speedup_vs_dense": t_dense / t_step,
+        "speedup_vs_best_dense": best_dense / t_step,
+        "dense_step_ms": t_dense * 1e3, "torch_matmul_step_ms": t_torch * 1e3, "best_dense_step_ms": best_dense * 1e3,
+        "frac_dense_peak": value / PEAK_BF16_DENSE, "frac_sparse_peak": value / PEAK_BF16_SPARSE,
+        "step_layers": {r.name: layer_line(r, per[r.name]) for r in runs},
+        "prep": {"layer": dom.name, "us": t_prep * 1e6, "bound": "hbm", "bytes": pb,
+                 "achieved_GBps": pb / t_prep / 1e9, "frac": pb / t_prep / PEAK_HBM},
         "roofline": roofline,
+        "pages_context": PAGES_CONTEXT,
     }
-    if "fp8" in t:
-        # FP8 (E4M3) variant of the same layer: context beside the bf16 line, not its value
-        out["fp8_variant"] = {"ms": t["fp8"] * 1e3, "tflops": flops / t["fp8"] / 1e12,
-                              "speedup_vs_dense_bf16": t["dense"] / t["fp8"], "speedup_vs_bf16_sparse": t_step / t["fp8"],
-                              "frac_fp8_dense_peak": flops / t["fp8"] / PEAK_FP8_DENSE}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
-    if args.all_layers:
-        layers = []
-        for name, lay in synth.LAYERS.items():
-            if lay.dtype != "bf16":
-                continue
-            dl, tl = bench_layer(name, max(5, args.steps // 5), 3)
-            line = {"layer": name, "M": lay.M, "K": lay.K, "N": lay.N, "R": lay.R,
-                    "dense_ms": tl["dense"] * 1e3, "dense_tflops": 2 * lay.M * lay.N * lay.K / tl["dense"] / 1e12,
-                    "torch_matmul_ms": tl["dense_torch"] * 1e3}
-            if "fp8" in tl:
-                line["fp8"] = {"ms": tl["fp8"] * 1e3, "tflops": lay.flops / tl["fp8"] / 1e12,
-                               "speedup": tl["dense"] / tl["fp8"], "speedup_vs_bf16_sparse": tl["auto"] / tl["fp8"]}
-            for vn in ("auto", *VARIANTS):
-                if vn in tl:
-                    line[vn] = {"ms": tl[vn] * 1e3, "tflops": lay.flops / tl[vn] / 1e12,
-                                "speedup": tl["dense"] / tl[vn], "speedup_vs_torch": tl["dense_torch"] / tl[vn]}
-                    if vn != "auto":
-                        line[vn].update(prep_us=tl[vn + "_prep"] * 1e6, main_us=tl[vn + "_main"] * 1e6)
-            print(json.dumps(line), file=sys.stderr, flush=True)
-            layers.append(line)
-            del dl
+    hosts = [(r.name, r.lay, r.host) for r in runs]
+    if args.workload == "video_block" and not args.no_layers:
+        del runs
+        torch.cuda.empty_cache()
+        layers = {}
+        for name in OTHER_LAYERS:
+            r = LayerRun(name)
+            layers[name] = layer_line(r, r.times(max(5, args.steps // 2), 3, fp8=True))
+            print(json.dumps({name: layers[name]}), file=sys.stderr, flush=True)
+            del r
             torch.cuda.empty_cache()
         out["layers"] = layers
+        out["tiny"] = tiny_latency(args.steps, args.warmup)
+        runs = None
     if args.blocks:
-        out["blocks"] = bench_blocks(max(5, args.steps // 5), 3)
+        out["blocks"] = bench_blocks(max(5, args.steps // 4), 3)
         print(json.dumps(out["blocks"]), file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(hosts, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -84,11 +84,12 @@ size_t rtl_linear_fused_workspace_bytes(rtl_dtype dt, int64_t M, int64_t N, int6
  *   row norms, s and (default variant) the 2-of-4 selection, packed as the compressed
  *   sparse-MFMA operand, in `workspace`; the sparse-MFMA GEMM then reads that operand
  *   (or, in the prologue variant, selects in its own A-operand prologue, see
- *   rtl_variant), and its epilogue scales the accumulators by s and then adds T L_A^T
- *   into them with one extra K = R MFMA slice before the single bf16 store of Y.  (GEMM
- *   tilings that add the slice before their main loop read T / s, formed by the pre-pass
- *   in double precision, and store s * acc: the same value in exact arithmetic.)
- *   Limits: K % 64 == 0, R % 32 == 0, R <= 128.  M and N are arbitrary.
+ *   rtl_variant).  The rank-R branch enters the same accumulators as one extra K = R
+ *   MFMA slice with T / s as its A operand (formed by the pre-pass in double precision
+ *   from the fp32 T and the double-precision norms, then rounded to bf16; 0 for an
+ *   all-zero row), and the single bf16 store writes Y = s * acc, so s multiplies the
+ *   sparse product and cancels on the rank-R product.  Limits: K % 64 == 0, R % 32 == 0,
+ *   R <= 128.  M and N are arbitrary.
  * fp32: same arithmetic in fp32 on the vector ALUs (no fp32 sparse MFMA exists).
  * dbg_idx [M,K/4] and dbg_s [M] are optional (NULL to skip): when given, the kernels
  *   write the selection codes and s they computed themselves, in the layout of
