@@ -21,8 +21,8 @@ import torch
 __all__ = [
     "RTL_F32", "RTL_BF16", "RTL_TIE_LOWER_INDEX", "EPS", "RtlError", "lib", "library_path",
     "rtl_sparsify", "rtl_linear_fused", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused_ex",
-    "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref",
-    "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
+    "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_fused_noalloc", "rtl_linear_dense_ref",
+    "RTL_NOALLOC_SCRATCH_BYTES", "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
     "rtl_status_string", "rtl_version",
     "rtl_quantize_weight_fp8", "rtl_linear_fused_fp8", "rtl_linear_fused_fp8_workspace_bytes",
 ]
@@ -34,12 +34,14 @@ RTL_F32, RTL_BF16 = 0, 1
 RTL_TIE_LOWER_INDEX = 0
 RTL_VARIANT_AUTO, RTL_VARIANT_PROLOGUE, RTL_VARIANT_PRECOMPRESSED = 0, 1, 2
 EPS = 1e-8
+RTL_NOALLOC_SCRATCH_BYTES = 128 << 20  # include/rtl.h
 STATUS = {0: "RTL_OK", 1: "RTL_ERR_NULL", 2: "RTL_ERR_SHAPE", 3: "RTL_ERR_ALIGN", 4: "RTL_ERR_UNSUPPORTED",
           5: "RTL_ERR_ARG", 6: "RTL_ERR_WORKSPACE", 7: "RTL_ERR_HIP"}
 
 # Every entry point include/rtl.h declares.
 EXPORTS = ["rtl_sparsify", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused", "rtl_linear_fused_ex",
-           "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_dense_ref", "rtl_quantize_weight_fp8",
+           "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_fused_noalloc", "rtl_linear_dense_ref",
+           "rtl_quantize_weight_fp8",
            "rtl_linear_fused_fp8_workspace_bytes", "rtl_linear_fused_fp8", "rtl_status_string",
            "rtl_last_error", "rtl_version"]
 
@@ -67,6 +69,8 @@ def _load() -> ctypes.CDLL:
     L.rtl_linear_fused_prep.restype = i32
     L.rtl_linear_fused_main.argtypes = [i32, i32, i64, i64, i64, i64, p, p, p, i32, f32, p, p, sz, p, p, p]
     L.rtl_linear_fused_main.restype = i32
+    L.rtl_linear_fused_noalloc.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, p, p]
+    L.rtl_linear_fused_noalloc.restype = i32
     L.rtl_linear_dense_ref.argtypes = [i32, i64, i64, i64, p, p, p, p]
     L.rtl_linear_dense_ref.restype = i32
     L.rtl_quantize_weight_fp8.argtypes = [i64, i64, p, p, p, p]
@@ -194,6 +198,21 @@ def rtl_linear_fused_main(X: torch.Tensor, W: torch.Tensor, LA, R: int, workspac
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.rtl_linear_fused_main(variant, _dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), tie, eps, _ptr(Y),
                                      _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
+    return Y
+
+
+def rtl_linear_fused_noalloc(X: torch.Tensor, W: torch.Tensor, LA, LB, tie: int = RTL_TIE_LOWER_INDEX,
+                             eps: float = EPS, Y=None, dbg_idx=None, dbg_s=None, stream=None) -> torch.Tensor:
+    """rtl_linear_fused with the library's own per-GPU workspace (no allocation in the
+    call; pass ``Y`` to keep the whole call allocation-free).  Calls that overlap on one
+    GPU share that workspace and must be serialised by the caller."""
+    M, K = X.shape
+    N = W.shape[0]
+    R = 0 if LB is None else LB.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _check(lib.rtl_linear_fused_noalloc(_dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
+                                        _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
     return Y
 
 

@@ -113,11 +113,13 @@ namespace {
 
 enum Stage { kWhole = 0, kPrep = 1, kMain = 2 };
 
-// Validation shared by rtl_linear_fused{,_ex,_prep,_main}.  Pointers a stage does not use
-// are ignored (prep: W, LA, Y; main: LB).
+// Validation shared by rtl_linear_fused{,_ex,_prep,_main,_noalloc}.  Pointers a stage does
+// not use are ignored (prep: W, LA, Y; main: LB).  `own_ws`: the library's scratch array
+// is the workspace (the caller passes none), checked against its size instead.
 rtl_status check_fused(Stage stage, rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
                        const void* X, const void* W, const void* LA, const void* LB, rtl_tie_rule tie, float eps,
-                       const void* Y, const void* ws, size_t ws_bytes, const void* dbg_idx, const void* dbg_s) {
+                       const void* Y, const void* ws, size_t ws_bytes, const void* dbg_idx, const void* dbg_s,
+                       bool own_ws = false) {
   rtl_status st;
   if ((st = check_dtype(dt)) != RTL_OK) return st;
   if (variant != RTL_VARIANT_AUTO && variant != RTL_VARIANT_PROLOGUE && variant != RTL_VARIANT_PRECOMPRESSED)
@@ -156,6 +158,14 @@ rtl_status check_fused(Stage stage, rtl_variant variant, rtl_dtype dt, int64_t M
   if (overlap(Yc, yb, dbg_idx, ib) || overlap(Yc, yb, dbg_s, sb) || overlap(dbg_idx, ib, dbg_s, sb) ||
       overlap(ws, need, Yc, yb) || overlap(ws, need, dbg_idx, ib) || overlap(ws, need, dbg_s, sb))
     return fail(RTL_ERR_ARG, "outputs overlap each other or the workspace");
+  if (own_ws) {
+    if (need > rtl::noalloc_scratch_bytes())
+      return fail(RTL_ERR_WORKSPACE,
+                  "this shape needs %zu bytes of workspace; the allocation-free entry point has %zu (use "
+                  "rtl_linear_fused with a caller-owned workspace)",
+                  need, rtl::noalloc_scratch_bytes());
+    return RTL_OK;
+  }
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(RTL_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
   return RTL_OK;
@@ -187,6 +197,26 @@ rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64
                             size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream) {
   return rtl_linear_fused_ex(RTL_VARIANT_AUTO, dt, M, N, K, R, X, W, LA, LB, tie, eps, Y, workspace, ws_bytes, dbg_idx,
                              dbg_s, stream);
+}
+
+rtl_status rtl_linear_fused_noalloc(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R, const void* X,
+                                    const void* W, const void* LA, const void* LB, rtl_tie_rule tie, float eps,
+                                    void* Y, uint8_t* dbg_idx, float* dbg_s, void* stream) {
+  rtl_status st = check_fused(kWhole, RTL_VARIANT_AUTO, dt, M, N, K, R, X, W, LA, LB, tie, eps, Y, nullptr, 0,
+                              dbg_idx, dbg_s, true);
+  if (st != RTL_OK) return st;
+  void* ws = nullptr;
+  int mismatch = 0;
+  hipError_t e = rtl::noalloc_scratch((hipStream_t)stream, &ws, &mismatch);
+  if (e != hipSuccess) return hip_status(e, "rtl_linear_fused_noalloc scratch address");
+  if (mismatch) return fail(RTL_ERR_ARG, "the stream must belong to the current device");
+  if (dt == RTL_BF16)
+    e = rtl::launch_fused_bf16(RTL_VARIANT_AUTO, M, N, K, R, X, W, LA, LB, eps, Y, ws, dbg_idx, dbg_s,
+                               (hipStream_t)stream);
+  else
+    e = rtl::launch_fused_f32(M, N, K, R, (const float*)X, (const float*)W, (const float*)LA, (const float*)LB, eps,
+                              (float*)Y, ws, dbg_idx, dbg_s, (hipStream_t)stream);
+  return hip_status(e, "rtl_linear_fused_noalloc launch");
 }
 
 rtl_status rtl_linear_fused_prep(rtl_variant variant, rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,

@@ -38,6 +38,11 @@ hipError_t launch_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const vo
                             const float* sw, const void* LA, const void* LB, float eps, void* Y, void* ws,
                             uint8_t* dbg_xq, float* dbg_sx, hipStream_t stream);
 
+// Allocation-free workspace: the per-device scratch array (noalloc.hip).  `mismatch` is set
+// when `stream` does not belong to the current device (no address is resolved then).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t stream, void** out, int* mismatch);
+
 // fp32 path
 size_t fused_f32_workspace(int64_t M, int64_t N, int64_t K, int64_t R);
 hipError_t launch_fused_f32(int64_t M, int64_t N, int64_t K, int64_t R, const float* X,

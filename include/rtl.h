@@ -141,6 +141,25 @@ rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, i
                                  size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream);
 
 /*
+ * rtl_linear_fused without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and result as rtl_linear_fused (variant AUTO) minus the
+ * workspace: the library keeps its own, a device array of RTL_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, held from the library's load on that GPU until the process ends; the
+ * call allocates nothing.  Shapes whose rtl_linear_fused_workspace_bytes exceed it are
+ * rejected with RTL_ERR_WORKSPACE (it covers, e.g., M = 4608 with K = 12288).  `stream`
+ * must belong to the current device (RTL_ERR_ARG otherwise).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race, and the caller must serialise them.  The array keeps the last call's
+ * intermediate results; nothing in it needs to start at zero.
+ */
+#define RTL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+rtl_status rtl_linear_fused_noalloc(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
+                                    const void* X, const void* W, const void* LA, const void* LB,
+                                    rtl_tie_rule tie, float eps, void* Y, uint8_t* dbg_idx,
+                                    float* dbg_s, void* stream);
+
+/*
  * Dense product Y = X W^T with the same tiling as the fused kernel: the layer the sparse
  * one replaces and the one that layers left dense keep (method step 3, selective layer
  * skipping).  X [M,K], W [N,K], Y [M,N].  bf16 needs K % 64 == 0.

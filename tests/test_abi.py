@@ -146,6 +146,29 @@ def test_fused_rejects_bad_calls():
         assert h.untouched()
 
 
+def test_noalloc_validates_before_touching_the_device():
+    """rtl_linear_fused_noalloc: the usual argument errors, and a shape whose workspace
+    exceeds the library's scratch array, are rejected by host-side validation (no HIP call,
+    so this runs without a GPU).  Far-apart fake addresses stand in for device buffers."""
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    L = rtl.lib
+    fake = [ctypes.c_void_p((i + 1) << 40) for i in range(5)]
+    X, W, LA, LB, Y = fake
+    M, N, K, R = 32760, 5120, 13824, 64
+    assert rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R) > rtl.RTL_NOALLOC_SCRATCH_BYTES
+    assert L.rtl_linear_fused_noalloc(rtl.RTL_BF16, M, N, K, R, X, W, LA, LB, 0, 1e-8, Y, None, None,
+                                      None) == inv["RTL_ERR_WORKSPACE"]
+    assert "allocation-free" in rtl.lib.rtl_last_error().decode()
+    assert L.rtl_linear_fused_noalloc(rtl.RTL_BF16, 64, 64, 100, 0, X, W, None, None, 0, 1e-8, Y, None, None,
+                                      None) == inv["RTL_ERR_UNSUPPORTED"]
+    assert L.rtl_linear_fused_noalloc(rtl.RTL_BF16, 64, 64, 128, 32, X, W, None, LB, 0, 1e-8, Y, None, None,
+                                      None) == inv["RTL_ERR_NULL"]
+    assert L.rtl_linear_fused_noalloc(rtl.RTL_BF16, 64, 64, 128, 32, X, W, LA, LB, 0, 2.0, Y, None, None,
+                                      None) == inv["RTL_ERR_ARG"]
+    assert L.rtl_linear_fused_noalloc(rtl.RTL_BF16, 64, 64, 128, 32, X, W, LA, LB, 0, 1e-8, X, None, None,
+                                      None) == inv["RTL_ERR_ARG"]  # Y aliases X
+
+
 def test_fused_variant_and_stage_checks():
     inv = {v: k for k, v in rtl.STATUS.items()}
     h = Host()
