@@ -122,6 +122,23 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _torch_stream(stream):
+    if stream is None or isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream))
+
+
+def _empty(shape, dtype, device, stream):
+    """A tensor allocated on the stream the call runs on (torch's current stream when
+    `stream` is None), so that torch's caching allocator does not give its memory to other
+    work before that stream is done with it."""
+    ts = _torch_stream(stream)
+    if ts is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(ts):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -136,11 +153,11 @@ def rtl_sparsify(X: torch.Tensor, tie: int = RTL_TIE_LOWER_INDEX, eps: float = E
     the caller are written in place."""
     M, K = X.shape
     if vals is None:
-        vals = torch.empty((M, K // 2), dtype=X.dtype, device=X.device)
+        vals = _empty((M, K // 2), X.dtype, X.device, stream)
     if idx is None:
-        idx = torch.empty((M, K // 4), dtype=torch.uint8, device=X.device)
+        idx = _empty((M, K // 4), torch.uint8, X.device, stream)
     if s is None:
-        s = torch.empty((M,), dtype=torch.float32, device=X.device)
+        s = _empty((M,), torch.float32, X.device, stream)
     _check(lib.rtl_sparsify(_dt(X), M, K, _ptr(X), tie, eps, _ptr(vals), _ptr(idx), _ptr(s), _stream(stream)))
     return vals, idx, s
 
@@ -149,10 +166,10 @@ def rtl_linear_fused_workspace_bytes(dtype: int, M: int, N: int, K: int, R: int)
     return int(lib.rtl_linear_fused_workspace_bytes(dtype, M, N, K, R))
 
 
-def _workspace(dt, M, N, K, R, workspace, device):
+def _workspace(dt, M, N, K, R, workspace, device, stream=None):
     need = rtl_linear_fused_workspace_bytes(dt, M, N, K, R)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=device)
+        workspace = _empty((need,), torch.uint8, device, stream)
     return workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
 
 
@@ -170,8 +187,8 @@ def rtl_linear_fused(X: torch.Tensor, W: torch.Tensor, LA, LB, tie: int = RTL_TI
     R = 0 if LB is None else LB.shape[0]
     dt = _dt(X)
     if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    workspace, ws_bytes = _workspace(dt, M, N, K, R, workspace, X.device)
+        Y = _empty((M, N), X.dtype, X.device, stream)
+    workspace, ws_bytes = _workspace(dt, M, N, K, R, workspace, X.device, stream)
     _check(lib.rtl_linear_fused_ex(variant, dt, M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
                                    _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
     return Y
@@ -194,7 +211,7 @@ def rtl_linear_fused_main(X: torch.Tensor, W: torch.Tensor, LA, R: int, workspac
     M, K = X.shape
     N = W.shape[0]
     if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+        Y = _empty((M, N), X.dtype, X.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.rtl_linear_fused_main(variant, _dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), tie, eps, _ptr(Y),
                                      _ptr(workspace), ws_bytes, _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
@@ -210,7 +227,7 @@ def rtl_linear_fused_noalloc(X: torch.Tensor, W: torch.Tensor, LA, LB, tie: int 
     N = W.shape[0]
     R = 0 if LB is None else LB.shape[0]
     if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+        Y = _empty((M, N), X.dtype, X.device, stream)
     _check(lib.rtl_linear_fused_noalloc(_dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
                                         _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
     return Y
@@ -221,7 +238,7 @@ def rtl_linear_dense_ref(X: torch.Tensor, W: torch.Tensor, Y=None, stream=None) 
     M, K = X.shape
     N = W.shape[0]
     if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+        Y = _empty((M, N), X.dtype, X.device, stream)
     _check(lib.rtl_linear_dense_ref(_dt(X), M, N, K, _ptr(X), _ptr(W), _ptr(Y), _stream(stream)))
     return Y
 
@@ -232,9 +249,9 @@ def rtl_quantize_weight_fp8(W: torch.Tensor, Wq=None, sw=None, stream=None):
     if W.dtype != torch.bfloat16:
         raise TypeError("the FP8 layer takes bf16 weights")
     if Wq is None:
-        Wq = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+        Wq = _empty((N, K), torch.uint8, W.device, stream)
     if sw is None:
-        sw = torch.empty((N,), dtype=torch.float32, device=W.device)
+        sw = _empty((N,), torch.float32, W.device, stream)
     _check(lib.rtl_quantize_weight_fp8(N, K, _ptr(W), _ptr(Wq), _ptr(sw), _stream(stream)))
     return Wq, sw
 
@@ -254,10 +271,10 @@ def rtl_linear_fused_fp8(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, LA
     if X.dtype != torch.bfloat16:
         raise TypeError("the FP8 layer takes bf16 activations")
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+        Y = _empty((M, N), torch.bfloat16, X.device, stream)
     need = rtl_linear_fused_fp8_workspace_bytes(M, N, K, R)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
+        workspace = _empty((need,), torch.uint8, X.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.rtl_linear_fused_fp8(M, N, K, R, _ptr(X), _ptr(Wq), _ptr(sw), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
                                     _ptr(workspace), ws_bytes, _ptr(dbg_xq), _ptr(dbg_sx), _stream(stream)))

@@ -84,6 +84,19 @@ def heavy_rows(seed_val: int, seed_pos: int, M: int, K: int, n_active: int, std_
     return out
 
 
+def group_latent(seed: int, M: int, K: int, d: int = 16, noise: float = 0.05) -> np.ndarray:
+    """Rows whose groups of 4 consecutive channels share one latent value under fixed
+    per-channel scales: x[4g + j] = (Z U)[g] * a[g, j] + noise, with Z ~ N(0,1) [M, d],
+    U ~ N(0, 1/d) [d, K/4], a = exp(N(0,1)) [K/4, 4] and N(0, noise^2) noise (streams
+    seed .. seed + 3).  Activations with a consistent channel-scale pattern and low-
+    dimensional content."""
+    Z = normal(seed, (M, d)).astype(np.float64)
+    U = normal(seed + 1, (d, K // 4), std=1.0 / np.sqrt(d)).astype(np.float64)
+    a = np.exp(normal(seed + 2, (K // 4, 4)).astype(np.float64))
+    X = ((Z @ U)[:, :, None] * a[None]).reshape(M, K) + normal(seed + 3, (M, K), std=noise)
+    return X.astype(np.float32)
+
+
 def to_bf16(a: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
     a = np.ascontiguousarray(a, dtype=np.float32)

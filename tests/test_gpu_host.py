@@ -61,24 +61,32 @@ def _fixed_channel_rows(seed, M, K, frac=0.08, scale=30.0):
     return X
 
 
-@pytest.mark.parametrize("recipe", ["per_row_channels", "shared_channels"])
+@pytest.mark.parametrize("recipe", ["per_row_channels", "shared_channels", "group_latent"])
 def test_lowrank_ablation(recipe):
-    """The fit always lowers the residual on its calibration rows (it minimises it; zero
-    factors are a candidate).  Whether the norm compensation or the branch lowers the
-    held-out error depends on the activations: the page's accuracy claims are about real
-    DiT activations (parity unpinned here), so the held-out errors are reported, not
-    asserted."""
+    """Held-out output error against the dense layer of the plain 2:4 product, the
+    norm-compensated one and the full layer with L_A, L_B fitted on calibration rows
+    (summary page, method step 2).  The fit always lowers the residual on its calibration
+    rows (it minimises it; zero factors are a candidate).  On i.i.d. background values the
+    residual is not linearly predictable from X, so the held-out errors are only reported;
+    on activations whose groups share a latent value under fixed channel scales
+    (group_latent) the dropped part is nearly a linear function of X, and the fitted branch
+    must cut the held-out error at least in half.  The full layer at the fitted factors is
+    checked against the oracle on held-out rows.  The page's accuracy claims (FID, image
+    reward on real DiT activations) stay unpinned."""
     from activation_sparse_gemm_amd.calib import ablation
     K, N, R = 512, 512, 64
     M_cal, M_test = 8192, 1024
     if recipe == "per_row_channels":
         lay = synth.Layer("abl", M_cal + M_test, K, N, 0, "bf16", "heavy", 0.08)
         d = synth.make_layer(lay, seed_base=7300)
-        X = to_dev(d["X"])
-        W = to_dev(d["W"])
+        Xh, Wh = d["X"], d["W"]
+    elif recipe == "shared_channels":
+        Xh = synth.to_bf16(_fixed_channel_rows(7400, M_cal + M_test, K))
+        Wh = synth.to_bf16(synth.normal(7402, (N, K), std=1.0 / np.sqrt(K)))
     else:
-        X = to_dev(synth.to_bf16(_fixed_channel_rows(7400, M_cal + M_test, K)))
-        W = to_dev(synth.to_bf16(synth.normal(7402, (N, K), std=1.0 / np.sqrt(K))))
+        Xh = synth.to_bf16(synth.group_latent(7700, M_cal + M_test, K))
+        Wh = synth.to_bf16(synth.normal(7704, (N, K), std=1.0 / np.sqrt(K)))
+    X, W = to_dev(Xh), to_dev(Wh)
     res = ablation(X[:M_cal], X[M_cal:], W, R=R)
     e = res["errors"]
     log(f"[ablation] {recipe}: K=N={K}, R={R}, fit on {M_cal} rows, held-out {M_test}: "
@@ -86,6 +94,18 @@ def test_lowrank_ablation(recipe):
     for k in ("sparse", "norm_compensated", "nc_lowrank", "bf16_full"):
         assert np.isfinite(e[k]["frob"]) and 0 < e[k]["frob"] < 1
     assert 0 < e["cal_residual_reduction"] < 1
+    if recipe == "group_latent":
+        assert e["nc_lowrank"]["frob"] < 0.5 * e["norm_compensated"]["frob"], e
+        assert e["cal_residual_reduction"] > 0.5
+    # the full layer at the fitted factors (fp32 path) against the oracle on held-out rows
+    LA32, LB32 = res["LA"].float().numpy(), res["LB"].float().numpy()
+    Xt32 = synth.bf16_to_f32(Xh[M_cal:])
+    W32 = synth.bf16_to_f32(Wh)
+    rows = np.arange(0, M_test, 7)
+    Yg = rtl.rtl_linear_fused(to_dev(Xt32), to_dev(W32), to_dev(LA32), to_dev(LB32))
+    torch.cuda.synchronize()
+    Yref, _ = oracle.linear(Xt32, W32, LA32, LB32, rows=rows)
+    check_y(to_host(Yg)[rows].astype(np.float64), Yref, "f32", f"ablation {recipe} fitted layer")
 
 
 def test_concurrent_calls_on_separate_streams():
@@ -134,3 +154,28 @@ def test_concurrent_calls_on_separate_streams():
     for i in range(len(shapes)):
         assert torch.equal(out[i], ref[i]), shapes[i]
     log(f"[concurrent] {len(shapes)} threads x 20 calls on separate streams: results identical")
+
+
+def test_explicit_stream_without_workspace():
+    """Calls on a side stream passed as stream=, with the workspace and Y allocated by the
+    binding, while the current stream allocates and overwrites fresh memory: every result
+    equals a lone call's (the binding allocates on the call's stream, so the caching
+    allocator cannot hand a workspace still in use to the current stream's work)."""
+    lay = synth.Layer("st", 2000, 1024, 4000, 64, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=7600)
+    X, W, LA, LB = (to_dev(d[k]) for k in ("X", "W", "LA", "LB"))
+    ref = rtl.rtl_linear_fused(X, W, LA, LB)
+    torch.cuda.synchronize()
+    need = rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, 2000, 4000, 1024, 64)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(6):
+        outs.append(rtl.rtl_linear_fused(X, W, LA, LB, stream=side))
+        junk = torch.full((need,), 255, dtype=torch.uint8, device="cuda")  # current stream
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for Y in outs:
+        assert torch.equal(Y.view(torch.int16), ref.view(torch.int16))
+    log(f"[stream] {len(outs)} side-stream calls with binding-allocated workspaces match the lone call")

@@ -46,3 +46,17 @@ def test_layer_shapes():
             assert d["LA"].shape == (lay.N, lay.R) and d["LB"].shape == (lay.R, lay.K)
         want = np.float32 if lay.dtype == "f32" else np.uint16
         assert d["X"].dtype == want
+
+
+def test_group_latent_recipe():
+    """Seeded and reproducible; every group of 4 channels is one latent value times fixed
+    per-channel scales (plus small noise), so the in-group magnitude order is nearly the
+    same in every row."""
+    a = synth.group_latent(7700, 256, 512)
+    b = synth.group_latent(7700, 256, 512)
+    assert a.dtype == np.float32 and a.shape == (256, 512) and np.array_equal(a, b)
+    assert not np.array_equal(a, synth.group_latent(7701, 256, 512))
+    g = np.abs(a.reshape(256, 128, 4))
+    top = np.argmax(g, axis=2)                       # largest channel of each group, per row
+    mode = np.array([np.bincount(top[:, j], minlength=4).max() for j in range(128)])
+    assert np.median(mode / 256) > 0.8
