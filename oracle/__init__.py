@@ -8,7 +8,8 @@ nothing from it.
 The arithmetic lives in ``rtl_oracle.c`` (plain C, fp64, OpenMP over rows); this
 module only builds it with gcc and marshals numpy arrays.  Method source: "RT-Lynx:
 Putting the GEMM Sparsity In a Right Way for Diffusion Models" (summary page, method
-overview, steps 1-2; the FP8 variant follows the reading stated in ``rtl_oracle.c``).
+overview, steps 1-2; step 3 for the MLP pair; the FP8 variant follows the reading stated
+in ``rtl_oracle.c``).
 All functions are pinned by the CPU tests; none is "parity unpinned".
 """
 from __future__ import annotations
@@ -60,6 +61,12 @@ def _load():
         lib.orc_num_threads.restype = i32
         lib.orc_set_num_threads.argtypes = [i32]
         lib.orc_set_num_threads.restype = None
+        lib.orc_gelu.argtypes = [d]
+        lib.orc_gelu.restype = d
+        lib.orc_round_bf16.argtypes = [d]
+        lib.orc_round_bf16.restype = ctypes.c_uint16
+        lib.orc_mlp.argtypes = [i64, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, i32, d, p, i64, p, p]
+        lib.orc_mlp.restype = i32
         lib.orc_e4m3_value.argtypes = [i32]
         lib.orc_e4m3_value.restype = d
         lib.orc_e4m3_encode_array.argtypes = [i64, p, p]
@@ -243,3 +250,48 @@ def linear_fp8(X, Wq, sw, LA, LB, rows=None, tie: int = TIE_LOWER, eps: float = 
                                 _ptr(rows_arr), nrows, _ptr(Y), _ptr(s), _ptr(T), _ptr(xq), _ptr(sx))
     _check(rc)
     return (Y, s, T[:, :R], xq, sx) if want_all else (Y, s)
+
+
+def gelu(x: float) -> float:
+    """GELU(x) = x Phi(x), exact erf form, in fp64."""
+    return _load().orc_gelu(float(x))
+
+
+def round_bf16(v: float) -> int:
+    """Bit pattern of the nearest bf16 value of a double (ties to even, rounded once)."""
+    return int(_load().orc_round_bf16(float(v)))
+
+
+def mlp(X, Wu, LAu, LBu, Wd, LAd, LBd, rows=None, tie: int = TIE_LOWER, eps: float = EPS, want_xd: bool = False):
+    """The MLP pair y = layer_down(bf16(GELU(bf16(layer_up(x))))) in fp64 for the given rows.
+
+    X [M,K], Wu [H,K], LAu [H,Ru], LBu [Ru,K], Wd [N,H], LAd [N,Rd], LBd [Rd,H], all bf16
+    bits (LA/LB pairs may be None).  Returns Y [rows, N] or (Y, Xd [rows, H] bf16 bits)."""
+    X = np.ascontiguousarray(X)
+    arrs = [X, Wu, Wd]
+    if any(_dtype_of(np.asarray(a)) != BF16 for a in arrs):
+        raise TypeError("the MLP pair takes bf16 inputs")
+    M, K = X.shape
+    H, N = Wu.shape[0], Wd.shape[0]
+    if Wu.shape[1] != K or Wd.shape[1] != H:
+        raise ValueError("Wu must be [H, K] and Wd [N, H]")
+
+    def lr(LA, LB, n, k):
+        if LA is None or LB is None:
+            return None, None, 0
+        LA, LB = np.ascontiguousarray(LA), np.ascontiguousarray(LB)
+        r = LB.shape[0]
+        if LA.shape != (n, r) or LB.shape != (r, k):
+            raise ValueError("low-rank factor shapes")
+        return LA, LB, r
+
+    LAu, LBu, Ru = lr(LAu, LBu, H, K)
+    LAd, LBd, Rd = lr(LAd, LBd, N, H)
+    Wu, Wd = np.ascontiguousarray(Wu), np.ascontiguousarray(Wd)
+    rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nrows = M if rows_arr is None else rows_arr.shape[0]
+    Y = np.zeros((nrows, N))
+    Xd = np.zeros((nrows, H), np.uint16)
+    _check(_load().orc_mlp(M, K, H, N, Ru, Rd, _ptr(X), _ptr(Wu), _ptr(LAu), _ptr(LBu), _ptr(Wd), _ptr(LAd),
+                           _ptr(LBd), tie, eps, _ptr(rows_arr), nrows, _ptr(Y), _ptr(Xd)))
+    return (Y, Xd) if want_xd else Y

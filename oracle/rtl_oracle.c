@@ -13,6 +13,9 @@
  *     s = ||X||_2 / (||X~||_2 + eps) with eps = 1e-8, and S(X) = s * X~.
  *   step 2 (LoRA compensation): Y_s = S(X) W^T on the sparse branch, the original dense
  *     X feeds a rank-R branch Y_r = X (L_A L_B)^T, and Y = Y_s + Y_r.
+ *   step 3 (selective layer skipping): in Qwen-Image both MLP projections are sparsified,
+ *     so the up projection's activated output is the down projection's input (orc_mlp;
+ *     the activation is read as exact-erf GELU, the tensors between the layers as bf16).
  *
  * Readings of points the page leaves open (each is listed with its reason in the
  * design notes):
@@ -457,4 +460,71 @@ int orc_linear_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, co
   free(Wd); free(LAd); free(LBd);
   if (bad & 2) return ORC_ENOMEM;
   return (bad & 1) ? ORC_ENONFINITE : ORC_OK;
+}
+
+/* ------------------------------------------------------------------ MLP pair */
+/*
+ * The MLP pair of a DiT block ("RT-Lynx", summary page, method step 3: in Qwen-Image both
+ * projections of the MLP are sparsified, so the up projection's output, after the
+ * activation, is the down projection's input).  Reading: the activation is GELU with the
+ * exact erf form, and the tensors between the layers are bf16, as a bf16 model stores
+ * them: per row,
+ *   u = bf16(layer_up(x)),  g = bf16(GELU(u)),  y = layer_down(g),
+ * each layer as orc_linear (fp64), bf16() rounding to nearest even.
+ */
+
+/* GELU(x) = x Phi(x) = x (1 + erf(x / sqrt(2))) / 2, Phi the standard normal CDF. */
+double orc_gelu(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
+
+/* Nearest bf16 value (ties to even) of a finite double, rounded once: 8 significant bits
+ * for |v| >= 2^-126, multiples of 2^-133 below (the bf16 subnormals).  Returns the bit
+ * pattern; magnitudes that round past the largest finite bf16 give infinity. */
+uint16_t orc_round_bf16(double v) {
+  double r;
+  if (v == 0.0 || !isfinite(v)) {
+    r = v;
+  } else if (fabs(v) < ldexp(1.0, -126)) {
+    r = ldexp(nearbyint(ldexp(v, 133)), -133);
+  } else {
+    int e;
+    const double m = frexp(v, &e); /* v = m 2^e, 0.5 <= |m| < 1 */
+    r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+  }
+  const float f = (float)r; /* exact: r has at most 8 significant bits (or overflows to inf) */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+/*
+ * The pair for a list of rows of X [M,K] (bf16 bits): up layer W_u [H,K], LA_u [H,Ru],
+ * LB_u [Ru,K]; down layer W_d [N,H], LA_d [N,Rd], LB_d [Rd,H].  Outputs Y [nrows,N] double
+ * and, when Xd_out is not NULL, the down layer's input g [nrows,H] (bf16 bits).
+ */
+int orc_mlp(int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd, const void* X,
+            const void* Wu, const void* LAu, const void* LBu, const void* Wd, const void* LAd,
+            const void* LBd, int tie, double eps, const int64_t* rows, int64_t nrows, double* Y,
+            uint16_t* Xd_out) {
+  if (M <= 0 || K <= 0 || H <= 0 || N <= 0 || H % 4 != 0 || !Y) return ORC_EARG;
+  if (!rows) nrows = M;
+  double* U = (double*)malloc(sizeof(double) * (size_t)(nrows * H));
+  uint16_t* G = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(nrows * H));
+  if (!U || !G) {
+    free(U); free(G);
+    return ORC_ENOMEM;
+  }
+  int rc = orc_linear(ORC_BF16, M, H, K, Ru, X, Wu, LAu, LBu, tie, eps, rows, nrows, U, NULL, NULL);
+  if (rc == ORC_OK) {
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < nrows * H; e++) {
+      const uint16_t ub = orc_round_bf16(U[e]);
+      const double u = orc_load(ORC_BF16, &ub, 0);
+      G[e] = orc_round_bf16(orc_gelu(u));
+    }
+    rc = orc_linear(ORC_BF16, nrows, N, H, Rd, G, Wd, LAd, LBd, tie, eps, NULL, nrows, Y, NULL, NULL);
+    if (rc == ORC_OK && Xd_out) memcpy(Xd_out, G, sizeof(uint16_t) * (size_t)(nrows * H));
+  }
+  free(U);
+  free(G);
+  return rc;
 }
