@@ -22,7 +22,8 @@ __all__ = [
     "RTL_F32", "RTL_BF16", "RTL_TIE_LOWER_INDEX", "EPS", "RtlError", "lib", "library_path",
     "rtl_sparsify", "rtl_linear_fused", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused_ex",
     "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_fused_noalloc", "rtl_linear_dense_ref",
-    "RTL_NOALLOC_SCRATCH_BYTES", "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
+    "RTL_NOALLOC_SCRATCH_BYTES", "rtl_mlp_fused", "rtl_mlp_fused_workspace_bytes", "RTL_MLP_AUTO",
+    "RTL_MLP_PRODUCER", "RTL_MLP_CONSUMER", "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
     "rtl_status_string", "rtl_version",
     "rtl_quantize_weight_fp8", "rtl_linear_fused_fp8", "rtl_linear_fused_fp8_workspace_bytes",
 ]
@@ -35,13 +36,14 @@ RTL_TIE_LOWER_INDEX = 0
 RTL_VARIANT_AUTO, RTL_VARIANT_PROLOGUE, RTL_VARIANT_PRECOMPRESSED = 0, 1, 2
 EPS = 1e-8
 RTL_NOALLOC_SCRATCH_BYTES = 128 << 20  # include/rtl.h
+RTL_MLP_AUTO, RTL_MLP_PRODUCER, RTL_MLP_CONSUMER = 0, 1, 2
 STATUS = {0: "RTL_OK", 1: "RTL_ERR_NULL", 2: "RTL_ERR_SHAPE", 3: "RTL_ERR_ALIGN", 4: "RTL_ERR_UNSUPPORTED",
           5: "RTL_ERR_ARG", 6: "RTL_ERR_WORKSPACE", 7: "RTL_ERR_HIP"}
 
 # Every entry point include/rtl.h declares.
 EXPORTS = ["rtl_sparsify", "rtl_linear_fused_workspace_bytes", "rtl_linear_fused", "rtl_linear_fused_ex",
            "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_fused_noalloc", "rtl_linear_dense_ref",
-           "rtl_quantize_weight_fp8",
+           "rtl_mlp_fused_workspace_bytes", "rtl_mlp_fused", "rtl_quantize_weight_fp8",
            "rtl_linear_fused_fp8_workspace_bytes", "rtl_linear_fused_fp8", "rtl_status_string",
            "rtl_last_error", "rtl_version"]
 
@@ -71,6 +73,11 @@ def _load() -> ctypes.CDLL:
     L.rtl_linear_fused_main.restype = i32
     L.rtl_linear_fused_noalloc.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i32, f32, p, p, p, p]
     L.rtl_linear_fused_noalloc.restype = i32
+    L.rtl_mlp_fused_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+    L.rtl_mlp_fused_workspace_bytes.restype = sz
+    L.rtl_mlp_fused.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, i32, f32, p, p, sz, p, p,
+                                p, p]
+    L.rtl_mlp_fused.restype = i32
     L.rtl_linear_dense_ref.argtypes = [i32, i64, i64, i64, p, p, p, p]
     L.rtl_linear_dense_ref.restype = i32
     L.rtl_quantize_weight_fp8.argtypes = [i64, i64, p, p, p, p]
@@ -230,6 +237,38 @@ def rtl_linear_fused_noalloc(X: torch.Tensor, W: torch.Tensor, LA, LB, tie: int 
         Y = _empty((M, N), X.dtype, X.device, stream)
     _check(lib.rtl_linear_fused_noalloc(_dt(X), M, N, K, R, _ptr(X), _ptr(W), _ptr(LA), _ptr(LB), tie, eps, _ptr(Y),
                                         _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
+    return Y
+
+
+def rtl_mlp_fused_workspace_bytes(M: int, K: int, H: int, N: int, Ru: int, Rd: int) -> int:
+    return int(lib.rtl_mlp_fused_workspace_bytes(M, K, H, N, Ru, Rd))
+
+
+def rtl_mlp_fused(X: torch.Tensor, Wu: torch.Tensor, LAu, LBu, Wd: torch.Tensor, LAd, LBd,
+                  tie: int = RTL_TIE_LOWER_INDEX, eps: float = EPS, Y=None, workspace=None, dbg_xd=None,
+                  dbg_idx=None, dbg_s=None, stream=None, variant: int = RTL_MLP_AUTO) -> torch.Tensor:
+    """The MLP pair Y = layer_down(bf16(GELU(bf16(layer_up(X))))) in one call (bf16).
+
+    X [M,K], Wu [H,K], LAu [H,Ru], LBu [Ru,K], Wd [N,H], LAd [N,Rd], LBd [Rd,H] (a layer's
+    LA/LB None: rank 0).  ``dbg_xd`` [M,H] bf16, ``dbg_idx`` [M,H/4] uint8 and ``dbg_s`` [M]
+    float32 receive the down layer's input, selection codes and s as the kernels formed them.
+    ``variant``: RTL_MLP_PRODUCER (down operand from the up GEMM's epilogue), RTL_MLP_CONSUMER
+    (GELU in the down layer's pre-pass) or RTL_MLP_AUTO."""
+    M, K = X.shape
+    H, N = Wu.shape[0], Wd.shape[0]
+    Ru = 0 if LBu is None else LBu.shape[0]
+    Rd = 0 if LBd is None else LBd.shape[0]
+    if X.dtype != torch.bfloat16:
+        raise TypeError("the MLP pair takes bf16 tensors")
+    if Y is None:
+        Y = _empty((M, N), X.dtype, X.device, stream)
+    need = rtl_mlp_fused_workspace_bytes(M, K, H, N, Ru, Rd)
+    if workspace is None:
+        workspace = _empty((max(need, 1),), torch.uint8, X.device, stream)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.rtl_mlp_fused(variant, RTL_BF16, M, K, H, N, Ru, Rd, _ptr(X), _ptr(Wu), _ptr(LAu), _ptr(LBu), _ptr(Wd),
+                             _ptr(LAd), _ptr(LBd), tie, eps, _ptr(Y), _ptr(workspace), ws_bytes, _ptr(dbg_xd),
+                             _ptr(dbg_idx), _ptr(dbg_s), _stream(stream)))
     return Y
 
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "librtl.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["rtl_api.cpp", "sparsify.hip", "prep_bf16.hip", "gemm_bf16.hip", "gemm_fp8.hip", "fp32_path.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "mlp_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

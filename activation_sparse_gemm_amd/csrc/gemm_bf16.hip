@@ -553,6 +553,110 @@ void gemm_kernel(const GemmArgs a) {
                     [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
 }
 
+// Producer epilogue of the MLP pair's up layer (half_kernel<128, true>), wave `wave` of
+// tile (tm, tn): rows m0 + 64 wave .. +63 (one 64-row panel of the down layer's operand),
+// columns n0 .. n0 + 127 (K steps 2 tn and 2 tn + 1 of the down layer).  For each 16-row
+// block rb: the lane's accumulators (columns 16 nb + r16, rows 16 rb + 4q + j) become
+// X_d = bf16(GELU(bf16(s acc))) in the wave's LDS block `blk` (row pitch 272 bytes); then
+// lane l reads 16 consecutive X_d values of row 16 rb + l % 16 (k = 16 (l / 16) of each K
+// step), selects, and writes them in the sparse-MFMA register order; the same rows feed
+// the MFMA product with L_B_down.  LDS writes and reads stay within the wave (in program
+// order), so no barrier is needed.
+__device__ __forceinline__ void produce_down_operand(const GemmArgs& a, const f32x4 (&acc)[4][8],
+                                                     const float (&s_acc)[4][4], uint8_t* blk, int tm, int tn,
+                                                     int wave, int lane) {
+  constexpr int PITCH = 2 * 128 + 16;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t M = a.M, N = a.N;
+  const int64_t Mp = (int64_t)a.n_panels * kPanel;
+  const int64_t m0 = (int64_t)tm * kBM + 64 * wave, n0 = (int64_t)tn * 128;
+  const int64_t p = (int64_t)tm * 4 + wave;  // panel of the down operand
+  const bool pan_ok = p < a.n_panels;
+  const int KTd = (int)(N / kBK);
+  const int Rd = (int)a.d_R;
+  const __amdgpu_buffer_rsrc_t lbres = make_rsrc(a.d_LB, (int64_t)Rd * N * 2);
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+#pragma unroll
+    for (int nb = 0; nb < 8; nb++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float u = __uint_as_float(f32_to_bf16_bits(acc[rb][nb][j] * s_acc[rb][j]) << 16);
+        *reinterpret_cast<uint16_t*>(blk + (4 * q + j) * PITCH + (nb * 16 + r16) * 2) =
+            (uint16_t)f32_to_bf16_bits(gelu_erf(u));
+      }
+    const int64_t row = m0 + 16 * rb + r16;  // the row this lane selects for
+    double nx2 = 0.0, nt2 = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint8_t* src = blk + r16 * PITCH + (64 * h + 16 * q) * 2;
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(src + 16);
+      const uint32_t w8[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      u32x4 v;
+      uint32_t code16 = 0, bytes = 0;
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        uint32_t vv, cc;
+        select_bf16(w8[2 * g], w8[2 * g + 1], vv, cc);
+        v[g] = vv;
+        code16 |= cc << (4 * g);
+        bytes |= cc << (8 * g);
+        nx2 = sq2_f64(w8[2 * g + 1], sq2_f64(w8[2 * g], nx2));
+        nt2 = sq2_f64(vv, nt2);
+      }
+      const int kt = 2 * tn + h;
+      if (pan_ok) {
+        *reinterpret_cast<u32x4*>(a.d_cvals + cvals_off(p, KTd, kt) + rb * 1024 + lane * 16) = v;
+        *reinterpret_cast<uint16_t*>(a.d_cidx + cidx_off(p, KTd, kt) + lane * 8 + rb * 2) = (uint16_t)code16;
+      }
+      if (row < M) {
+        const int64_t col = n0 + 64 * h + 16 * q;
+        if (a.d_dbg_x != nullptr) {
+          *reinterpret_cast<u32x4*>(a.d_dbg_x + row * N + col) = c0;
+          *reinterpret_cast<u32x4*>(a.d_dbg_x + row * N + col + 8) = c1;
+        }
+        if (a.d_dbg_idx != nullptr) *reinterpret_cast<uint32_t*>(a.d_dbg_idx + row * (N / 4) + col / 4) = bytes;
+      }
+    }
+    nx2 += __shfl_xor(nx2, 16, 64);
+    nt2 += __shfl_xor(nt2, 16, 64);
+    nx2 += __shfl_xor(nx2, 32, 64);
+    nt2 += __shfl_xor(nt2, 32, 64);
+    if (q == 0 && row < Mp) {
+      a.d_npart[((int64_t)tn * Mp + row) * 2 + 0] = nx2;
+      a.d_npart[((int64_t)tn * Mp + row) * 2 + 1] = nt2;
+    }
+    // partial X_d L_B_down^T over the tile's 128 columns: A = rows 16 rb + r16 (k = 32 kk +
+    // 8q .. +7 from LDS), B = rows cb 16 + r16 of L_B_down (same k); accumulator rows
+    // 16 rb + 4q + j, column cb 16 + r16.
+    f32x4 tacc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) tacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(blk + r16 * PITCH + (32 * kk + 8 * q) * 2);
+#pragma unroll
+      for (int cb = 0; cb < 4; cb++)
+        if (cb < Rd / 16) {
+          const u32x4 lb = __builtin_amdgcn_raw_buffer_load_b128(
+              lbres, (uint32_t)(((cb * 16 + r16) * N + n0 + 32 * kk + 8 * q) * 2), 0, 0);
+          tacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                             __builtin_bit_cast(bf16x8, lb), tacc[cb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++)
+      if (cb < Rd / 16) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int64_t r = m0 + 16 * rb + 4 * q + j;
+          if (r < Mp) a.d_tpart[((int64_t)tn * Mp + r) * Rd + cb * 16 + r16] = tacc[cb][j];
+        }
+      }
+  }
+}
+
 // Pre-compressed GEMM with 4 waves (one per SIMD) on a 256 x TW output tile, wave w owns
 // rows 64w..64w+63 and all TW columns.  TW = 96 or 128: two workgroups per CU, which reach
 // their barriers at different times, so one's matrix-core work covers the other's step
@@ -563,13 +667,24 @@ void gemm_kernel(const GemmArgs a) {
 // straight into registers (no sharing, no duplication) and the workgroup loads a TW x 64
 // W tile straight into a 4-buffer LDS ring (no register staging), with the same
 // interleaving and K stagger as gemm_kernel.
+//
+// PROD (TW = 128): the up layer of the MLP pair ("RT-Lynx", summary page, method step 3:
+// the MLP's up and down projections are both sparsified, so the up output, after the
+// activation, is the down input).  Instead of storing Y its epilogue forms the down layer's
+// input X_d = bf16(GELU(bf16(Y))) (exact-erf GELU in fp32) and writes what the down
+// layer's pre-pass would: the 2-of-4 selection of X_d packed as the down layer's
+// compressed operand (the tile's 128 columns are two 64-wide K steps of the down layer,
+// its four waves four 64-row panels), and per tile the partial squared norms of X_d and
+// X_d~ over its columns and the partial rank-R product X_d L_B_down^T, which a fixed-order
+// reduction turns into T_down / s and s.  X_d itself never reaches device memory.
 constexpr int kHalfThreads = 256;
 
-template <int TW>
+template <int TW, bool PROD = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads),
                           amdgpu_waves_per_eu(TW >= 192 ? 1 : 2, TW >= 192 ? 1 : 2)))
 void half_kernel(const GemmArgs a) {
   static_assert(TW == 128 || TW == 96 || TW == 192 || TW == 256, "tile widths");
+  static_assert(!PROD || TW == 128, "the producer epilogue runs on 128-wide tiles");
   constexpr int NB = TW / 16;                   // 16-column blocks per wave
   constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
@@ -754,6 +869,10 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
   __syncthreads();  // the LDS ring is free
+  if constexpr (PROD) {
+    produce_down_operand(a, acc, s_acc, wl + wave * 16 * (2 * TW + 16), tm, tn, wave, lane);
+    return;
+  }
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wave, n0, wl + wave * 16 * (2 * TW + 16), lane,
                     [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
 }
@@ -836,6 +955,28 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   }
   if (tn == 192) launch_main_tn<192>(comp, g, dbg_idx, stream);
   else launch_main_tn<256>(comp, g, dbg_idx, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_mlp_up_bf16(int64_t M, int64_t H, int64_t K, int64_t Ru, const void* Wu, const void* LAu,
+                              float eps, const void* ws_up, const PairDown& d, hipStream_t stream) {
+  const WsLayout L = ws_layout(M, K, Ru, true);
+  const uint8_t* base = (const uint8_t*)ws_up;
+  GemmArgs g = gemm_args(M, H, K, Ru, nullptr, Wu, LAu, nullptr, eps, 128);
+  g.T = (const uint16_t*)(base + L.t);
+  g.s = (const float*)(base + L.norm);
+  g.cvals = base + L.cvals;
+  g.cidx = base + L.cidx;
+  g.d_cvals = d.cvals;
+  g.d_cidx = d.cidx;
+  g.d_tpart = d.tpart;
+  g.d_npart = d.npart;
+  g.d_LB = (const uint16_t*)d.LB;
+  g.d_R = d.R;
+  g.d_dbg_x = d.dbg_x;
+  g.d_dbg_idx = d.dbg_idx;
+  hipLaunchKernelGGL((half_kernel<128, true>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream,
+                     g);
   return hipGetLastError();
 }
 

@@ -40,6 +40,18 @@ struct GemmArgs {
   int tiles_m, tiles_n, n_panels;
   const float* ax;        // FP8 layer: [Mp] row absmax of X
   const float* sw;        // FP8 layer: [N] weight dequantisation scales
+  // MLP pair, producer epilogue of the up layer (its output columns are the down layer's
+  // K): the down layer's compressed operand, per-tile partial T_down [tiles_n, Mp, d_R]
+  // f32 and squared norms [tiles_n, Mp, 2] f64, L_B of the down layer [d_R, N], optional
+  // copies of the down layer's input [M, N] bf16 and selection codes [M, N/4].
+  uint8_t* d_cvals;
+  uint8_t* d_cidx;
+  float* d_tpart;
+  double* d_npart;
+  const uint16_t* d_LB;
+  int64_t d_R;
+  uint16_t* d_dbg_x;
+  uint8_t* d_dbg_idx;
 };
 
 // Output tile store through LDS: the accumulator layout (lane = column 16nb + r16, rows

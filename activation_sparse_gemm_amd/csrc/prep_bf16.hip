@@ -28,6 +28,7 @@ struct PrepArgs {
   int fold;           // write T / s (formed in double precision) instead of T
   float* ax;          // FP8 layer: [Mp] row absmax of X (written when ks == 1)
   float* apart;       // FP8 layer: [ks, Mp] partial row absmax when ks > 1
+  uint16_t* dbg_x;    // ACT: [M, K] the activated input, or null
 };
 
 // Pre-pass over X.  Workgroup (row tile, K split): PW waves, wave w the 16-row block w of
@@ -40,7 +41,9 @@ struct PrepArgs {
 // prep_reduce_kernel sums them in a fixed order.  COMPRESS writes the compressed operand;
 // without it (the prologue variant) the selection still runs, for ||X~||^2.  AMAX (the
 // FP8 layer) also takes each row's largest magnitude, the scale of its 8-bit quantisation.
-template <bool COMPRESS, int RC, int PW, bool AMAX>  // RC = R / 32, PW waves = 16-row blocks per workgroup
+// ACT (the down layer of the MLP pair) applies GELU to every loaded value first (bf16 in,
+// exact-erf GELU in fp32, rounded to bf16): the layer's input is GELU of the stored X.
+template <bool COMPRESS, int RC, int PW, bool AMAX, bool ACT = false>  // RC = R / 32, PW waves = 16-row blocks per workgroup
 __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   constexpr int R = 32 * RC, CB = 2 * RC;
   constexpr int NT = 64 * PW;
@@ -99,7 +102,19 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   // stores and adds nothing to the sums, so every wave issues the same memory operations.
   auto compute = [&](int kt, const Stage& st, int buf, bool valid) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 xv0 = valid ? st.x[0] : z, xv1 = valid ? st.x[1] : z;
+    u32x4 x0 = st.x[0], x1 = st.x[1];
+    if (ACT) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        x0[e] = gelu_bf16x2(x0[e]);
+        x1[e] = gelu_bf16x2(x1[e]);
+      }
+      if (a.dbg_x != nullptr && row_ok && valid) {
+        *reinterpret_cast<u32x4*>(a.dbg_x + row * K + kt * kBK + 16 * q) = x0;
+        *reinterpret_cast<u32x4*>(a.dbg_x + row * K + kt * kBK + 16 * q + 8) = x1;
+      }
+    }
+    const u32x4 xv0 = valid ? x0 : z, xv1 = valid ? x1 : z;
     const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
 #pragma unroll
     for (int g = 0; g < 8; g++) nx2 = sq2_f64(w8[g], nx2);
@@ -110,8 +125,7 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     {
       u32x4 v;
       uint32_t code16 = 0, bytes = 0;
-      const uint32_t r8[8] = {st.x[0][0], st.x[0][1], st.x[0][2], st.x[0][3],
-                              st.x[1][0], st.x[1][1], st.x[1][2], st.x[1][3]};
+      const uint32_t r8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         uint32_t vv, cc;
@@ -342,16 +356,22 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const PrepArgs a, const P
 }
 
 // The pre-pass launches (prep_kernel, then the split reduction when K is split).
-template <bool AMAX>
+template <bool AMAX, bool ACT = false>
 static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const PrepSplit& sp, int64_t R,
                                 hipStream_t stream, bool reduce = true) {
   const dim3 grid((unsigned)(Mp / (16 * sp.waves)), (unsigned)sp.ks), block(64 * sp.waves);
-#define RTL_PREP(C, RC)                                                                          \
-  do {                                                                                           \
-    if (sp.waves == 8) hipLaunchKernelGGL((prep_kernel<C, RC, 8, AMAX>), grid, block, 0, stream, p); \
-    else hipLaunchKernelGGL((prep_kernel<C, RC, 4, AMAX>), grid, block, 0, stream, p);          \
+#define RTL_PREP(C, RC)                                                                                \
+  do {                                                                                                 \
+    if (sp.waves == 8) hipLaunchKernelGGL((prep_kernel<C, RC, 8, AMAX, ACT>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((prep_kernel<C, RC, 4, AMAX, ACT>), grid, block, 0, stream, p);          \
   } while (0)
-  if constexpr (AMAX) {
+  if constexpr (ACT) {
+    switch ((int)(R / 32)) {
+      case 0: RTL_PREP(true, 0); break;
+      case 1: RTL_PREP(true, 1); break;
+      default: RTL_PREP(true, 2); break;
+    }
+  } else if constexpr (AMAX) {
     switch ((int)(R / 32)) {
       case 0: RTL_PREP(true, 0); break;
       case 1: RTL_PREP(true, 1); break;
@@ -419,6 +439,54 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     p.dbg_idx = dbg_idx;
   }
   launch_prep_kernels<false>(p, comp, Mp, sp, R, stream);
+  return hipGetLastError();
+}
+
+// The pre-pass of the MLP pair's down layer: its input is GELU of X (the stored bf16 up
+// output), applied as the values are loaded; otherwise the pre-compressed variant's
+// pre-pass (R <= 64).
+hipError_t launch_prep_gelu_bf16(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB, float eps,
+                                 void* ws, uint16_t* dbg_x, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream) {
+  const WsLayout L = ws_layout(M, K, R, true);
+  uint8_t* base = (uint8_t*)ws;
+  PrepArgs p{};
+  p.M = M; p.K = K; p.R = R; p.X = (const uint16_t*)X; p.LB = (const uint16_t*)LB; p.eps = eps;
+  p.T = (uint16_t*)(base + L.t);
+  const int64_t Mp = padded_rows(M);
+  const PrepSplit sp = prep_split(M, K);
+  p.ks = sp.ks;
+  p.kts = sp.kts;
+  p.tpart = (float*)(base + L.tpart);
+  p.npart = (double*)(base + L.npart);
+  p.s = (float*)(base + L.norm);
+  p.dbg_s = dbg_s;
+  p.fold = 1;
+  p.cvals = base + L.cvals;
+  p.cidx = base + L.cidx;
+  p.dbg_idx = dbg_idx;
+  p.dbg_x = dbg_x;
+  (void)N;
+  launch_prep_kernels<false, true>(p, true, Mp, sp, R, stream);
+  return hipGetLastError();
+}
+
+// The fixed-order reduction of `ks` partial T and squared norms (the layout of the K-split
+// pre-pass) into T / s (bf16) and s: the MLP pair's down layer, whose partials come from
+// the up GEMM's epilogue.
+hipError_t launch_split_reduce_bf16(int64_t M, int64_t R, int ks, const float* tpart, const double* npart, float eps,
+                                    void* T, float* s, float* dbg_s, hipStream_t stream) {
+  PrepArgs p{};
+  p.M = M; p.R = R; p.eps = eps;
+  p.T = (uint16_t*)T;
+  p.s = s;
+  p.dbg_s = dbg_s;
+  p.tpart = const_cast<float*>(tpart);
+  p.npart = const_cast<double*>(npart);
+  p.ks = ks;
+  p.fold = 1;
+  const int64_t Mp = padded_rows(M);
+  const int64_t items = Mp * (R >= 4 ? R / 4 : 1);
+  hipLaunchKernelGGL(prep_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p, Mp);
   return hipGetLastError();
 }
 

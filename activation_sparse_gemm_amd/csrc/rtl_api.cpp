@@ -242,6 +242,55 @@ rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, i
                     "rtl_linear_fused_main launch");
 }
 
+size_t rtl_mlp_fused_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd) {
+  if (M <= 0 || K <= 0 || H <= 0 || N <= 0 || Ru < 0 || Rd < 0) return 0;
+  return rtl::mlp_bf16_workspace(M, K, H, N, Ru, Rd);
+}
+
+rtl_status rtl_mlp_fused(rtl_mlp_variant variant, rtl_dtype dt, int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd,
+                         const void* X, const void* Wu, const void* LAu, const void* LBu, const void* Wd,
+                         const void* LAd, const void* LBd, rtl_tie_rule tie, float eps, void* Y, void* workspace,
+                         size_t ws_bytes, void* dbg_xd, uint8_t* dbg_idx, float* dbg_s, void* stream) {
+  rtl_status st;
+  if ((st = check_dtype(dt)) != RTL_OK) return st;
+  if (dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "the MLP pair is bf16 only");
+  if (variant != RTL_MLP_AUTO && variant != RTL_MLP_PRODUCER && variant != RTL_MLP_CONSUMER)
+    return fail(RTL_ERR_UNSUPPORTED, "unsupported MLP variant %d", (int)variant);
+  if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
+  if (M <= 0 || K <= 0 || H <= 0 || N <= 0 || Ru < 0 || Rd < 0)
+    return fail(RTL_ERR_SHAPE, "need M, K, H, N > 0 and ranks >= 0 (M=%lld K=%lld H=%lld N=%lld)", (long long)M,
+                (long long)K, (long long)H, (long long)N);
+  if (K % 64 != 0 || H % 128 != 0 || Ru % 32 != 0 || Ru > 128 || (Rd != 0 && Rd != 32 && Rd != 64))
+    return fail(RTL_ERR_UNSUPPORTED,
+                "the MLP pair needs K %% 64 == 0, H %% 128 == 0, Ru %% 32 == 0 with Ru <= 128, Rd in {0, 32, 64} "
+                "(K=%lld H=%lld Ru=%lld Rd=%lld)",
+                (long long)K, (long long)H, (long long)Ru, (long long)Rd);
+  if (!X || !Wu || !Wd || !Y || (Ru > 0 && (!LAu || !LBu)) || (Rd > 0 && (!LAd || !LBd)))
+    return fail(RTL_ERR_NULL, "X, Wu, Wd, Y (and each layer's LA, LB when its rank > 0) are required");
+  const void* ptrs[] = {X, Wu, LAu, LBu, Wd, LAd, LBd, Y, workspace, dbg_xd, dbg_idx, dbg_s};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if ((st = check_eps(eps)) != RTL_OK) return st;
+  const size_t need = rtl::mlp_bf16_workspace(M, K, H, N, Ru, Rd);
+  const void* ins[7] = {X, Wu, Ru > 0 ? LAu : nullptr, Ru > 0 ? LBu : nullptr, Wd, Rd > 0 ? LAd : nullptr,
+                        Rd > 0 ? LBd : nullptr};
+  const size_t inb[7] = {(size_t)(M * K * 2), (size_t)(H * K * 2), (size_t)(H * Ru * 2), (size_t)(Ru * K * 2),
+                         (size_t)(N * H * 2), (size_t)(N * Rd * 2), (size_t)(Rd * H * 2)};
+  const void* outs[5] = {Y, workspace, dbg_xd, dbg_idx, dbg_s};
+  const size_t outb[5] = {(size_t)(M * N * 2), need, (size_t)(M * H * 2), (size_t)(M * (H / 4)), (size_t)(M * 4)};
+  for (int o = 0; o < 5; o++) {
+    for (int i = 0; i < 7; i++)
+      if (overlap(outs[o], outb[o], ins[i], inb[i])) return fail(RTL_ERR_ARG, "an output or the workspace overlaps an input");
+    for (int o2 = o + 1; o2 < 5; o2++)
+      if (overlap(outs[o], outb[o], outs[o2], outb[o2])) return fail(RTL_ERR_ARG, "outputs overlap each other or the workspace");
+  }
+  if (!workspace || ws_bytes < need)
+    return fail(RTL_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0);
+  return hip_status(rtl::launch_mlp_bf16((int)variant, M, K, H, N, Ru, Rd, X, Wu, LAu, LBu, Wd, LAd, LBd, eps, Y, workspace,
+                                         (uint16_t*)dbg_xd, dbg_idx, dbg_s, (hipStream_t)stream),
+                    "rtl_mlp_fused launch");
+}
+
 rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, const void* X, const void* W, void* Y,
                                 void* stream) {
   rtl_status st;

@@ -106,6 +106,13 @@ __device__ __forceinline__ double inv_scale_from_norms(double nx2, double nt2, f
   return nx2 > 0.0 ? (sqrt(nt2) + (double)eps) / sqrt(nx2) : 0.0;
 }
 
+// GELU(u) = u Phi(u) = u (1 + erf(u / sqrt 2)) / 2 (the exact erf form), in fp32, and its
+// application to the two bf16 values packed in a word (results rounded to bf16).
+__device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w) {
+  return pack_bf16x2(gelu_erf(bf16lo(w)), gelu_erf(bf16hi(w)));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

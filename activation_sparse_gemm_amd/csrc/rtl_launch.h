@@ -38,6 +38,34 @@ hipError_t launch_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, const vo
                             const float* sw, const void* LA, const void* LB, float eps, void* Y, void* ws,
                             uint8_t* dbg_xq, float* dbg_sx, hipStream_t stream);
 
+// MLP pair (bf16): up layer, GELU, down layer.  Producer variant: the down layer's operand
+// produced in the up GEMM's epilogue; consumer variant: the up layer stores its bf16 output
+// and the down layer's pre-pass applies GELU as it loads it.
+constexpr int kMlpAuto = 0, kMlpProducer = 1, kMlpConsumer = 2;
+int resolve_mlp_variant(int variant);
+size_t mlp_bf16_workspace(int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd);
+hipError_t launch_mlp_bf16(int variant, int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd, const void* X,
+                           const void* Wu, const void* LAu, const void* LBu, const void* Wd, const void* LAd,
+                           const void* LBd, float eps, void* Y, void* ws, uint16_t* dbg_x, uint8_t* dbg_idx,
+                           float* dbg_s, hipStream_t stream);
+// pieces of launch_mlp_bf16
+struct PairDown {
+  uint8_t* cvals;
+  uint8_t* cidx;
+  float* tpart;    // [H / 128, Mp, Rd]
+  double* npart;   // [H / 128, Mp, 2]
+  const void* LB;  // L_B of the down layer [Rd, H]
+  int64_t R;
+  uint16_t* dbg_x;
+  uint8_t* dbg_idx;
+};
+hipError_t launch_mlp_up_bf16(int64_t M, int64_t H, int64_t K, int64_t Ru, const void* Wu, const void* LAu,
+                              float eps, const void* ws_up, const PairDown& d, hipStream_t stream);
+hipError_t launch_prep_gelu_bf16(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB, float eps,
+                                 void* ws, uint16_t* dbg_x, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream);
+hipError_t launch_split_reduce_bf16(int64_t M, int64_t R, int ks, const float* tpart, const double* npart, float eps,
+                                    void* T, float* s, float* dbg_s, hipStream_t stream);
+
 // Allocation-free workspace: the per-device scratch array (noalloc.hip).  `mismatch` is set
 // when `stream` does not belong to the current device (no address is resolved then).
 size_t noalloc_scratch_bytes();

@@ -325,6 +325,70 @@ def bench_blocks(steps: int, warmup: int) -> dict:
     return {"M": BLOCK_M, "layers": per, "all_dense_ms": dense, "all_torch_matmul_ms": torch_ms, "models": models}
 
 
+def bench_mlp_pair(steps: int, warmup: int) -> dict:
+    """Configuration 4 as one MLP (M = 4608, 3072 -> 12288 -> 3072, R = 64 both): the fused
+    pair (rtl_mlp_fused, default variant: GELU in the down layer's pre-pass; and the variant
+    whose up GEMM epilogue produces the down operand) against the two separate layers, with
+    and without torch's exact GELU between them, and against the all-dense pair (in-library
+    dense GEMM and torch.matmul, GELU between)."""
+    import torch
+
+    import activation_sparse_gemm_amd as rtl
+    import synth
+    M, K, H, N, R = 4608, 3072, 12288, 3072, 64
+    up = synth.make_layer("mlp_up")
+    X, Wu, LAu, LBu = (to_dev(up[k]) for k in ("X", "W", "LA", "LB"))
+    Wd = to_dev(synth.to_bf16(synth.normal(4011, (N, H), std=1.0 / np.sqrt(H))))
+    LAd = to_dev(synth.to_bf16(synth.normal(4012, (N, R), std=0.02)))
+    LBd = to_dev(synth.to_bf16(synth.normal(4013, (R, H), std=0.02)))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Yu = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((rtl.rtl_mlp_fused_workspace_bytes(M, K, H, N, R, R),), dtype=torch.uint8, device="cuda")
+    wsu = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, H, K, R),), dtype=torch.uint8,
+                      device="cuda")
+    wsd = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, H, R),), dtype=torch.uint8,
+                      device="cuda")
+    Wut, Wdt = Wu.t(), Wd.t()
+    gelu = torch.nn.functional.gelu
+
+    def fused():
+        rtl.rtl_mlp_fused(X, Wu, LAu, LBu, Wd, LAd, LBd, Y=Y, workspace=ws)
+
+    def producer():
+        rtl.rtl_mlp_fused(X, Wu, LAu, LBu, Wd, LAd, LBd, Y=Y, workspace=ws, variant=rtl.RTL_MLP_PRODUCER)
+
+    def separate_gelu():
+        rtl.rtl_linear_fused(X, Wu, LAu, LBu, Y=Yu, workspace=wsu)
+        xd = gelu(Yu, approximate="none")
+        rtl.rtl_linear_fused(xd, Wd, LAd, LBd, Y=Y, workspace=wsd)
+
+    def separate():  # no activation between the layers (the down layer reads the up output)
+        rtl.rtl_linear_fused(X, Wu, LAu, LBu, Y=Yu, workspace=wsu)
+        rtl.rtl_linear_fused(Yu, Wd, LAd, LBd, Y=Y, workspace=wsd)
+
+    def dense():
+        rtl.rtl_linear_dense_ref(X, Wu, Y=Yu)
+        rtl.rtl_linear_dense_ref(gelu(Yu, approximate="none"), Wd, Y=Y)
+
+    def torch_dense():
+        torch.matmul(X, Wut, out=Yu)
+        torch.matmul(gelu(Yu, approximate="none"), Wdt, out=Y)
+
+    t = {k: time_loop(f, steps, warmup) for k, f in (("fused", fused), ("producer", producer),
+                                                     ("separate_gelu", separate_gelu),
+                                                     ("separate", separate), ("dense", dense),
+                                                     ("torch_dense", torch_dense))}
+    flops = (2 * M * H * K + 2 * M * R * (K + H)) + (2 * M * N * H + 2 * M * R * (H + N))
+    return {"workload": f"MLP pair: M={M}, {K}->{H} (GELU) ->{N}, R={R}, bf16", "fused_ms": t["fused"] * 1e3,
+            "producer_epilogue_variant_ms": t["producer"] * 1e3,
+            "separate_with_gelu_ms": t["separate_gelu"] * 1e3, "separate_no_gelu_ms": t["separate"] * 1e3,
+            "dense_with_gelu_ms": t["dense"] * 1e3, "torch_matmul_with_gelu_ms": t["torch_dense"] * 1e3,
+            "fused_tflops": flops / t["fused"] / 1e12,
+            "speedup_vs_separate_with_gelu": t["separate_gelu"] / t["fused"],
+            "speedup_vs_dense": t["dense"] / t["fused"],
+            "speedup_vs_best_dense": min(t["dense"], t["torch_dense"]) / t["fused"]}
+
+
 def copy_calibration(mib: int):
     """A plain device copy of known size, for scaling the HBM byte counters of a profile
     run: each launch reads and writes exactly `mib` MiB."""
@@ -433,6 +497,9 @@ def main():
             del r
             torch.cuda.empty_cache()
         out["layers"] = layers
+        out["mlp_pair"] = bench_mlp_pair(max(5, args.steps // 2), 3)
+        print(json.dumps({"mlp_pair": out["mlp_pair"]}), file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
         out["tiny"] = tiny_latency(args.steps, args.warmup)
         runs = None
     if args.blocks:

@@ -141,6 +141,40 @@ rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, i
                                  size_t ws_bytes, uint8_t* dbg_idx, float* dbg_s, void* stream);
 
 /*
+ * The MLP pair of a DiT block as one call ("RT-Lynx", summary page, method step 3: in
+ * Qwen-Image both MLP projections are sparsified, so the up projection's output, after the
+ * activation, is the down projection's input):
+ *   Y = layer_down(bf16(GELU(bf16(layer_up(X)))))
+ * with GELU(x) = x Phi(x) (exact erf form, evaluated in fp32) and each layer as in
+ * rtl_linear_fused (bf16 only):
+ *   up:   X [M,K],  Wu [H,K], LAu [H,Ru], LBu [Ru,K]
+ *   down:           Wd [N,H], LAd [N,Rd], LBd [Rd,H],  Y [M,N]
+ * Two variants compute the same Y:
+ *  RTL_MLP_PRODUCER: the up GEMM's epilogue forms the down layer's input and writes, in
+ *    place of the up output, the down layer's 2-of-4 selection packed as its compressed
+ *    operand, plus per-tile partial squared norms and partial rank-R products, which a
+ *    fixed-order reduction turns into the down layer's s and T / s; the down input never
+ *    reaches device memory.
+ *  RTL_MLP_CONSUMER: the up layer stores its bf16 output once (in the workspace) and the
+ *    down layer's pre-pass applies GELU to each value as it loads it.
+ *  RTL_MLP_AUTO: the library's pick, currently CONSUMER (faster on gfx950: the activation's
+ *    vector-ALU work costs less in a memory-bound pre-pass than in a GEMM epilogue).
+ * Limits: K % 64 == 0, H % 128 == 0, Ru % 32 == 0 with Ru <= 128, Rd in {0, 32, 64}.  A
+ * layer's LA and LB may be NULL when its rank is 0.  Optional outputs (NULL to skip):
+ * dbg_xd [M,H] bf16, the down layer's input as the kernels formed it; dbg_idx [M,H/4] its
+ * selection codes (layout of rtl_sparsify); dbg_s [M] the down layer's s.  The workspace
+ * size covers both variants.  Outputs must not overlap inputs or each other; calls that
+ * share a workspace must be serialised.  Validation and errors as for rtl_linear_fused.
+ */
+typedef enum { RTL_MLP_AUTO = 0, RTL_MLP_PRODUCER = 1, RTL_MLP_CONSUMER = 2 } rtl_mlp_variant;
+size_t rtl_mlp_fused_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd);
+rtl_status rtl_mlp_fused(rtl_mlp_variant variant, rtl_dtype dt, int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd,
+                         const void* X, const void* Wu, const void* LAu, const void* LBu, const void* Wd,
+                         const void* LAd, const void* LBd, rtl_tie_rule tie, float eps, void* Y,
+                         void* workspace, size_t ws_bytes, void* dbg_xd, uint8_t* dbg_idx, float* dbg_s,
+                         void* stream);
+
+/*
  * rtl_linear_fused without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments and result as rtl_linear_fused (variant AUTO) minus the

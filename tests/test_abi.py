@@ -315,3 +315,36 @@ def test_fp8_workspace_bytes():
     # the bf16 layer's workspace plus row absmax and the 8-bit operand (M*K/2 codes, M*K/32 position bytes)
     assert need >= rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, 4096, 3072, 3072, 64) + 4096 * 1536 + 4096 * 96
     assert Wb(4096, 3072, 3000, 64) == 0 and Wb(0, 3072, 3072, 64) == 0
+
+
+def test_mlp_pair_validation():
+    """rtl_mlp_fused rejects bad calls before launching anything (host stand-in buffers)."""
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    L = rtl.lib
+    M, K, H, N, R = 64, 128, 256, 64, 32
+
+    def call(dt=rtl.RTL_BF16, M=M, K=K, H=H, N=N, Ru=R, Rd=R, eps=1e-8, ws_bytes=None, **over):
+        h = Host()
+        bufs = {k: h.buf(max(n, 16))[0] for k, n in dict(X=M * K * 2, Wu=H * K * 2, LAu=H * R * 2, LBu=R * K * 2,
+                                                          Wd=N * H * 2, LAd=N * R * 2, LBd=R * H * 2,
+                                                          Y=M * N * 2).items()}
+        need = rtl.rtl_mlp_fused_workspace_bytes(64, 128, 256, 64, 32, 32)
+        bufs["ws"] = h.buf(need)[0]
+        bufs.update(over)
+        st = L.rtl_mlp_fused(0, dt, M, K, H, N, Ru, Rd, bufs["X"], bufs["Wu"], bufs["LAu"], bufs["LBu"], bufs["Wd"],
+                             bufs["LAd"], bufs["LBd"], 0, eps, bufs["Y"], bufs["ws"],
+                             need if ws_bytes is None else ws_bytes, None, None, None, None)
+        return st, h
+
+    cases = [(dict(dt=rtl.RTL_F32), "RTL_ERR_UNSUPPORTED"), (dict(H=192), "RTL_ERR_UNSUPPORTED"),
+             (dict(K=96), "RTL_ERR_UNSUPPORTED"), (dict(Rd=96), "RTL_ERR_UNSUPPORTED"),
+             (dict(M=0), "RTL_ERR_SHAPE"), (dict(Wd=None), "RTL_ERR_NULL"), (dict(LBd=None), "RTL_ERR_NULL"),
+             (dict(eps=-1.0), "RTL_ERR_ARG"), (dict(ws_bytes=16), "RTL_ERR_WORKSPACE")]
+    for over, want in cases:
+        st, h = call(**over)
+        assert st == inv[want], (over, rtl.STATUS.get(st))
+        assert h.untouched()
+    need = rtl.rtl_mlp_fused_workspace_bytes(4608, 3072, 12288, 3072, 64, 64)
+    # the up layer's workspace, the down layer's compressed operand (H/2 bf16 + H/16 bytes per
+    # row), and per-128-column-tile partials T_down (f32) and norms (f64)
+    assert need >= 4608 * (12288 + 12288 // 16) + 96 * 4608 * (64 * 4 + 16)
