@@ -29,7 +29,8 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "librtl.so")
+# RTL_LIBRARY selects another build of the same library (e.g. one with sanitized host code).
+library_path = os.environ.get("RTL_LIBRARY") or os.path.join(_PKG, "librtl.so")
 
 RTL_F32, RTL_BF16 = 0, 1
 RTL_TIE_LOWER_INDEX = 0

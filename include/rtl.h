@@ -55,10 +55,13 @@ typedef enum {
   RTL_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
 } rtl_status;
 
-typedef enum { RTL_F32 = 0, RTL_BF16 = 1 } rtl_dtype;
+/* The enums a call takes carry enumerators at both ends of the 32-bit range (the *_RANGE_*
+ * entries, not valid arguments), so that every int a caller passes is a representable
+ * value, which validation then accepts or rejects. */
+typedef enum { RTL_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1, RTL_F32 = 0, RTL_BF16 = 1, RTL_DTYPE_RANGE_MAX_ = 0x7FFFFFFF } rtl_dtype;
 
 /* Tie rule of the 2-of-4 selection: equal magnitudes favour the lower index. */
-typedef enum { RTL_TIE_LOWER_INDEX = 0 } rtl_tie_rule;
+typedef enum { RTL_TIE_RANGE_MIN_ = -0x7FFFFFFF - 1, RTL_TIE_LOWER_INDEX = 0, RTL_TIE_RANGE_MAX_ = 0x7FFFFFFF } rtl_tie_rule;
 
 /*
  * Selection, compression and rescale factor of every row (method step 1), standalone.
@@ -105,11 +108,13 @@ rtl_status rtl_linear_fused(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64
 
 /* Where the bf16 path runs the 2-of-4 selection. */
 typedef enum {
+  RTL_VARIANT_RANGE_MIN_ = -0x7FFFFFFF - 1,
   RTL_VARIANT_AUTO = 0,          /* the library's pick: currently PRECOMPRESSED, faster at
                                     every measured shape on gfx950 */
   RTL_VARIANT_PROLOGUE = 1,      /* in the A-operand prologue of the sparse-MFMA GEMM */
-  RTL_VARIANT_PRECOMPRESSED = 2  /* in the pre-pass over X, which hands the GEMM the
+  RTL_VARIANT_PRECOMPRESSED = 2, /* in the pre-pass over X, which hands the GEMM the
                                     compressed operand (kept values + positions) */
+  RTL_VARIANT_RANGE_MAX_ = 0x7FFFFFFF
 } rtl_variant;
 
 /*
@@ -166,7 +171,13 @@ rtl_status rtl_linear_fused_main(rtl_variant variant, rtl_dtype dt, int64_t M, i
  * size covers both variants.  Outputs must not overlap inputs or each other; calls that
  * share a workspace must be serialised.  Validation and errors as for rtl_linear_fused.
  */
-typedef enum { RTL_MLP_AUTO = 0, RTL_MLP_PRODUCER = 1, RTL_MLP_CONSUMER = 2 } rtl_mlp_variant;
+typedef enum {
+  RTL_MLP_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  RTL_MLP_AUTO = 0,
+  RTL_MLP_PRODUCER = 1,
+  RTL_MLP_CONSUMER = 2,
+  RTL_MLP_RANGE_MAX_ = 0x7FFFFFFF
+} rtl_mlp_variant;
 size_t rtl_mlp_fused_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd);
 rtl_status rtl_mlp_fused(rtl_mlp_variant variant, rtl_dtype dt, int64_t M, int64_t K, int64_t H, int64_t N, int64_t Ru, int64_t Rd,
                          const void* X, const void* Wu, const void* LAu, const void* LBu, const void* Wd,

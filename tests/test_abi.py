@@ -348,3 +348,22 @@ def test_mlp_pair_validation():
     # the up layer's workspace, the down layer's compressed operand (H/2 bf16 + H/16 bytes per
     # row), and per-128-column-tile partials T_down (f32) and norms (f64)
     assert need >= 4608 * (12288 + 12288 // 16) + 96 * 4608 * (64 * 4 + 16)
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="the calls pass validation and would launch kernels: machines without a GPU only")
+def test_runtime_errors_are_reported_as_rtl_err_hip():
+    """A call that passes validation on a machine without a GPU reaches the HIP runtime,
+    which fails: the status is RTL_ERR_HIP with the runtime's message (the far-apart fake
+    addresses are never dereferenced, since nothing can be launched)."""
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    L = rtl.lib
+    X, W, LA, LB, Y, ws = (ctypes.c_void_p((i + 1) << 40) for i in range(6))
+    need = rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, 64, 64, 128, 32)
+    st = L.rtl_linear_fused(rtl.RTL_BF16, 64, 64, 128, 32, X, W, LA, LB, 0, 1e-8, Y, ws, need, None, None, None)
+    assert st == inv["RTL_ERR_HIP"], rtl.STATUS.get(st)
+    assert "launch" in L.rtl_last_error().decode()
+    st = L.rtl_linear_fused_noalloc(rtl.RTL_BF16, 64, 64, 128, 32, X, W, LA, LB, 0, 1e-8, Y, None, None, None)
+    assert st == inv["RTL_ERR_HIP"], rtl.STATUS.get(st)
+    st = L.rtl_linear_dense_ref(rtl.RTL_BF16, 64, 64, 128, X, W, Y, None)
+    assert st == inv["RTL_ERR_HIP"], rtl.STATUS.get(st)
