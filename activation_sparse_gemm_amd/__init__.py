@@ -24,6 +24,7 @@ __all__ = [
     "rtl_linear_fused_prep", "rtl_linear_fused_main", "rtl_linear_fused_noalloc", "rtl_linear_dense_ref",
     "RTL_NOALLOC_SCRATCH_BYTES", "rtl_mlp_fused", "rtl_mlp_fused_workspace_bytes", "RTL_MLP_AUTO",
     "RTL_MLP_PRODUCER", "RTL_MLP_CONSUMER", "RTL_VARIANT_AUTO", "RTL_VARIANT_PROLOGUE", "RTL_VARIANT_PRECOMPRESSED",
+    "RTL_VARIANT_STREAM_K",
     "rtl_status_string", "rtl_version",
     "rtl_quantize_weight_fp8", "rtl_linear_fused_fp8", "rtl_linear_fused_fp8_workspace_bytes",
 ]
@@ -34,9 +35,9 @@ library_path = os.environ.get("RTL_LIBRARY") or os.path.join(_PKG, "librtl.so")
 
 RTL_F32, RTL_BF16 = 0, 1
 RTL_TIE_LOWER_INDEX = 0
-RTL_VARIANT_AUTO, RTL_VARIANT_PROLOGUE, RTL_VARIANT_PRECOMPRESSED = 0, 1, 2
+RTL_VARIANT_AUTO, RTL_VARIANT_PROLOGUE, RTL_VARIANT_PRECOMPRESSED, RTL_VARIANT_STREAM_K = 0, 1, 2, 3
 EPS = 1e-8
-RTL_NOALLOC_SCRATCH_BYTES = 128 << 20  # include/rtl.h
+RTL_NOALLOC_SCRATCH_BYTES = 192 << 20  # include/rtl.h
 RTL_MLP_AUTO, RTL_MLP_PRODUCER, RTL_MLP_CONSUMER = 0, 1, 2
 STATUS = {0: "RTL_OK", 1: "RTL_ERR_NULL", 2: "RTL_ERR_SHAPE", 3: "RTL_ERR_ALIGN", 4: "RTL_ERR_UNSUPPORTED",
           5: "RTL_ERR_ARG", 6: "RTL_ERR_WORKSPACE", 7: "RTL_ERR_HIP"}

@@ -13,6 +13,9 @@
 //  accumulators as one extra K = R MFMA slice with T / s (formed by the pre-pass in double
 //  precision) as its A operand, and the single store writes Y = s * acc; so the M x N
 //  low-rank product never reaches device memory, and s * (T / s) L_A^T = T L_A^T.
+#include <atomic>
+#include <random>
+
 #include "lora_lds.h"
 
 namespace rtl {
@@ -679,6 +682,255 @@ __device__ __forceinline__ void produce_down_operand(const GemmArgs& a, const f3
 // reduction turns into T_down / s and s.  X_d itself never reaches device memory.
 constexpr int kHalfThreads = 256;
 
+// What half_tile does with its K range of an output tile.
+constexpr int kRoleTile = 0;     // the whole of K: the epilogue stores Y
+constexpr int kRolePartial = 1;  // a leading part of K (stream-K): the fp32 partial accumulators
+                                 // go to the workgroup's slot, then its flag is set
+constexpr int kRoleFinal = 2;    // the trailing part of K (stream-K): the partials of the
+                                 // workgroups w_first..w_self-1 are added in that order, then
+                                 // the epilogue
+
+// LDS of a half-kernel workgroup: the 4-buffer W ring, then (192-wide tiles) the rank-R
+// operands or (other widths) L_A.
+template <int TW>
+constexpr int half_lds_bytes() {
+  return 4 * TW * 128 + (TW == 192 ? kLoraT + TW * 128 + 1024 : TW * 128);
+}
+
+// The stream-K kernel's tile: one output tile (tm, tn) over K steps kb + [0, len) (taken
+// from step kb + koff on, and round) by the four waves of a half-kernel workgroup, `wl`
+// its LDS, with one of the roles above.  It is half_kernel's tile code made to take a K
+// range and a role; half_kernel keeps its own copy, because at 256 accumulators and 256
+// VGPRs per lane the register allocation of the shared version measured 3.5% slower on
+// whole tiles.
+template <int TW>
+__device__ __forceinline__ void sk_tile(const GemmArgs& a, const SkArgs& sk, uint8_t* wl, int tm, int tn, int kb,
+                                        int len, int koff, int role, int w_first, int w_self) {
+  static_assert(TW == 256, "stream-K runs 256-wide tiles");
+  constexpr int NB = TW / 16;                   // 16-column blocks per wave
+  constexpr int WLD = TW * 8 / kHalfThreads;    // 16-byte W chunks per thread per K step
+  constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
+  // One workgroup per CU; L_A is staged in LDS past the ring (R <= 64) at the start, and
+  // the rank-R branch with T / s from memory and the single store Y = s * acc come at the
+  // end.  A partial K range leaves both to the workgroup that finishes the tile.
+  uint8_t* const lora = wl + WBUF * TW * 128;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * TW;
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int KT = (int)(K / kBK);
+
+  // W staging: thread t moves rows t/8 + 32i, i < WLD; columns past N read as zeros.
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(a.W + n0 * K, (N - n0) * K * 2);
+  const int srow = tid >> 3;
+
+  // The wave's 64-row panel of the compressed operand (register order).
+  struct AF {
+    u32x4 v[4];
+    uint32_t iw[2];
+  };
+  const int64_t pan = min((int64_t)tm * 4 + wave, (int64_t)a.n_panels - 1);
+  const __amdgpu_buffer_rsrc_t cvres = make_rsrc(a.cvals + cvals_off(pan, KT, 0), (int64_t)KT * 4096);
+  const __amdgpu_buffer_rsrc_t cires = make_rsrc(a.cidx + cidx_off(pan, KT, 0), (int64_t)KT * 512);
+  // Part p < 4: kept values of row block p; part 4: the position words.
+  auto load_frag_part = [&](int kt, AF& f, int part) {
+    if (part < 4) {
+      f.v[part] = __builtin_amdgcn_raw_buffer_load_b128(cvres, (uint32_t)(lane * 16 + part * 1024), kt * 4096, 0);
+    } else {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(cires, (uint32_t)(lane * 8), kt * 512, 0);
+      f.iw[0] = w[0];
+      f.iw[1] = w[1];
+    }
+  };
+  auto load_frag = [&](int kt, AF& f) {
+#pragma unroll
+    for (int part = 0; part < 5; part++) load_frag_part(kt, f, part);
+  };
+  auto read_b = [&](int buf, int nb) {
+    const uint8_t* base = wl + buf * TW * 128;
+    const int n = nb * 16 + r16;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
+    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto kp = [&](int i) {
+    const int k = min(i, len - 1) + koff;
+    return kb + (k >= len ? k - len : k);
+  };
+  // Direct-to-LDS W staging (DTL): the i-th 16-byte load of lane l in wave w lands at
+  // byte (4 i + w) * 1024 + 16 l of its stage, row n = 32 i + 8 w + l / 8 at swizzled
+  // position l % 8, which sw_off assigns to logical chunk (l % 8) ^ (n % 8).
+  const uint32_t d_voff = (uint32_t)(srow * K * 2 + 16 * ((lane & 7) ^ (srow & 7)));
+  auto dtl_w = [&](int kt, int buf, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wres, (__attribute__((address_space(3))) void*)(wl + buf * TW * 128 + (4 * i + wave) * 1024), 16, d_voff,
+        (int)(i * 32 * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
+  };
+  // DTL step kt on ring buffer kt % 4: blocks 0-4 load one part each of A for step
+  // kt + AAH, each of the last WLD blocks loads one chunk of W stage kt + 3 into buffer
+  // (kt + 3) % 4 (last read in step kt - 1); before the barrier each wave waits for its
+  // loads of stage kt + 2, so the next step's first B fragments, read before the barrier,
+  // find their buffer complete.
+  // A fragments are loaded AAH steps ahead, B fragments read BQ column blocks ahead.
+  constexpr int AAH = 1, BQ = 2, NSET = AAH + 1, PER = 4;
+  u32x8 bp[BQ];
+  auto step_dtl = [&](int kt, int buf, const AF& cur, AF& anext) {
+    const int nbuf = buf == WBUF - 1 ? 0 : buf + 1, dbuf = buf == 0 ? WBUF - 1 : buf - 1;
+    u32x8 bq[BQ + 1];
+#pragma unroll
+    for (int j = 0; j < BQ; j++) bq[j] = bp[j];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      if (nb + BQ < NB) bq[(nb + BQ) % (BQ + 1)] = read_b(buf, nb + BQ);
+      if (nb < 5) load_frag_part(kp(kt + AAH), anext, nb);
+      if (nb >= NB - WLD) dtl_w(kp(kt + 3), dbuf, nb - (NB - WLD));
+      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % (BQ + 1)]);
+      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0]), bv, acc[0][nb],
+                                                             (int)cur.iw[0], 0, 0);
+      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1]), bv, acc[1][nb],
+                                                             (int)cur.iw[0], 0, 1);
+      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2]), bv, acc[2][nb],
+                                                             (int)cur.iw[1], 0, 0);
+      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3]), bv, acc[3][nb],
+                                                             (int)cur.iw[1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < BQ; j++) bp[j] = read_b(nbuf, j);
+    wait_vmcnt<5 + WLD>();
+    barrier_nofence();
+  };
+
+  AF fa[NSET];
+  // (L_A into LDS, then) A of the first steps, then W stages 0-2 (A before W, as in the
+  // loop); stages 0 and 1 complete before the first B reads.
+  const bool lalds = a.R > 0 && a.R <= 64 && role != kRolePartial;
+  if (lalds) lora_stage_la<TW, 4>(lora, a, n0, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < AAH; j++) load_frag(kp(j), fa[j]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int st = 0; st < 3; st++)
+#pragma unroll
+    for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+  wait_vmcnt<WLD>();
+  barrier_nofence();
+#pragma unroll
+  for (int j = 0; j < BQ; j++) bp[j] = read_b(0, j);
+  // Ring buffers cycle with period 4, A sets with period AAH + 1: whole periods in the
+  // loop (no exit in its body), then the rest.
+  int kt = 0;
+  for (; kt + PER <= len; kt += PER) {
+#pragma unroll
+    for (int j = 0; j < PER; j++) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
+  }
+#pragma unroll
+  for (int j = 0; j < PER - 1; j++)
+    if (kt + j < len) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
+  wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
+
+  // Stream-K: slot w of the partials holds the accumulators of workgroup w in register
+  // order (16 bytes per lane per (wave, row block, column block)), so every lane moves its
+  // own registers with full 16-byte accesses.  Partials and flags are written and read
+  // with device-scope cache policy (the form of relaxed device-scope atomics): coherent
+  // across the XCDs' L2 caches without writing back or invalidating whole caches, which
+  // would cost the other workgroups their cached operands.  Ordering: each thread waits
+  // for its partial stores to complete, then the barrier, then the flag; the reader sees
+  // the flag, then the barrier, then loads the partials.
+  constexpr int kDevScope = 16;  // cache policy: device-scope coherence
+  auto slot_rsrc = [&](int w) {
+    return make_rsrc(sk.part + (int64_t)w * (kBM * TW), (int64_t)kBM * TW * 4);
+  };
+  auto slot_off = [&](int rb, int nb) { return (uint32_t)((((wave * 4 + rb) * NB + nb) * 64 + lane) * 16); };
+  if (role == kRolePartial) {
+    const __amdgpu_buffer_rsrc_t r = slot_rsrc(w_self);
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][nb]), r, slot_off(rb, nb), 0,
+                                               kDevScope);
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(sk.flag + w_self, sk.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (role == kRoleFinal) {
+    // The workgroups before this one in K order set their flags after writing their
+    // partials and never wait on a later workgroup, so the wait ends; the poll count is
+    // bounded all the same (the kernel would then finish with a wrong tile, not hang).
+    if (tid == 0) {
+      for (int w = w_first; w < w_self; w++) {
+        for (int it = 0; it < (1 << 24); it++) {
+          if (__hip_atomic_load(sk.flag + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sk.epoch) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+    __syncthreads();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        f32x4 p = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(w_first), slot_off(rb, nb),
+                                                                                  0, kDevScope));
+        for (int w = w_first + 1; w < w_self; w++)
+          p += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(slot_rsrc(w), slot_off(rb, nb), 0,
+                                                                               kDevScope));
+        acc[rb][nb] = p + acc[rb][nb];
+      }
+  }
+
+  // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
+  // accumulator rows 16rb + 4q + j (lane 4q + j); the rank-R slice acc += (T / s) L_A^T;
+  // then Y = s * acc.
+  float s_row[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+    const int64_t row = m0 + 64 * wave + 16 * rb + r16;
+    s_row[rb] = a.s[row < M ? row : M - 1];
+  }
+  const int64_t R = a.R;
+  for (int kk = 0; kk < (int)(R / 32); kk++) {
+    u32x4 ta[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+      const int64_t row = m0 + 64 * wave + 16 * rb + r16;
+      ta[rb] = *reinterpret_cast<const u32x4*>(a.T + (row < M ? row : M - 1) * R + 32 * kk + 8 * q);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const int64_t col = n0 + nb * 16 + r16;
+      const u32x4 la = lalds ? lora_la_lds(lora, (int)R, nb * 16 + r16, kk, q)
+                             : *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++)
+        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
+                                                              __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
+    }
+  }
+  float s_acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
+  __syncthreads();  // the LDS ring is free
+  store_tile<4, NB>(a.Y, M, N, m0 + 64 * wave, n0, wl + wave * 16 * (2 * TW + 16), lane,
+                    [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
+}
+
 template <int TW, bool PROD = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads),
                           amdgpu_waves_per_eu(TW >= 192 ? 1 : 2, TW >= 192 ? 1 : 2)))
@@ -877,6 +1129,90 @@ void half_kernel(const GemmArgs a) {
                     [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
 }
 
+// Stream-K GEMM ("RT-Lynx: Putting the GEMM Sparsity In a Right Way for Diffusion
+// Models", summary page, method step 4, item (4)) for fewer tiles than CUs: P workgroups,
+// one per CU; the K steps of all tiles, in tile order, are split into P contiguous ranges
+// of nearly equal length (shorter than a tile), so no CU idles for want of a tile.  A
+// range covers the end of one tile and/or the start of the next.  The start of the next
+// (a range that ends inside a tile) is done first and published as a partial; the
+// workgroup whose range holds a tile's last K step then adds the partials of the
+// workgroups before it, in workgroup order (the order of their K ranges), to its own and
+// stores the tile, so Y does not depend on timing.
+template <int TW>
+__global__ __attribute__((amdgpu_flat_work_group_size(kHalfThreads, kHalfThreads), amdgpu_waves_per_eu(1, 1)))
+void sk_kernel(const GemmArgs a, const SkArgs sk) {
+  static_assert(TW == 256, "stream-K runs the 256-wide half kernel");
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[half_lds_bytes<TW>()];
+  const int w = blockIdx.x;
+  const int KT = (int)(a.K / kBK);
+  // Workgroup v's range of K steps starts at start(v); step i lies in the range of
+  // workgroup range_of(i).
+  auto start = [&](int64_t v) { return v * sk.base + min(v, sk.extra); };
+  auto range_of = [&](int64_t i) {
+    const int64_t big = sk.extra * (sk.base + 1);
+    return (int)(i < big ? i / (sk.base + 1) : sk.extra + (i - big) / sk.base);
+  };
+  const int64_t i0 = start(w), i1 = start(w + 1);
+  if (i1 <= i0) return;
+  const int t0 = (int)(i0 / KT), t1 = (int)((i1 - 1) / KT);
+  const int b0 = (int)(i0 % KT), e1 = (int)((i1 - 1) % KT) + 1;
+  const bool part = e1 < KT;             // the range ends inside tile t1
+  const bool fin = !(part && t0 == t1);  // the range holds the last K step of tile t0
+  if (part) {
+    int tm, tn;
+    tile_from_index(t1, a.tiles_m, a.tiles_n, tm, tn);
+    const int kb = t0 == t1 ? b0 : 0;
+    sk_tile<TW>(a, sk, wl, tm, tn, kb, e1 - kb, 0, kRolePartial, 0, w);
+  }
+  if (fin) {
+    if (part) __syncthreads();  // another wave may still read the LDS ring of the partial
+    int tm, tn;
+    tile_from_index(t0, a.tiles_m, a.tiles_n, tm, tn);
+    sk_tile<TW>(a, sk, wl, tm, tn, b0, KT - b0, b0 == 0 ? (tm + tn) % 8 % KT : 0, b0 == 0 ? kRoleTile : kRoleFinal,
+                         b0 == 0 ? 0 : range_of((int64_t)t0 * KT), w);
+  }
+}
+
+// Stream-K plan for the 256-wide half kernel, one workgroup per CU, when there are fewer
+// tiles than CUs: each CU gets ceil(tiles KT / P) K steps instead of a whole tile's KT.
+// It is taken when that, plus kSkFixupSteps for publishing and adding the partials
+// (measured), beats KT by 3%.
+constexpr int kSkWorkgroups = 256;  // CUs of the chip
+constexpr int kSkFixupSteps = 12;
+struct SkPlan {
+  int64_t base, extra;
+};
+static bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan& p) {
+  const int64_t P = kSkWorkgroups, KT = K / kBK;
+  if (choose_tn(M, N) != 256 || K <= 8192) return false;  // shapes of the 256-wide half kernel
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + 255) / 256);
+  if (tiles >= P) return false;
+  const int64_t steps = tiles * KT;
+  p.base = steps / P;
+  p.extra = steps % P;
+  if (p.base < 8) return false;
+  return (double)((steps + P - 1) / P) + kSkFixupSteps < 0.97 * (double)KT;
+}
+
+// Flags of the stream-K partials hold the epoch of the launch that set them: a per-process
+// random start, then one step per launch, so flags left in a workspace by earlier
+// launches never match.
+static uint64_t next_sk_epoch() {
+  static std::atomic<uint64_t> epoch{[] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ 1;
+  }()};
+  uint64_t e;
+  do e = epoch.fetch_add(1); while (e == 0);
+  return e;
+}
+
+size_t sk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  SkPlan p;
+  if (!sk_plan(M, N, K, p)) return 0;
+  return align256((size_t)kSkWorkgroups * 8) + (size_t)kSkWorkgroups * kBM * 256 * 4;
+}
+
 static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W, const void* LA,
                           void* Y, float eps, int tn_width) {
   GemmArgs g{};
@@ -922,7 +1258,8 @@ static void launch_main_tn(bool comp, GemmArgs g, uint8_t* dbg_idx, hipStream_t 
 hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,
                             const void* LA, float eps, void* Y, const void* ws, uint8_t* dbg_idx, float* dbg_s,
                             hipStream_t stream) {
-  const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
+  const int rv = resolve_variant_bf16(variant, M, N, K);
+  const bool comp = rv != kVariantPrologue;
   const WsLayout L = ws_layout(M, K, R, comp);
   const uint8_t* base = (const uint8_t*)ws;
   const int tn = choose_tn(M, N);
@@ -950,6 +1287,18 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   // workload layers: K = 12288 and 13824 6-7% faster in the 4-wave kernel, K = 5120 3%
   // slower.
   if (comp && tn == 256 && K > 8192) {
+    SkPlan sp;
+    if (rv == kVariantStreamK && sk_plan(M, N, K, sp)) {
+      uint8_t* skb = const_cast<uint8_t*>(base) + align256(ws_layout(M, K, R, true).total);
+      SkArgs k{};
+      k.flag = reinterpret_cast<uint64_t*>(skb);
+      k.part = reinterpret_cast<float*>(skb + align256((size_t)kSkWorkgroups * 8));
+      k.epoch = next_sk_epoch();
+      k.base = sp.base;
+      k.extra = sp.extra;
+      hipLaunchKernelGGL((sk_kernel<256>), dim3(kSkWorkgroups), dim3(kHalfThreads), 0, stream, g, k);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((half_kernel<256>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream, g);
     return hipGetLastError();
   }

@@ -12,17 +12,20 @@ constexpr int kBM = 256;  // rows per GEMM workgroup
 // remap so that each XCD gets a contiguous run of logical tiles, and walk logical tiles
 // in groups of kGroupM tile-rows so that an XCD's tiles share X rows and W columns in L2.
 constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_from_index(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int width = kGroupM * tiles_n;
+  const int first_m = (t / width) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  tm = first_m + (t % width) % gsz;
+  tn = (t % width) / gsz;
+}
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   const int w = blockIdx.x;
   const int xcd = w & 7, slot = w >> 3;
   const int per = total >> 3, rem = total & 7;
   const int t = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-  const int width = kGroupM * tiles_n;
-  const int first_m = (t / width) * kGroupM;
-  const int gsz = min(tiles_m - first_m, kGroupM);
-  tm = first_m + (t % width) % gsz;
-  tn = (t % width) / gsz;
+  tile_from_index(t, tiles_m, tiles_n, tm, tn);
 }
 
 struct GemmArgs {
@@ -52,6 +55,19 @@ struct GemmArgs {
   int64_t d_R;
   uint16_t* d_dbg_x;
   uint8_t* d_dbg_idx;
+};
+
+// Stream-K decomposition (sk_kernel), a separate kernel argument (extra fields in GemmArgs
+// cost the tile kernels registers): the K steps of all tiles, in tile order, are dealt out
+// in contiguous ranges, base + 1 to each of the first `extra` workgroups and base to the
+// rest.  A workgroup whose range ends inside a tile leaves its fp32 partial accumulators
+// in slot w of `part` ([P][kBM][TW] f32, accumulator register order) and sets flag[w] to
+// `epoch`.
+struct SkArgs {
+  float* part;
+  uint64_t* flag;
+  uint64_t epoch;
+  int64_t base, extra;
 };
 
 // Output tile store through LDS: the accumulator layout (lane = column 16nb + r16, rows

@@ -9,7 +9,7 @@
 
 namespace rtl {
 
-constexpr size_t kNoallocBytes = (size_t)128 << 20;
+constexpr size_t kNoallocBytes = (size_t)192 << 20;
 static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
 
 namespace {

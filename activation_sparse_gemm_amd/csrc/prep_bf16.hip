@@ -406,19 +406,20 @@ static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const 
 // streaming the compressed operand is faster at every measured shape.
 int resolve_variant_bf16(int variant, int64_t M, int64_t N, int64_t K) {
   (void)M; (void)N; (void)K;
-  if (variant == kVariantPrologue || variant == kVariantPrecompressed) return variant;
+  if (variant == kVariantPrologue || variant == kVariantPrecompressed || variant == kVariantStreamK) return variant;
   return kVariantPrecompressed;
 }
 
 size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R) {
-  (void)N;
   const WsLayout a = ws_layout(M, K, R, false), b = ws_layout(M, K, R, true);
-  return a.total > b.total ? a.total : b.total;
+  const size_t sk = sk_workspace_bytes(M, N, K);
+  const size_t bt = sk ? align256(b.total) + sk : b.total;
+  return a.total > bt ? a.total : bt;
 }
 
 hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
                             float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream) {
-  const bool comp = resolve_variant_bf16(variant, M, N, K) == kVariantPrecompressed;
+  const bool comp = resolve_variant_bf16(variant, M, N, K) != kVariantPrologue;
   const WsLayout L = ws_layout(M, K, R, comp);
   uint8_t* base = (uint8_t*)ws;
   PrepArgs p{};

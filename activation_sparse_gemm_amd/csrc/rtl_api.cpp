@@ -122,7 +122,8 @@ rtl_status check_fused(Stage stage, rtl_variant variant, rtl_dtype dt, int64_t M
                        bool own_ws = false) {
   rtl_status st;
   if ((st = check_dtype(dt)) != RTL_OK) return st;
-  if (variant != RTL_VARIANT_AUTO && variant != RTL_VARIANT_PROLOGUE && variant != RTL_VARIANT_PRECOMPRESSED)
+  if (variant != RTL_VARIANT_AUTO && variant != RTL_VARIANT_PROLOGUE && variant != RTL_VARIANT_PRECOMPRESSED &&
+      variant != RTL_VARIANT_STREAM_K)
     return fail(RTL_ERR_UNSUPPORTED, "unsupported variant %d", (int)variant);
   if (stage != kWhole && dt != RTL_BF16) return fail(RTL_ERR_UNSUPPORTED, "the split launches are bf16 only");
   if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);

@@ -15,9 +15,13 @@ hipError_t launch_sparsify(int dt, int64_t M, int64_t K, const void* X, float ep
 
 // bf16 path.  Variants of the fused layer: the 2-of-4 selection in the GEMM's A-operand
 // prologue, or in the pre-pass over X with the GEMM reading the compressed operand.
-constexpr int kVariantAuto = 0, kVariantPrologue = 1, kVariantPrecompressed = 2;
+constexpr int kVariantAuto = 0, kVariantPrologue = 1, kVariantPrecompressed = 2, kVariantStreamK = 3;
 int resolve_variant_bf16(int variant, int64_t M, int64_t N, int64_t K);
 size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R);
+// Stream-K GEMM (variant kVariantStreamK): the workspace it needs past the pre-pass
+// outputs of the pre-compressed variant (placed at align256(ws_layout(M, K, R,
+// true).total)); 0 when the shape runs whole tiles only.
+size_t sk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
                             float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream);
 hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,

@@ -114,6 +114,18 @@ typedef enum {
   RTL_VARIANT_PROLOGUE = 1,      /* in the A-operand prologue of the sparse-MFMA GEMM */
   RTL_VARIANT_PRECOMPRESSED = 2, /* in the pre-pass over X, which hands the GEMM the
                                     compressed operand (kept values + positions) */
+  RTL_VARIANT_STREAM_K = 3,      /* PRECOMPRESSED, with a stream-K GEMM (summary page,
+                                    method step 4, item (4)) where the output has fewer
+                                    256 x 256 tiles than the chip has CUs and K > 8192:
+                                    the K steps of all tiles are split evenly over one
+                                    workgroup per CU, and each tile is finished by adding
+                                    the fp32 partials of the workgroups before it in a
+                                    fixed order (Y is the same on every run).  Elsewhere
+                                    identical to PRECOMPRESSED.  AUTO does not pick it:
+                                    on gfx950 the split ranges walk K out of step, so the
+                                    tiles stop sharing operand reads in L2, which costs
+                                    more than the idle CUs it saves (measured at M = 4608,
+                                    N = 3072, K = 12288: 266 us against 167 us). */
   RTL_VARIANT_RANGE_MAX_ = 0x7FFFFFFF
 } rtl_variant;
 
@@ -198,7 +210,7 @@ rtl_status rtl_mlp_fused(rtl_mlp_variant variant, rtl_dtype dt, int64_t M, int64
  * threads) race, and the caller must serialise them.  The array keeps the last call's
  * intermediate results; nothing in it needs to start at zero.
  */
-#define RTL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+#define RTL_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
 rtl_status rtl_linear_fused_noalloc(rtl_dtype dt, int64_t M, int64_t N, int64_t K, int64_t R,
                                     const void* X, const void* W, const void* LA, const void* LB,
                                     rtl_tie_rule tie, float eps, void* Y, uint8_t* dbg_idx,

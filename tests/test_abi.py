@@ -177,9 +177,13 @@ def test_fused_variant_and_stage_checks():
     Y, _ = h.buf(64 * 64 * 4)
     ws, _ = h.buf(1 << 20)
     L = rtl.lib
-    # unknown variant
+    # unknown variant; the stream-K variant is known (here it fails only on the workspace)
     assert L.rtl_linear_fused_ex(7, rtl.RTL_BF16, 64, 64, 128, 0, X, W, None, None, 0, 1e-8, Y, ws, 1 << 20,
                                  None, None, None) == inv["RTL_ERR_UNSUPPORTED"]
+    assert L.rtl_linear_fused_ex(4, rtl.RTL_BF16, 64, 64, 128, 0, X, W, None, None, 0, 1e-8, Y, ws, 1 << 20,
+                                 None, None, None) == inv["RTL_ERR_UNSUPPORTED"]
+    assert L.rtl_linear_fused_ex(rtl.RTL_VARIANT_STREAM_K, rtl.RTL_BF16, 64, 64, 128, 0, X, W, None, None, 0, 1e-8,
+                                 Y, ws, 16, None, None, None) == inv["RTL_ERR_WORKSPACE"]
     # the split launches are bf16 only
     assert L.rtl_linear_fused_prep(0, rtl.RTL_F32, 64, 64, 128, 0, X, None, 0, 1e-8, ws, 1 << 20, None, None,
                                    None) == inv["RTL_ERR_UNSUPPORTED"]

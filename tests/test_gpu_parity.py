@@ -282,6 +282,42 @@ def test_fused_256_tiles_every_rank(K, R):
     check_tiles(synth.make_layer(lay, seed_base=9290 + R + K), "fused-256")
 
 
+# Stream-K: fewer 256 x 256 tiles than CUs with K > 8192.  1540 x 8000 is 7 x 32 = 224
+# tiles (4 rows in the last tile-row, 64 columns in the last tile-column); K = 8256 is 129 K
+# steps, dealt out 113 or 112 to each of the 256 workgroups, so nearly every tile is
+# finished by one workgroup from the partial of the one before.  Every rank class (none,
+# staged L_A, L_A from memory).  The call is repeated bit for bit with a fresh workspace
+# full of random bytes (flags left in memory never match a launch's epoch) and with the
+# same workspace again.
+@pytest.mark.parametrize("R", [0, 64, 128])
+def test_fused_stream_k(R):
+    M, N, K = 1540, 8000, 8256
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=9490 + R)
+    Y, _ = check_tiles(d, "stream-k", variant=rtl.RTL_VARIANT_STREAM_K)
+    dev = {k: to_dev(d[k]) for k in ("X", "W", "LA", "LB")}
+    need = rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g)
+    Y2 = rtl.rtl_linear_fused(dev["X"], dev["W"], dev["LA"], dev["LB"], workspace=ws, variant=rtl.RTL_VARIANT_STREAM_K)
+    Y3 = rtl.rtl_linear_fused(dev["X"], dev["W"], dev["LA"], dev["LB"], workspace=ws, variant=rtl.RTL_VARIANT_STREAM_K)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+    assert torch.equal(Y.view(torch.int16), Y3.view(torch.int16))
+
+
+def test_fused_stream_k_mlp_down():
+    """The stream-K variant at the text-to-image MLP's down-projection shape (4608 x 3072,
+    K = 12288: 216 tiles, 162 K steps per workgroup): Y in full against the oracle, and the
+    selection codes and s against the whole-tile variant's."""
+    d = layer("mlp_down")
+    log(f"[stream-k] mlp_down M={d['M']} N={d['N']} K={d['K']} R={d['R']}")
+    Y, dbg_idx, dbg_s = run_fused(d, variant=rtl.RTL_VARIANT_STREAM_K)
+    Yref, _ = oracle_layer("mlp_down")
+    check_y(f64(to_host(Y), "bf16"), Yref, "bf16", "mlp_down stream-k")
+    assert np.array_equal(to_host(dbg_idx), oracle.sparsify(d["X"])["idx"])
+
+
 # Irregular shapes drawn from a fixed seed (so the cases are the same on every run): M and N
 # with ragged tails, every supported R, K up to 20 steps of 64 (whole and partial turns of
 # the GEMM's register ring), both variants.  Shapes stay small enough for the full oracle.

@@ -69,7 +69,8 @@ def test_noalloc_two_calls_second_smaller_match_workspace_entry_point():
 
 
 def test_noalloc_largest_supported_shape_and_fp32():
-    # mlp_down's shape needs 71 MiB of workspace (inside the 128 MiB array); then the fp32
+    # mlp_down's shape needs 135 MiB of workspace (it has room for the stream-K variant's
+    # partials too), inside the 192 MiB array; then the fp32
     # path (no workspace) through the same entry point
     d, dev = _inputs(4608, 3072, 12288, 64, "bf16", 12003)
     need = rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, 4608, 3072, 12288, 64)
