@@ -56,8 +56,10 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Pre-pass decomposition.  Rows are padded to 128.  When 128-row workgroups (8 waves)
 // already cover the chip, each takes a whole row tile and all of K; otherwise 64-row
-// workgroups (4 waves, two per CU) split K so that about 512 of them run, each with at
-// least kPrepMinSteps K steps, and a small kernel sums the splits.
+// workgroups (4 waves, two per CU) split K as many ways as still lets all of them run at
+// once (at most 512 workgroups, a split of at least kPrepMinSteps K steps), and a small
+// kernel sums the splits.  (Rounding the split count up instead, to reach 512 or more,
+// measured 13-16% slower at M = 4608: the last splits then wait for a second round.)
 constexpr int kPrepMinSteps = 4;
 struct PrepSplit {
   int waves, ks, kts;
@@ -66,7 +68,7 @@ inline PrepSplit prep_split(int64_t M, int64_t K) {
   const int64_t Mp = padded_rows(M), KT = K / kBK;
   if (Mp / kPrepRows >= 256) return PrepSplit{8, 1, (int)KT};
   const int64_t tiles = Mp / 64;
-  int64_t ks = (512 + tiles - 1) / tiles;
+  int64_t ks = 512 / tiles;
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, KT / kPrepMinSteps));
   ks = std::max<int64_t>(ks, 1);
   const int64_t kts = (KT + ks - 1) / ks;

@@ -187,6 +187,8 @@ class LayerRun:
             t["prep"] = time_loop(self.prep, steps, warmup)
             t["main"] = time_loop(self.main, steps, warmup)
             t["prologue_variant"] = time_loop(lambda: self.fused(rtl.RTL_VARIANT_PROLOGUE), max(3, steps // 4), 2)
+            if stream_k_applies(self.M, self.N, self.K):
+                t["stream_k"] = time_loop(lambda: self.fused(rtl.RTL_VARIANT_STREAM_K), max(3, steps // 4), 2)
             if fp8 and self.K % 128 == 0:
                 import torch
                 Wq, sw = rtl.rtl_quantize_weight_fp8(self.W)  # a static weight, quantised once
@@ -196,6 +198,12 @@ class LayerRun:
                                                                       workspace=ws8), steps, warmup)
                 del Wq, sw, ws8
         return t
+
+
+def stream_k_applies(M: int, N: int, K: int) -> bool:
+    """Shapes on which RTL_VARIANT_STREAM_K runs the stream-K GEMM (the library's rule):
+    fewer 256 x 256 output tiles than the 256 CUs, and K > 8192."""
+    return -(-M // 256) * -(-N // 256) < 256 and K > 8192
 
 
 def prep_bytes(M: int, K: int, R: int) -> int:
@@ -225,6 +233,8 @@ def layer_line(run: LayerRun, t: dict) -> dict:
                     prep_frac_hbm=prep_bytes(run.M, run.K, run.R) / t["prep"] / PEAK_HBM,
                     gemm_frac_mfma=gemm_alg_flops(run.M, run.N, run.K, run.R) / t["main"] / PEAK_BF16_DENSE,
                     prologue_variant_ms=t["prologue_variant"] * 1e3)
+        if "stream_k" in t:
+            line["stream_k_variant_ms"] = t["stream_k"] * 1e3
         if "fp8" in t:
             line["fp8"] = {"ms": t["fp8"] * 1e3, "tflops": f / t["fp8"] / 1e12,
                            "speedup_vs_dense_bf16": t["dense"] / t["fp8"], "speedup_vs_bf16_layer": t["layer"] / t["fp8"],
