@@ -11,7 +11,8 @@
 namespace rtl {
 
 constexpr int kFT = 32;    // tile rows and columns
-constexpr int kFK = 32;    // K per step
+constexpr int kFK = 128;   // K per step: its loads are all in flight together
+constexpr int kFG = kFK / 32;  // groups of 4 per loader thread per step
 constexpr int kFMaxR = 128;
 
 template <bool SPARSE>
@@ -25,12 +26,12 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
   __shared__ float Ws[kFT][kFK + 1];
   __shared__ float Bs[kFMaxR][kFK + 1];  // L_B tile
   __shared__ float Ts[kFT][kFMaxR];
-  __shared__ double red[2][kFT][kFK / 4];
+  __shared__ double red[2][kFT][8];
   __shared__ float srow[kFT];
 
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.y * kFT, n0 = (int64_t)blockIdx.x * kFT;
-  // loader role: one group of 4 per thread, tile row lr, group lg
+  // loader role: tile row lr, groups lg, lg + 8, ... of each step
   const int lr = tid >> 3, lg = tid & 7;
   const int64_t xr = m0 + lr < M ? m0 + lr : M - 1;
   const int64_t wr = n0 + lr < N ? n0 + lr : N - 1;
@@ -45,27 +46,43 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
   for (int i = 0; i < kFT * kFMaxR / 256; i++) tacc[i] = 0.f;
   double nx2 = 0.0, nt2 = 0.0;
 
+  constexpr int kLBMax = kFMaxR * (kFK / 4) / 256;  // 16-byte L_B loads per thread per step, at most
   for (int64_t k0 = 0; k0 < K; k0 += kFK) {
-    // X group: selection (tile prologue)
-    {
-      const int64_t k = k0 + 4 * lg;
-      uint32_t x[4] = {0u, 0u, 0u, 0u};
-      if (k < K) {
-        const u32x4 d = *reinterpret_cast<const u32x4*>(X + xr * K + k);
-        x[0] = d[0]; x[1] = d[1]; x[2] = d[2]; x[3] = d[3];
+    // The step's loads first (X and W groups of this thread, its share of the L_B tile), all
+    // in flight together; then the selection (tile prologue) and the LDS tiles.
+    u32x4 xd[kFG], wd[kFG], bd[SPARSE ? kLBMax : 1];
+#pragma unroll
+    for (int j = 0; j < kFG; j++) {
+      const int64_t k = k0 + 4 * (lg + 8 * j);
+      xd[j] = k < K ? *reinterpret_cast<const u32x4*>(X + xr * K + k) : u32x4{0u, 0u, 0u, 0u};
+      wd[j] = k < K ? *reinterpret_cast<const u32x4*>(W + wr * K + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (SPARSE) {
+#pragma unroll
+      for (int i = 0; i < kLBMax; i++) {
+        const int e = tid + 256 * i, rr = e / (kFK / 4), gg = e % (kFK / 4);
+        const int64_t kb = k0 + 4 * gg;
+        bd[i] = e < (int)R * (kFK / 4) && kb < K ? *reinterpret_cast<const u32x4*>(LB + (int64_t)rr * K + kb)
+                                                 : u32x4{0u, 0u, 0u, 0u};
       }
+    }
+#pragma unroll
+    for (int j = 0; j < kFG; j++) {
+      const int kl = 4 * (lg + 8 * j);
+      const int64_t k = k0 + kl;
+      const uint32_t x[4] = {xd[j][0], xd[j][1], xd[j][2], xd[j][3]};
       float kept[4] = {__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3])};
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        Xs[lr][4 * lg + j] = kept[j];
-        nx2 = fma((double)kept[j], (double)kept[j], nx2);
+      for (int jj = 0; jj < 4; jj++) {
+        Xs[lr][kl + jj] = kept[jj];
+        nx2 = fma((double)kept[jj], (double)kept[jj], nx2);
       }
       if (SPARSE) {
         int lo, hi;
         select_f32(x, lo, hi);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          if (j != lo && j != hi) kept[j] = 0.f;
+        for (int jj = 0; jj < 4; jj++)
+          if (jj != lo && jj != hi) kept[jj] = 0.f;
         const float vlo = __uint_as_float(x[lo]), vhi = __uint_as_float(x[hi]);
         nt2 = fma((double)vlo, (double)vlo, nt2);
         nt2 = fma((double)vhi, (double)vhi, nt2);
@@ -73,20 +90,17 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
           dbg_idx[(m0 + lr) * (K / 4) + k / 4] = (uint8_t)(lo | (hi << 2));
       }
 #pragma unroll
-      for (int j = 0; j < 4; j++) As[lr][4 * lg + j] = kept[j];
-      const int64_t kw = k0 + 4 * lg;
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (kw < K) wv = *reinterpret_cast<const u32x4*>(W + wr * K + kw);
+      for (int jj = 0; jj < 4; jj++) As[lr][kl + jj] = kept[jj];
 #pragma unroll
-      for (int j = 0; j < 4; j++) Ws[lr][4 * lg + j] = __uint_as_float(wv[j]);
-      if (SPARSE) {
-        for (int e = tid; e < (int)R * (kFK / 4); e += 256) {
-          const int rr = e / (kFK / 4), gg = e % (kFK / 4);
-          const int64_t kb = k0 + 4 * gg;
-          u32x4 bv = {0u, 0u, 0u, 0u};
-          if (kb < K) bv = *reinterpret_cast<const u32x4*>(LB + (int64_t)rr * K + kb);
+      for (int jj = 0; jj < 4; jj++) Ws[lr][kl + jj] = __uint_as_float(wd[j][jj]);
+    }
+    if (SPARSE) {
 #pragma unroll
-          for (int j = 0; j < 4; j++) Bs[rr][4 * gg + j] = __uint_as_float(bv[j]);
+      for (int i = 0; i < kLBMax; i++) {
+        const int e = tid + 256 * i, rr = e / (kFK / 4), gg = e % (kFK / 4);
+        if (e < (int)R * (kFK / 4)) {
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) Bs[rr][4 * gg + jj] = __uint_as_float(bd[i][jj]);
         }
       }
     }
@@ -126,7 +140,7 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
     __syncthreads();
     if (tid < kFT) {
       double a = 0.0, t = 0.0;
-      for (int g = 0; g < kFK / 4; g++) {
+      for (int g = 0; g < 8; g++) {
         a += red[0][tid][g];
         t += red[1][tid][g];
       }

@@ -431,6 +431,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import synth
+    if args.workload != "video_block" and synth.LAYERS[args.workload].dtype != "bf16":
+        print("--workload takes the video block or a bf16 layer; the fp32 Tiny layer is latency-bound and "
+              "reported in microseconds under the default run's \"tiny\" key.", file=sys.stderr)
+        sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
