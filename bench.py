@@ -91,10 +91,12 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.05) -> float:
+def time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.05, per_step: list | None = None) -> float:
     """Mean seconds per call of fn over `steps` calls after `warmup` calls (and at least
     `min_warm_s` seconds of them, so the clocks have settled), timed with events on the
-    current stream (the stream the library launches on), synchronised on both sides."""
+    current stream (the stream the library launches on), synchronised on both sides.  With
+    `per_step`, an event is also recorded between calls (a stream marker, no
+    synchronisation) and the seconds of each call are appended to it."""
     import torch
     t0 = time.perf_counter()
     n = 0
@@ -105,11 +107,17 @@ def time_loop(fn, steps: int, warmup: int, min_warm_s: float = 0.05) -> float:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)] if per_step is not None else []
     start.record()
-    for _ in range(steps):
+    for i in range(steps):
         fn()
+        if per_step is not None and i < steps - 1:
+            marks[i].record()
     end.record()
     torch.cuda.synchronize()
+    if per_step is not None:
+        ev = [start] + marks + [end]
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(steps))
     return start.elapsed_time(end) / 1e3 / steps
 
 
@@ -459,7 +467,8 @@ def main():
             r.torch_dense()
 
     # the timed step: exactly `warmup` untimed passes, then exactly `steps` passes
-    t_step = time_loop(step, args.steps, args.warmup, min_warm_s=0.0)
+    step_times = []
+    t_step = time_loop(step, args.steps, args.warmup, min_warm_s=0.0, per_step=step_times)
     t_dense = time_loop(dense_step, args.steps, args.warmup)
     t_torch = time_loop(torch_step, args.steps, args.warmup)
     per = {r.name: r.times(max(5, args.steps // 2), 3, fp8=True) for r in runs}
@@ -487,6 +496,7 @@ def main():
         "metric": METRIC, "value": value / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "step_ms_median": float(np.median(step_times)) * 1e3, "step_ms_min": min(step_times) * 1e3,
         "config": {"workload": wl, "M": M, "layers": {r.name: {"K": r.K, "N": r.N, "R": r.R,
                                                                "path": "dense" if r.dense_only else "fused"}
                                                       for r in runs}},
