@@ -79,6 +79,22 @@ const char* rtl_status_string(rtl_status st) {
   return "unknown rtl_status";
 }
 
+}  // extern "C"
+
+namespace {
+// Extents the kernels reach with 32-bit offsets from the start of a tile or row block: K up
+// to kMaxK, and fewer than 2^31 output tiles of 256 x 128 (M and N each below 2^31).
+constexpr int64_t kMaxK = (int64_t)1 << 22;
+rtl_status check_extent(int64_t M, int64_t N, int64_t K) {
+  if (K > kMaxK) return fail(RTL_ERR_SHAPE, "K must be at most %lld (K=%lld)", (long long)kMaxK, (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || ((M + 255) / 256) * ((N + 127) / 128) > INT32_MAX)
+    return fail(RTL_ERR_SHAPE, "M x N is too large (M=%lld N=%lld)", (long long)M, (long long)N);
+  return RTL_OK;
+}
+}  // namespace
+
+extern "C" {
+
 rtl_status rtl_sparsify(rtl_dtype dt, int64_t M, int64_t K, const void* X, rtl_tie_rule tie, float eps,
                         void* vals, uint8_t* idx, float* s, void* stream) {
   rtl_status st;
@@ -86,6 +102,7 @@ rtl_status rtl_sparsify(rtl_dtype dt, int64_t M, int64_t K, const void* X, rtl_t
   if (tie != RTL_TIE_LOWER_INDEX) return fail(RTL_ERR_UNSUPPORTED, "unsupported tie rule %d", (int)tie);
   if (M <= 0 || K <= 0 || K % 4 != 0) return fail(RTL_ERR_SHAPE, "need M > 0, K > 0, K %% 4 == 0 (M=%lld K=%lld)",
                                                   (long long)M, (long long)K);
+  if ((st = check_extent(M, 1, K)) != RTL_OK) return st;
   if (!X || !vals || !idx || !s) return fail(RTL_ERR_NULL, "X, vals, idx and s are required");
   if (misaligned(X) || misaligned(vals) || misaligned(idx) || misaligned(s))
     return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -130,6 +147,7 @@ rtl_status check_fused(Stage stage, rtl_variant variant, rtl_dtype dt, int64_t M
   if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
     return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
                 (long long)N, (long long)K, (long long)R);
+  if ((st = check_extent(M, N, K)) != RTL_OK) return st;
   const bool uses_w = stage != kPrep, uses_lb = stage != kMain;
   if (!X || (uses_w && (!W || !Y)) || (R > 0 && ((uses_w && !LA) || (uses_lb && !LB))))
     return fail(RTL_ERR_NULL, "X, W, Y (and LA, LB when R > 0) are required");
@@ -261,6 +279,7 @@ rtl_status rtl_mlp_fused(rtl_mlp_variant variant, rtl_dtype dt, int64_t M, int64
   if (M <= 0 || K <= 0 || H <= 0 || N <= 0 || Ru < 0 || Rd < 0)
     return fail(RTL_ERR_SHAPE, "need M, K, H, N > 0 and ranks >= 0 (M=%lld K=%lld H=%lld N=%lld)", (long long)M,
                 (long long)K, (long long)H, (long long)N);
+  if ((st = check_extent(M, H, K)) != RTL_OK || (st = check_extent(M, N, H)) != RTL_OK) return st;
   if (K % 64 != 0 || H % 128 != 0 || Ru % 32 != 0 || Ru > 128 || (Rd != 0 && Rd != 32 && Rd != 64))
     return fail(RTL_ERR_UNSUPPORTED,
                 "the MLP pair needs K %% 64 == 0, H %% 128 == 0, Ru %% 32 == 0 with Ru <= 128, Rd in {0, 32, 64} "
@@ -299,6 +318,7 @@ rtl_status rtl_linear_dense_ref(rtl_dtype dt, int64_t M, int64_t N, int64_t K, c
   if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0)
     return fail(RTL_ERR_SHAPE, "need M, N, K > 0 and K %% 4 == 0 (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
                 (long long)K);
+  if ((st = check_extent(M, N, K)) != RTL_OK) return st;
   if (!X || !W || !Y) return fail(RTL_ERR_NULL, "X, W and Y are required");
   if (misaligned(X) || misaligned(W) || misaligned(Y)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (dt == RTL_BF16 && K % 64 != 0) return fail(RTL_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0 (K=%lld)", (long long)K);
@@ -320,6 +340,8 @@ extern "C" {
 rtl_status rtl_quantize_weight_fp8(int64_t N, int64_t K, const void* W, uint8_t* Wq, float* sw, void* stream) {
   if (N <= 0 || K <= 0 || K % 8 != 0)
     return fail(RTL_ERR_SHAPE, "need N > 0, K > 0, K %% 8 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  rtl_status st;
+  if ((st = check_extent(1, N, K)) != RTL_OK) return st;
   if (!W || !Wq || !sw) return fail(RTL_ERR_NULL, "W, Wq and sw are required");
   if (misaligned(W) || misaligned(Wq) || misaligned(sw)) return fail(RTL_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   const size_t wb = (size_t)N * K * 2, qb = (size_t)N * K, sb = (size_t)N * 4;
@@ -341,6 +363,7 @@ rtl_status rtl_linear_fused_fp8(int64_t M, int64_t N, int64_t K, int64_t R, cons
   if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0 || R < 0)
     return fail(RTL_ERR_SHAPE, "need M, N, K > 0, K %% 4 == 0, R >= 0 (M=%lld N=%lld K=%lld R=%lld)", (long long)M,
                 (long long)N, (long long)K, (long long)R);
+  if ((st = check_extent(M, N, K)) != RTL_OK) return st;
   if (!X || !Wq || !sw || !Y || (R > 0 && (!LA || !LB)))
     return fail(RTL_ERR_NULL, "X, Wq, sw, Y (and LA, LB when R > 0) are required");
   if (misaligned(X) || misaligned(Wq) || misaligned(sw) || misaligned(Y) || misaligned(LA) || misaligned(LB) ||

@@ -32,7 +32,12 @@
  *    overflows them (s > 0 for every nonzero row).  The products (X~ W^T, X L_B^T and Y)
  *    accumulate in fp32 and must lie in its range.
  *  - eps must lie in [0, 1] (RTL_ERR_ARG otherwise); the method uses 1e-8.
- *  - Thread-safe: no global mutable state apart from the thread-local error message.
+ *  - Extents: K <= 2^22, and M and N below 2^31 with fewer than 2^31 output tiles of
+ *    256 x 128 (RTL_ERR_SHAPE otherwise): the kernels address each tile's rows with 32-bit
+ *    offsets from the tile's start.
+ *  - Thread-safe: the only global mutable state is the thread-local error message, an
+ *    atomic counter that stamps stream-K launches (RTL_VARIANT_STREAM_K) and the
+ *    per-device address of the allocation-free call's device array (resolved once).
  */
 #ifndef RTL_H
 #define RTL_H
@@ -47,7 +52,7 @@ extern "C" {
 typedef enum {
   RTL_OK = 0,
   RTL_ERR_NULL = 1,        /* a required pointer is NULL */
-  RTL_ERR_SHAPE = 2,       /* M, N or K <= 0, K % 4 != 0, R < 0 */
+  RTL_ERR_SHAPE = 2,       /* M, N or K <= 0, K % 4 != 0, R < 0, or beyond the extents */
   RTL_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned */
   RTL_ERR_UNSUPPORTED = 4, /* tie rule, dtype, or a shape limit of the bf16 kernels */
   RTL_ERR_ARG = 5,         /* eps outside [0, 1] or NaN; an output overlaps an input */

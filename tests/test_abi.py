@@ -199,6 +199,28 @@ def test_fused_variant_and_stage_checks():
     assert h.untouched()
 
 
+def test_extents_beyond_32_bit_tile_offsets_are_rejected():
+    """K above 2^22, or an M x N with 2^31 or more 256 x 128 output tiles, is a shape error
+    on every entry point (validation only: fake device addresses, no HIP call)."""
+    inv = {v: k for k, v in rtl.STATUS.items()}
+    L = rtl.lib
+    fake = [ctypes.c_void_p((i + 1) << 40) for i in range(6)]
+    X, W, LA, LB, Y, ws = fake
+    bigK = (1 << 22) + 64
+    assert L.rtl_linear_fused(rtl.RTL_BF16, 64, 64, bigK, 0, X, W, None, None, 0, 1e-8, Y, ws, 1 << 30, None, None,
+                              None) == inv["RTL_ERR_SHAPE"]
+    assert "at most" in L.rtl_last_error().decode()
+    assert L.rtl_linear_dense_ref(rtl.RTL_BF16, 64, 64, bigK, X, W, Y, None) == inv["RTL_ERR_SHAPE"]
+    assert L.rtl_sparsify(rtl.RTL_BF16, 64, bigK, X, 0, 1e-8, W, Y, LA, None) == inv["RTL_ERR_SHAPE"]
+    huge = 1 << 30  # (2^30 / 256) x (2^30 / 128) = 2^33 tiles
+    assert L.rtl_linear_dense_ref(rtl.RTL_BF16, huge, huge, 64, X, W, Y, None) == inv["RTL_ERR_SHAPE"]
+    assert L.rtl_linear_fused(rtl.RTL_F32, huge, huge, 64, 0, X, W, None, None, 0, 1e-8, Y, ws, 1 << 30, None, None,
+                              None) == inv["RTL_ERR_SHAPE"]
+    # at the limit the same calls pass validation (they then fail on the workspace size only)
+    assert L.rtl_linear_fused(rtl.RTL_BF16, 64, 64, 1 << 22, 0, X, W, None, None, 0, 1e-8, Y, ws, 16, None, None,
+                              None) == inv["RTL_ERR_WORKSPACE"]
+
+
 def test_fused_rejects_aliasing():
     inv = {v: k for k, v in rtl.STATUS.items()}
     h = Host()
