@@ -1173,25 +1173,22 @@ void sk_kernel(const GemmArgs a, const SkArgs sk) {
   }
 }
 
-// Stream-K plan for the 256-wide half kernel, one workgroup per CU, when there are fewer
-// tiles than CUs: each CU gets ceil(tiles KT / P) K steps instead of a whole tile's KT.
-// It is taken when that, plus kSkFixupSteps for publishing and adding the partials
-// (measured), beats KT by 3%.
+// Stream-K plan for the 256-wide half kernel (shapes with K > 8192 that take 256-wide
+// tiles), one workgroup per CU, when there are fewer tiles than CUs: each CU gets
+// ceil(tiles KT / P) K steps instead of a whole tile's KT, at least 8 of them.
 constexpr int kSkWorkgroups = 256;  // CUs of the chip
-constexpr int kSkFixupSteps = 12;
 struct SkPlan {
   int64_t base, extra;
 };
 static bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan& p) {
   const int64_t P = kSkWorkgroups, KT = K / kBK;
-  if (choose_tn(M, N) != 256 || K <= 8192) return false;  // shapes of the 256-wide half kernel
+  if (choose_tn(M, N) != 256 || K <= 8192) return false;
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + 255) / 256);
   if (tiles >= P) return false;
   const int64_t steps = tiles * KT;
   p.base = steps / P;
   p.extra = steps % P;
-  if (p.base < 8) return false;
-  return (double)((steps + P - 1) / P) + kSkFixupSteps < 0.97 * (double)KT;
+  return p.base >= 8;
 }
 
 // Flags of the stream-K partials hold the epoch of the launch that set them: a per-process

@@ -209,9 +209,11 @@ class LayerRun:
 
 
 def stream_k_applies(M: int, N: int, K: int) -> bool:
-    """Shapes on which RTL_VARIANT_STREAM_K runs the stream-K GEMM (the library's rule):
-    fewer 256 x 256 output tiles than the 256 CUs, and K > 8192."""
-    return -(-M // 256) * -(-N // 256) < 256 and K > 8192
+    """Shapes on which RTL_VARIANT_STREAM_K runs the stream-K GEMM (the library's rule for
+    the shapes that take 256-wide tiles): fewer 256 x 256 output tiles than the 256 CUs,
+    K > 8192, and at least 8 K steps of 64 per CU."""
+    tiles = -(-M // 256) * -(-N // 256)
+    return tiles < 256 and K > 8192 and tiles * (K // 64) // 256 >= 8
 
 
 def prep_bytes(M: int, K: int, R: int) -> int:

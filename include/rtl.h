@@ -120,8 +120,10 @@ typedef enum {
   RTL_VARIANT_PRECOMPRESSED = 2, /* in the pre-pass over X, which hands the GEMM the
                                     compressed operand (kept values + positions) */
   RTL_VARIANT_STREAM_K = 3,      /* PRECOMPRESSED, with a stream-K GEMM (summary page,
-                                    method step 4, item (4)) where the output has fewer
-                                    256 x 256 tiles than the chip has CUs and K > 8192:
+                                    method step 4, item (4)) where the output takes
+                                    256-wide tiles, has fewer 256 x 256 tiles than the
+                                    chip has CUs, K > 8192, and every CU gets at least 8
+                                    K steps of 64 (tiles * K / 64 >= 2048):
                                     the K steps of all tiles are split evenly over one
                                     workgroup per CU, and each tile is finished by adding
                                     the fp32 partials of the workgroups before it in a
