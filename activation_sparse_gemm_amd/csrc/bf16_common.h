@@ -76,9 +76,10 @@ inline PrepSplit prep_split(int64_t M, int64_t K) {
 }
 
 // Workspace: T (or T / s) [Mp,R] bf16 | s [Mp] f32 | (pre-compressed) values, position
-// words | (K split) partial T [ks,Mp,R] f32, partial squared norms [ks,Mp,2] f64.
+// words | (K split) partial T [ks,Mp,R] f32, partial squared norms [ks,Mp,2] f64, one
+// 64-bit flag per pre-pass workgroup [ks,Mp/64].
 struct WsLayout {
-  size_t t, norm, cvals, cidx, tpart, npart, total;
+  size_t t, norm, cvals, cidx, tpart, npart, pflag, total;
 };
 inline WsLayout ws_layout(int64_t M, int64_t K, int64_t R, bool comp) {
   const int64_t Mp = padded_rows(M);
@@ -91,7 +92,8 @@ inline WsLayout ws_layout(int64_t M, int64_t K, int64_t R, bool comp) {
   L.cidx = L.cvals + (comp ? align256((size_t)Mp * (K / 2) * 2) : 0);
   L.tpart = L.cidx + (comp ? align256((size_t)(Mp / kPanel) * (K / kBK) * 512) : 0);
   L.npart = L.tpart + align256((size_t)(parts * Mp * R * 4));
-  L.total = L.npart + align256((size_t)(parts * Mp * 2 * 8));
+  L.pflag = L.npart + align256((size_t)(parts * Mp * 2 * 8));
+  L.total = L.pflag + align256((size_t)(parts * (Mp / 64) * 8));
   return L;
 }
 

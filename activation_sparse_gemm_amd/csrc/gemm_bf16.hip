@@ -1191,10 +1191,7 @@ static bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan& p) {
   return p.base >= 8;
 }
 
-// Flags of the stream-K partials hold the epoch of the launch that set them: a per-process
-// random start, then one step per launch, so flags left in a workspace by earlier
-// launches never match.
-static uint64_t next_sk_epoch() {
+uint64_t next_launch_epoch() {
   static std::atomic<uint64_t> epoch{[] {
     std::random_device rd;
     return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ 1;
@@ -1290,7 +1287,7 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
       SkArgs k{};
       k.flag = reinterpret_cast<uint64_t*>(skb);
       k.part = reinterpret_cast<float*>(skb + align256((size_t)kSkWorkgroups * 8));
-      k.epoch = next_sk_epoch();
+      k.epoch = next_launch_epoch();
       k.base = sp.base;
       k.extra = sp.extra;
       hipLaunchKernelGGL((sk_kernel<256>), dim3(kSkWorkgroups), dim3(kHalfThreads), 0, stream, g, k);

@@ -23,6 +23,9 @@ struct PrepArgs {
   float* dbg_s;       // [M] or null
   float* tpart;       // [ks, Mp, R] partial T when ks > 1
   double* npart;      // [ks, Mp, 2] partial squared norms when ks > 1
+  uint64_t* pflag;    // [ks, Mp / 64] flags: the last split sums the partials in the launch
+                      // (null: a separate reduction does, from the [ks, Mp, R] layout)
+  uint64_t epoch;     // this launch's flag stamp
   int ks;             // K splits
   int kts;            // K steps per split
   int fold;           // write T / s (formed in double precision) instead of T
@@ -38,7 +41,8 @@ struct PrepArgs {
 // step passes through LDS once per workgroup and is shared by its rows.  X and L_B
 // are loaded three steps ahead.  The squared norms ||X||^2 and ||X~||^2 are summed in
 // double precision.  With several K splits the partial T and norms go to the workspace and
-// prep_reduce_kernel sums them in a fixed order.  COMPRESS writes the compressed operand;
+// either the last split of the row tile sums them in the same launch (pflag set) or
+// prep_reduce_kernel does, both in split order.  Workgroup id = split * row tiles + row tile.  COMPRESS writes the compressed operand;
 // without it (the prologue variant) the selection still runs, for ||X~||^2.  AMAX (the
 // FP8 layer) also takes each row's largest magnitude, the scale of its 8-bit quantisation.
 // ACT (the down layer of the MLP pair) applies GELU to every loaded value first (bf16 in,
@@ -54,9 +58,11 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
   const int q = lane >> 4, r16 = lane & 15;
   const int64_t K = a.K;
   const int KT = (int)(K / kBK);
-  const int split = blockIdx.y;
+  const int gx = (int)(gridDim.x / a.ks);  // row tiles
+  const int split = (int)blockIdx.x / gx;
+  const int bx = (int)blockIdx.x - split * gx;
   const int kt0 = split * a.kts, nk = min(a.kts, KT - kt0);
-  const int64_t rbk = (int64_t)blockIdx.x * PW + wave;  // global 16-row block
+  const int64_t rbk = (int64_t)bx * PW + wave;  // global 16-row block
   const int64_t row = rbk * 16 + r16;
   const bool row_ok = row < a.M;
   const int64_t p = rbk >> 2;
@@ -190,30 +196,8 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
   }
   const float axv = __uint_as_float(amax << 16);
-  if (a.ks == 1) {
-    if (q == 0) {
-      if (AMAX) a.ax[row] = axv;
-      const float sv = scale_from_norms(nx2, nt2, a.eps);
-      a.s[row] = sv;
-      if (a.dbg_s != nullptr && row_ok) a.dbg_s[row] = sv;
-    }
-    // T rows 4q + j of the block, column cb*16 + r16 (accumulator layout), rounded to bf16;
-    // with `fold`, T / s, the factor 1 / s of row 4q + j taken from lane 4q + j in double.
-    double inv[4] = {1.0, 1.0, 1.0, 1.0};
-    if (a.fold) {
-      const double iv = inv_scale_from_norms(nx2, nt2, a.eps);
-#pragma unroll
-      for (int j = 0; j < 4; j++) inv[j] = __shfl(iv, 4 * q + j, 64);
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const float t = a.fold ? (float)((double)tacc[cb][j] * inv[j]) : tacc[cb][j];
-        a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(t);
-      }
-  } else {
-    const int64_t Mp = (int64_t)gridDim.x * 16 * PW;
+  if (a.ks > 1 && (AMAX || a.pflag == nullptr)) {
+    const int64_t Mp = (int64_t)gx * 16 * PW;
     if (q == 0) {
       a.npart[(split * Mp + row) * 2 + 0] = nx2;
       a.npart[(split * Mp + row) * 2 + 1] = nt2;
@@ -223,7 +207,113 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     for (int cb = 0; cb < CB; cb++)
 #pragma unroll
       for (int j = 0; j < 4; j++) a.tpart[(split * Mp + rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = tacc[cb][j];
+    return;
   }
+  if (a.ks > 1) {
+    // The last split of the row tile finishes it.  The other splits store their partial T
+    // (register order: 16 bytes per lane and column block, [split][row tile][wave][cb]
+    // [lane]) and squared norms ([split][row tile][row] as two doubles), then set their flag
+    // to the launch's stamp.  The last split waits for those flags, adds the partials in
+    // split order and its own last, and goes on as an unsplit workgroup.  It waits only on
+    // lower workgroup ids, which are dispatched before it, so the wait ends; the polls
+    // share a bound all the same (the launch would then finish with wrong rows, not hang).
+    // Partials and flags use device-scope cache policy (the form relaxed device-scope
+    // atomics take): coherent across the XCDs' L2 caches without cache-wide write-backs.
+    // Ordering: stores complete (wait), barrier, flag; flag seen, barrier, loads.
+    typedef double f64x2 __attribute__((ext_vector_type(2)));
+    constexpr int kDevScope = 16;
+    auto t_rsrc = [&](int sp) {
+      return make_rsrc(a.tpart + ((int64_t)sp * gx + bx) * (16 * PW * R), (int64_t)16 * PW * R * 4);
+    };
+    auto n_rsrc = [&](int sp) {
+      return make_rsrc(a.npart + ((int64_t)sp * gx + bx) * (16 * PW * 2), (int64_t)16 * PW * 16);
+    };
+    auto t_off = [&](int cb) { return (uint32_t)(((wave * (CB > 0 ? CB : 1) + cb) * 64 + lane) * 16); };
+    const uint32_t n_off = (uint32_t)((wave * 16 + r16) * 16);
+    if (split < a.ks - 1) {
+      const __amdgpu_buffer_rsrc_t tr = t_rsrc(split);
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, tacc[cb]), tr, t_off(cb), 0, kDevScope);
+      if (q == 0) {
+        const f64x2 nn = {nx2, nt2};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, nn), n_rsrc(split), n_off, 0, kDevScope);
+      }
+      asm volatile("" ::: "memory");
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(a.pflag + blockIdx.x, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (wave == 0) {  // lane i polls the flag of split s0 + i, all in flight together
+      int polls = 1 << 22;
+      for (int s0 = 0; s0 < a.ks - 1; s0 += 64) {
+        const int sp = s0 + lane;
+        bool seen = sp >= a.ks - 1;
+        for (;;) {
+          if (!seen)
+            seen = __hip_atomic_load(a.pflag + (int64_t)sp * gx + bx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   a.epoch;
+          if (__all(seen) || --polls <= 0) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+    __syncthreads();
+    asm volatile("" ::: "memory");
+    f32x4 tsum[CB > 0 ? CB : 1];
+#pragma unroll
+    for (int cb = 0; cb < (CB > 0 ? CB : 1); cb++) tsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    double xs = 0.0, ts = 0.0;
+    constexpr int BS = CB <= 4 ? 8 : 4;  // splits per batch of loads, all in flight together
+    for (int s0 = 0; s0 < a.ks - 1; s0 += BS) {
+      f32x4 v[BS][CB > 0 ? CB : 1];
+      f64x2 nv[BS];
+#pragma unroll
+      for (int u = 0; u < BS; u++) {
+        const int sp = min(s0 + u, a.ks - 2);
+        const __amdgpu_buffer_rsrc_t tr = t_rsrc(sp);
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+          v[u][cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, t_off(cb), 0, kDevScope));
+        nv[u] = __builtin_bit_cast(f64x2, __builtin_amdgcn_raw_buffer_load_b128(n_rsrc(sp), n_off, 0, kDevScope));
+      }
+#pragma unroll
+      for (int u = 0; u < BS; u++)
+        if (s0 + u < a.ks - 1) {
+#pragma unroll
+          for (int cb = 0; cb < CB; cb++) tsum[cb] += v[u][cb];
+          xs += nv[u][0];
+          ts += nv[u][1];
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) tacc[cb] = tsum[cb] + tacc[cb];
+    nx2 = xs + nx2;
+    nt2 = ts + nt2;
+  }
+  // The whole row tile's sums: s, and T or T / s.
+  if (q == 0) {
+    if (AMAX) a.ax[row] = axv;
+    const float sv = scale_from_norms(nx2, nt2, a.eps);
+    a.s[row] = sv;
+    if (a.dbg_s != nullptr && row_ok) a.dbg_s[row] = sv;
+  }
+  // T rows 4q + j of the block, column cb*16 + r16 (accumulator layout), rounded to bf16;
+  // with `fold`, T / s, the factor 1 / s of row 4q + j taken from lane 4q + j in double.
+  double inv[4] = {1.0, 1.0, 1.0, 1.0};
+  if (a.fold) {
+    const double iv = inv_scale_from_norms(nx2, nt2, a.eps);
+#pragma unroll
+    for (int j = 0; j < 4; j++) inv[j] = __shfl(iv, 4 * q + j, 64);
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float t = a.fold ? (float)((double)tacc[cb][j] * inv[j]) : tacc[cb][j];
+      a.T[(rbk * 16 + 4 * q + j) * R + cb * 16 + r16] = (uint16_t)f32_to_bf16_bits(t);
+    }
 }
 
 // One item of the K-split reduction of prep_kernel's partials, summed in split order:
@@ -359,7 +449,7 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const PrepArgs a, const P
 template <bool AMAX, bool ACT = false>
 static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const PrepSplit& sp, int64_t R,
                                 hipStream_t stream, bool reduce = true) {
-  const dim3 grid((unsigned)(Mp / (16 * sp.waves)), (unsigned)sp.ks), block(64 * sp.waves);
+  const dim3 grid((unsigned)(Mp / (16 * sp.waves) * sp.ks)), block(64 * sp.waves);
 #define RTL_PREP(C, RC)                                                                                \
   do {                                                                                                 \
     if (sp.waves == 8) hipLaunchKernelGGL((prep_kernel<C, RC, 8, AMAX, ACT>), grid, block, 0, stream, p); \
@@ -394,7 +484,7 @@ static void launch_prep_kernels(const PrepArgs& p, bool comp, int64_t Mp, const 
     }
   }
 #undef RTL_PREP
-  if (sp.ks > 1 && reduce) {
+  if (sp.ks > 1 && reduce && p.pflag == nullptr) {
     const int64_t items = Mp * (R >= 4 ? R / 4 : 1);
     const dim3 rgrid((unsigned)((items + 255) / 256)), rblock(256);
     hipLaunchKernelGGL(prep_reduce_kernel, rgrid, rblock, 0, stream, p, Mp);
@@ -434,6 +524,10 @@ hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
   p.s = (float*)(base + L.norm);
   p.dbg_s = dbg_s;
   p.fold = 1;  // the bf16 GEMMs add (T / s) L_A^T and store s * acc
+  if (sp.ks > 1) {
+    p.pflag = (uint64_t*)(base + L.pflag);
+    p.epoch = next_launch_epoch();
+  }
   if (comp) {
     p.cvals = base + L.cvals;
     p.cidx = base + L.cidx;
@@ -462,6 +556,10 @@ hipError_t launch_prep_gelu_bf16(int64_t M, int64_t N, int64_t K, int64_t R, con
   p.s = (float*)(base + L.norm);
   p.dbg_s = dbg_s;
   p.fold = 1;
+  if (sp.ks > 1) {
+    p.pflag = (uint64_t*)(base + L.pflag);
+    p.epoch = next_launch_epoch();
+  }
   p.cvals = base + L.cvals;
   p.cidx = base + L.cidx;
   p.dbg_idx = dbg_idx;

@@ -22,6 +22,10 @@ size_t fused_bf16_workspace(int64_t M, int64_t N, int64_t K, int64_t R);
 // outputs of the pre-compressed variant (placed at align256(ws_layout(M, K, R,
 // true).total)); 0 when the shape runs whole tiles only.
 size_t sk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Stamp for the flags by which one workgroup of a launch tells another that its partial
+// results are in the workspace: a per-process random start, then one step per call, never
+// 0, so flags left in a workspace by earlier launches do not match.
+uint64_t next_launch_epoch();
 hipError_t launch_prep_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* LB,
                             float eps, void* ws, uint8_t* dbg_idx, float* dbg_s, hipStream_t stream);
 hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_t R, const void* X, const void* W,

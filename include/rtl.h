@@ -36,7 +36,8 @@
  *    256 x 128 (RTL_ERR_SHAPE otherwise): the kernels address each tile's rows with 32-bit
  *    offsets from the tile's start.
  *  - Thread-safe: the only global mutable state is the thread-local error message, an
- *    atomic counter that stamps stream-K launches (RTL_VARIANT_STREAM_K) and the
+ *    atomic counter that stamps the launches whose workgroups hand partial sums to one
+ *    another through the workspace (the K-split pre-pass, the stream-K GEMM) and the
  *    per-device address of the allocation-free call's device array (resolved once).
  */
 #ifndef RTL_H
