@@ -39,8 +39,10 @@ struct PrepArgs {
 // row (k = 16q..16q+15 of a step), which serve both the selection (four groups of 4) and,
 // read as two 8-wide K slices, the A operand of the rank-R product; the L_B slice of each
 // step passes through LDS once per workgroup and is shared by its rows.  X and L_B
-// are loaded three steps ahead.  The squared norms ||X||^2 and ||X~||^2 are summed in
-// double precision.  With several K splits the partial T and norms go to the workspace and
+// are loaded three steps ahead.  The squared norms ||X||^2 and ||X~||^2: each lane sums its
+// 16 values of a K step in fp32 (packed dot products) and adds that to a double sum, as
+// are the sums across lanes and splits; a row whose total lies outside [2^-80, 2^100] is
+// summed again in double over all of K at the end (the FP8 layer sums in double throughout).  With several K splits the partial T and norms go to the workspace and
 // either the last split of the row tile sums them in the same launch (pflag set) or
 // prep_reduce_kernel does, both in split order.  Workgroup id = split * row tiles + row tile.  COMPRESS writes the compressed operand;
 // without it (the prologue variant) the selection still runs, for ||X~||^2.  AMAX (the
@@ -122,8 +124,15 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     }
     const u32x4 xv0 = valid ? x0 : z, xv1 = valid ? x1 : z;
     const uint32_t w8[8] = {xv0[0], xv0[1], xv0[2], xv0[3], xv1[0], xv1[1], xv1[2], xv1[3]};
+    if (AMAX) {
 #pragma unroll
-    for (int g = 0; g < 8; g++) nx2 = sq2_f64(w8[g], nx2);
+      for (int g = 0; g < 8; g++) nx2 = sq2_f64(w8[g], nx2);
+    } else {
+      float f = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; g++) f = sq2_f32(w8[g], f);
+      nx2 += (double)f;
+    }
     if (AMAX) {
 #pragma unroll
       for (int g = 0; g < 8; g++) amax = max(amax, max(w8[g] & 0x7FFFu, (w8[g] >> 16) & 0x7FFFu));
@@ -131,6 +140,7 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     {
       u32x4 v;
       uint32_t code16 = 0, bytes = 0;
+      float ft = 0.f;
       const uint32_t r8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
       for (int g = 0; g < 4; g++) {
@@ -139,9 +149,14 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
         v[g] = vv;
         code16 |= cc << (4 * g);
         bytes |= cc << (8 * g);
-        const double t = sq2_f64(vv, nt2);
-        nt2 = valid ? t : nt2;
+        if (AMAX) {
+          const double t = sq2_f64(vv, nt2);
+          nt2 = valid ? t : nt2;
+        } else {
+          ft = sq2_f32(vv, ft);
+        }
       }
+      if (!AMAX && valid) nt2 += (double)ft;
       if (COMPRESS) {
       *reinterpret_cast<u32x4*>(a.cvals + cvals_off(p, KT, kt) + rb * 1024 + lane * 16) = v;
       *reinterpret_cast<uint16_t*>(a.cidx + cidx_off(p, KT, kt) + lane * 8 + rb * 2) = (uint16_t)code16;
@@ -291,6 +306,48 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     for (int cb = 0; cb < CB; cb++) tacc[cb] = tsum[cb] + tacc[cb];
     nx2 = xs + nx2;
     nt2 = ts + nt2;
+  }
+  // Rows whose total lies in [2^-80, 2^100] keep it: no square or fp32 step sum exceeds the
+  // total, so none overflowed, and squares that underflowed add at most K 2^-126 <= 2^-104,
+  // under 2^-24 of the total; each step sum is within 16 2^-24 of exact (8 dot products of
+  // non-negative terms), and the double sums add far less.  Any other row (all-zero rows included)
+  // is summed again in double precision from X over all of K, the row's four lanes each
+  // taking their 16 values of every K step, then added across the lanes.
+  if (!AMAX) {
+    const bool redo = row_ok && !(nx2 >= 0x1p-80 && nx2 <= 0x1p100);
+    if (__any(redo)) {
+      double x2 = 0.0, t2 = 0.0;
+      if (redo) {
+        for (int kt = 0; kt < KT; kt++) {
+          u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff, kt * kBK * 2, 0);
+          u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(xres, x_voff + 16, kt * kBK * 2, 0);
+          if (ACT) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              x0[e] = gelu_bf16x2(x0[e]);
+              x1[e] = gelu_bf16x2(x1[e]);
+            }
+          }
+          const uint32_t r8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+          for (int g = 0; g < 8; g++) x2 = sq2_f64(r8[g], x2);
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            uint32_t vv, cc;
+            select_bf16(r8[2 * g], r8[2 * g + 1], vv, cc);
+            t2 = sq2_f64(vv, t2);
+          }
+        }
+      }
+      x2 += __shfl_xor(x2, 16, 64);
+      t2 += __shfl_xor(t2, 16, 64);
+      x2 += __shfl_xor(x2, 32, 64);
+      t2 += __shfl_xor(t2, 32, 64);
+      if (redo) {
+        nx2 = x2;
+        nt2 = t2;
+      }
+    }
   }
   // The whole row tile's sums: s, and T or T / s.
   if (q == 0) {

@@ -95,6 +95,14 @@ __device__ __forceinline__ double sq2_f64(uint32_t d, double acc) {
   return fma(hi, hi, fma(lo, lo, acc));
 }
 
+// The same in fp32, one packed dot product per word: squares below 2^-126 lose bits and
+// squares above 2^128 overflow, so a caller keeps it for rows whose fp32 sum ends inside a
+// range where neither can matter and sums the others again with sq2_f64.
+__device__ __forceinline__ float sq2_f32(uint32_t d, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d), __builtin_bit_cast(bf16x2, d), acc, false);
+}
+
 // s = ||X|| / (||X~|| + eps) from the squared norms, in double precision, rounded to fp32;
 // an all-zero row (nx2 == 0, hence nt2 == 0) has s = 0.  For a nonzero row nt2 > 0
 // (the two largest magnitudes of some group are kept), so eps == 0 is allowed.

@@ -27,9 +27,11 @@
  *  - Selection compares magnitudes exactly (as integers on the sign-cleared bit
  *    patterns); ties go to the lower channel index; exactly two positions are kept in
  *    every group even when it holds fewer than two nonzeros.  Inputs must be finite.
- *  - The squared row norms ||X||^2 and ||X~||^2 are summed in double precision and s is
- *    formed in double precision and rounded to fp32, so no finite row underflows or
- *    overflows them (s > 0 for every nonzero row).  The products (X~ W^T, X L_B^T and Y)
+ *  - The squared row norms ||X||^2 and ||X~||^2 are summed in double precision (the bf16
+ *    layer's pre-pass sums the squares of each K step of 64 in fp32 first, and sums again
+ *    in double any row whose total lies outside [2^-80, 2^100], where fp32 squares could
+ *    underflow or overflow) and s is formed in double precision and rounded to fp32, so no
+ *    finite row underflows or overflows them (s > 0 for every nonzero row).  The products (X~ W^T, X L_B^T and Y)
  *    accumulate in fp32 and must lie in its range.
  *  - eps must lie in [0, 1] (RTL_ERR_ARG otherwise); the method uses 1e-8.
  *  - Extents: K <= 2^22, and M and N below 2^31 with fewer than 2^31 output tiles of

@@ -77,7 +77,7 @@ def check_pair(p, tag, variant, rows=None):
     gs = to_host(ds)
     nz = sel["s"] > 0
     assert np.all(gs[~nz] == 0)
-    assert np.all(np.abs(gs[nz] - sel["s"][nz]) <= tol_s() * sel["s"][nz])
+    assert np.all(np.abs(gs[nz] - sel["s"][nz]) <= tol_s("step") * sel["s"][nz])
     rows = np.arange(M) if rows is None else rows
     Yref, Xd_ref = oracle.mlp(p["X"], p["Wu"], p["LAu"], p["LBu"], p["Wd"], p["LAd"], p["LBd"], rows=rows,
                               want_xd=True)

@@ -45,7 +45,7 @@ def check_sparsify(d, tag):
     zero = ref["s"] == 0
     assert np.all(gs[zero] == 0)
     rel = np.abs(gs[~zero] - ref["s"][~zero]) / ref["s"][~zero]
-    assert rel.max(initial=0) <= tol_s(K), rel.max()
+    assert rel.max(initial=0) <= tol_s("double"), rel.max()
     return gi
 
 
@@ -104,12 +104,13 @@ def run_fused(d, with_dbg=True, variant=rtl.RTL_VARIANT_AUTO):
     return Y, (gi.t if gi else None), (gs.t if gs else None)
 
 
-def check_s(gs, sref):
+def check_s(gs, sref, dt="bf16"):
+    """s of the fused layer (the bf16 pre-pass sums each K step's squares in fp32)."""
     zero = sref == 0
     assert np.all(gs[zero] == 0)
     assert np.all(gs[~zero] > 0)
     rel = np.abs(gs[~zero] - sref[~zero]) / sref[~zero]
-    assert rel.max(initial=0) <= tol_s(), rel.max(initial=0)
+    assert rel.max(initial=0) <= tol_s("step" if dt == "bf16" else "double"), rel.max(initial=0)
 
 
 def check_fused_full(d, tag, variant=rtl.RTL_VARIANT_AUTO):
@@ -120,7 +121,7 @@ def check_fused_full(d, tag, variant=rtl.RTL_VARIANT_AUTO):
     err, _ = check_y(f64(to_host(Y), dt), Yref, dt, tag)
     ref = oracle.sparsify(d["X"])
     assert np.array_equal(to_host(dbg_idx), ref["idx"])
-    check_s(to_host(dbg_s), sref)
+    check_s(to_host(dbg_s), sref, dt)
     return err
 
 
