@@ -942,9 +942,11 @@ void half_kernel(const GemmArgs a) {
   constexpr int WBUF = 4;                       // W goes straight into a 4-buffer LDS ring
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
   // take the rank-R branch first, from T / s, L_A and s staged in LDS past the ring.  The
-  // other widths stage only L_A there, at the start, and take the branch at the end with
-  // T / s from memory (two 128-wide workgroups, or one 256-wide one, then fill the 160 KB
-  // of LDS).  The single store writes Y = s * acc.
+  // other widths stage L_A there (two 128-wide workgroups, or one 256-wide one, then fill
+  // the 160 KB of LDS); 128-wide tiles take the branch at the end with T / s from memory,
+  // 256-wide ones first, with T / s staged in ring buffer 3 (just before the L_A copy, and
+  // first written by the main loop after the branch) and s read into registers.  The
+  // single store writes Y = s * acc.
   constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = !LSTG;
   __shared__ __attribute__((aligned(1024)))
   uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : LAST ? TW * 128 : 0)];
@@ -1004,6 +1006,9 @@ void half_kernel(const GemmArgs a) {
     const int k = min(i, KT - 1) + koff;
     return k >= KT ? k - KT : k;
   };
+  // A operand of logical step i: past the last step (an empty step), step KT, which lies
+  // outside the panel's buffer range and reads as zeros.
+  auto kpa = [&](int i) { return ONE && i >= KT ? KT : kp(i); };
   u32x8 bp0, bp1;
   // Direct-to-LDS W staging (DTL): the i-th 16-byte load of lane l in wave w lands at
   // byte (4 i + w) * 1024 + 16 l of its stage, row n = 32 i + 8 w + l / 8 at swizzled
@@ -1031,7 +1036,7 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
       if (nb + BQ < NB) bq[(nb + BQ) % (BQ + 1)] = read_b(buf, nb + BQ);
-      if (nb < 5) load_frag_part(kp(kt + AAH), anext, nb);
+      if (nb < 5) load_frag_part(kpa(kt + AAH), anext, nb);
       if (nb >= NB - WLD) dtl_w(kp(kt + 3), dbuf, nb - (NB - WLD));
       const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % (BQ + 1)]);
       acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0]), bv, acc[0][nb],
@@ -1056,6 +1061,18 @@ void half_kernel(const GemmArgs a) {
   // reads.
   const bool lfirst = LSTG && a.R <= 64;
   const bool lalds = LAST && a.R > 0 && a.R <= 64;
+  const bool tfirst = TW == 256 && !PROD && lalds;
+  uint8_t* const lora3 = wl + 3 * TW * 128;  // ring buffer 3 and then the L_A copy
+  float s_pre[4];
+  if (tfirst) {
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+      const int64_t row = m0 + 64 * wave + 16 * rb + r16;
+      s_pre[rb] = a.s[row < M ? row : M - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lora_stage_t<4>(lora3, a, m0, wave, lane);
+  }
   if (lfirst) lora_stage_lds<TW, 4>(lora, a, m0, n0, wave, lane);
   if (lalds) lora_stage_la<TW, 4>(lora, a, n0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -1066,25 +1083,36 @@ void half_kernel(const GemmArgs a) {
   for (int st = 0; st < 3; st++)
 #pragma unroll
     for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
-  if (lfirst) {
+  if (lfirst || tfirst) {
     wait_vmcnt<5 * AAH + 3 * WLD>();  // the rank-R operands (issued before the loads since)
     barrier_nofence();
-    lora_slice_lds<NB>(acc, lora, (int)a.R, 64 * wave, 0, lane);
+    lora_slice_lds<NB>(acc, lfirst ? lora : lora3, (int)a.R, 64 * wave, 0, lane);
   }
   wait_vmcnt<WLD>();
   barrier_nofence();
 #pragma unroll
   for (int j = 0; j < BQ; j++) bp[j] = read_b(0, j);
   // Ring buffers cycle with period 4, A sets with period AAH + 1: whole periods in the
-  // loop (no exit in its body), then the rest.
+  // loop (no exit in its body).  One workgroup per CU: the last period is padded with
+  // empty steps, whose A operand is read past the end of the wave's panel (zeros), so their
+  // MFMAs add nothing (code after the loop for the rest would hold all 256 accumulators in
+  // general registers at once: 10-15% slower where K / 64 is not a multiple of 4).  Two
+  // per CU: the rest of the steps after the loop.
   int kt = 0;
-  for (; kt + PER <= KT; kt += PER) {
+  if constexpr (ONE) {
+    for (; kt < KT; kt += PER) {
 #pragma unroll
-    for (int j = 0; j < PER; j++) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
+      for (int j = 0; j < PER; j++) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
+    }
+  } else {
+    for (; kt + PER <= KT; kt += PER) {
+#pragma unroll
+      for (int j = 0; j < PER; j++) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
+    }
+#pragma unroll
+    for (int j = 0; j < PER - 1; j++)
+      if (kt + j < KT) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
   }
-#pragma unroll
-  for (int j = 0; j < PER - 1; j++)
-    if (kt + j < KT) step_dtl(kt + j, j % WBUF, fa[j % NSET], fa[(j + AAH) % NSET]);
   wait_vmcnt<0>();  // no load into the ring is left in flight when the epilogue reuses it
 
   // Epilogue: s of row 16rb + r16 (the row this lane feeds as A operand) and of the
@@ -1094,10 +1122,10 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
     const int64_t row = m0 + 64 * wave + 16 * rb + r16;
-    s_row[rb] = lfirst ? lora_s_lds<TW>(lora, 64 * wave + 16 * rb + r16) : a.s[row < M ? row : M - 1];
+    s_row[rb] = lfirst ? lora_s_lds<TW>(lora, 64 * wave + 16 * rb + r16) : tfirst ? s_pre[rb] : a.s[row < M ? row : M - 1];
   }
   const int64_t R = a.R;
-  for (int kk = 0; kk < (lfirst ? 0 : (int)(R / 32)); kk++) {
+  for (int kk = 0; kk < (lfirst || tfirst ? 0 : (int)(R / 32)); kk++) {
     u32x4 ta[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {

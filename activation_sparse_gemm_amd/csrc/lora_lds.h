@@ -25,22 +25,28 @@ __device__ __forceinline__ void lora_stage_la(uint8_t* dst, const GemmArgs& a, i
     __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
                                              (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
 }
+// The tile's T rows (rows m0..m0 + 255) into dst, swizzled as above.
+template <int NW>
+__device__ __forceinline__ void lora_stage_t(uint8_t* dst, const GemmArgs& a, int64_t m0, int wave, int lane) {
+  const int64_t R = a.R, Mp = (int64_t)a.n_panels * kPanel;
+  const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
+  const int ch = R >= 8 ? (int)(R / 8) : 1;                  // 16-byte chunks per row
+  const int src = (lane & ~(ch - 1)) | ((lane ^ (lane / ch)) & (ch - 1));  // chunk this lane loads
+  for (int j = wave; j < (int)(R / 2); j += NW)  // 1 KB blocks of the 256 x R tile of T
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                             (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
+}
 // T, L_A and s of the tile (layout above).
 template <int TW, int NW>
 __device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a, int64_t m0, int64_t n0, int wave,
                                                int lane) {
   constexpr int kLoraA = TW * 64 * 2, SPW = 1024 / NW;
-  const int64_t R = a.R, Mp = (int64_t)a.n_panels * kPanel;
+  const int64_t Mp = (int64_t)a.n_panels * kPanel;
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.s + m0, (Mp - m0) * 4);
   if (16 * lane < SPW)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(lora + kLoraT + kLoraA + wave * SPW),
                                              16, (uint32_t)(wave * SPW + lane * 16), 0, 0, 0);
-  const __amdgpu_buffer_rsrc_t tres = make_rsrc(a.T + m0 * R, (Mp - m0) * R * 2);
-  const int ch = R >= 8 ? (int)(R / 8) : 1;                  // 16-byte chunks per row
-  const int src = (lane & ~(ch - 1)) | ((lane ^ (lane / ch)) & (ch - 1));  // chunk this lane loads
-  for (int j = wave; j < (int)(R / 2); j += NW)  // 1 KB blocks of the 256 x R tile of T
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(lora + j * 1024), 16,
-                                             (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
+  lora_stage_t<NW>(lora, a, m0, wave, lane);
   lora_stage_la<TW, NW>(lora + kLoraT, a, n0, wave, lane);
 }
 // Fragment of staged L_A for tile column c, K = R slice kk: chunk 4 kk + q of row c.
