@@ -408,6 +408,8 @@ void gemm_kernel(const GemmArgs a) {
 
   Raw xr0, xr1;
   WStage w0, w1;
+  const bool lfirst = CALDS && a.R > 0 && a.R <= 64;
+  float s_first[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (MODE == kModeDense) {
     AStage a0, a1;
     // same issue order as the loop (A, then W) so the wait counts at the loop head match
@@ -432,6 +434,11 @@ void gemm_kernel(const GemmArgs a) {
   } else if constexpr (CALDS) {
     AFrag f0, f1;
     AStg s0, s1;
+    // R <= 64: the rank-R slice first, from T / s, L_A and s copied into the W ring (its
+    // first two buffers, which the first stages fill only after the slice), while the
+    // first stages' loads are in flight; s then stays in registers.
+    if (lfirst) lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
     // same issue order as the loop (A, then W, per stage) so the wait counts at the loop
     // head match the steady state
     load_ast(kp(0), s0);
@@ -440,6 +447,14 @@ void gemm_kernel(const GemmArgs a) {
     load_ast(kp(1), s1);
     load_w(kp(1), w1);
     __builtin_amdgcn_sched_barrier(0);
+    if (lfirst) {
+      wait_vmcnt<2 * (3 + WLD)>();  // the rank-R operands (issued before the two stages)
+      barrier_nofence();
+      lora_slice_lds<NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) s_first[rb] = lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16);
+      __syncthreads();  // every wave is done with the copy
+    }
     store_ast(s0, 0);
     store_w(w0, 0);
     store_ast(s1, 1);
@@ -499,26 +514,16 @@ void gemm_kernel(const GemmArgs a) {
   }
 
   if (SPARSE) {
-    // Epilogue: acc += (T / s)_tile L_A_tile^T (K = R in slices of 32), then Y = s * acc.
-    // Pre-compressed mode with R <= 64 first copies the tile's T / s, L_A and s into the
-    // (now free) W ring once per workgroup and takes the slice from there (loaded by every
-    // wave straight from memory they are a 192 KB burst per workgroup through L2).
-    const bool lds_slice = MODE == kModeComp && a.R <= 64;
-    if (lds_slice) {
-      wait_vmcnt<0>();
-      __syncthreads();  // every wave is done with the ring
-      lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
-      wait_vmcnt<0>();
-      __syncthreads();
-      lora_slice_lds<NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
-    }
+    // Epilogue: unless taken first, acc += (T / s)_tile L_A_tile^T (K = R in slices of
+    // 32, loaded by every wave straight from memory); then Y = s * acc.
+    const bool lds_slice = lfirst;
     // s of row 16rb + r16 (the row this lane feeds as A operand), then of the accumulator
     // rows 16rb + 4q + j, held by lane 4q + j.
     float s_row[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-      s_row[rb] = lds_slice ? lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16) : a.s[row < M ? row : M - 1];
+      s_row[rb] = lds_slice ? s_first[rb] : a.s[row < M ? row : M - 1];
     }
     float s_acc[4][4];
 #pragma unroll
