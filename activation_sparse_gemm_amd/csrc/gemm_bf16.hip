@@ -948,9 +948,10 @@ void half_kernel(const GemmArgs a) {
   // 192-wide tiles run one workgroup per CU (192 accumulators per lane) and, for R <= 64,
   // take the rank-R branch first, from T / s, L_A and s staged in LDS past the ring.  The
   // other widths stage L_A there (two 128-wide workgroups, or one 256-wide one, then fill
-  // the 160 KB of LDS); 128-wide tiles take the branch at the end with T / s from memory,
-  // 256-wide ones first, with T / s staged in ring buffer 3 (just before the L_A copy, and
-  // first written by the main loop after the branch) and s read into registers.  The
+  // the 160 KB of LDS) and, for R <= 64, also take the branch first, with T / s staged in
+  // the ring just before the L_A copy (256 wide: buffer 3, first written by the main loop
+  // after the branch; 128 wide: buffers 2-3, W stage 2 then loaded after the branch) and s
+  // read into registers; for R > 64 they take it at the end with T / s from memory.  The
   // single store writes Y = s * acc.
   constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = !LSTG;
   __shared__ __attribute__((aligned(1024)))
@@ -1066,8 +1067,11 @@ void half_kernel(const GemmArgs a) {
   // reads.
   const bool lfirst = LSTG && a.R <= 64;
   const bool lalds = LAST && a.R > 0 && a.R <= 64;
-  const bool tfirst = TW == 256 && !PROD && lalds;
-  uint8_t* const lora3 = wl + 3 * TW * 128;  // ring buffer 3 and then the L_A copy
+  const bool tfirst = (TW == 256 || TW == 128) && lalds;
+  // T / s right before the L_A copy: ring buffer 3 (256 wide), buffers 2-3 (128 wide, whose
+  // W stage 2 is then loaded after the slice)
+  constexpr bool LATE2 = TW == 128;
+  uint8_t* const lora3 = wl + (LATE2 ? 2 : 3) * TW * 128;
   float s_pre[4];
   if (tfirst) {
 #pragma unroll
@@ -1084,14 +1088,27 @@ void half_kernel(const GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < AAH; j++) load_frag(kp(j), fa[j]);
   __builtin_amdgcn_sched_barrier(0);
+  if (LATE2 && tfirst) {
 #pragma unroll
-  for (int st = 0; st < 3; st++)
+    for (int st = 0; st < 2; st++)
 #pragma unroll
-    for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
-  if (lfirst || tfirst) {
-    wait_vmcnt<5 * AAH + 3 * WLD>();  // the rank-R operands (issued before the loads since)
+      for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+    wait_vmcnt<5 * AAH + 2 * WLD>();  // the rank-R operands (issued before the loads since)
     barrier_nofence();
-    lora_slice_lds<NB>(acc, lfirst ? lora : lora3, (int)a.R, 64 * wave, 0, lane);
+    lora_slice_lds<NB>(acc, lora3, (int)a.R, 64 * wave, 0, lane);
+    barrier_nofence();  // every wave is done with the copy of T / s in buffers 2-3
+#pragma unroll
+    for (int i = 0; i < WLD; i++) dtl_w(kp(2), 2, i);
+  } else {
+#pragma unroll
+    for (int st = 0; st < 3; st++)
+#pragma unroll
+      for (int i = 0; i < WLD; i++) dtl_w(kp(st), st, i);
+    if (lfirst || tfirst) {
+      wait_vmcnt<5 * AAH + 3 * WLD>();  // the rank-R operands (issued before the loads since)
+      barrier_nofence();
+      lora_slice_lds<NB>(acc, lfirst ? lora : lora3, (int)a.R, 64 * wave, 0, lane);
+    }
   }
   wait_vmcnt<WLD>();
   barrier_nofence();
