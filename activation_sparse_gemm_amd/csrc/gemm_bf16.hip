@@ -1327,10 +1327,9 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     return hipGetLastError();
   }
   // 256-wide pre-compressed tiles: the 4-wave kernel (less LDS traffic per K step) for
-  // long K, the 8-wave one (lower fixed cost per tile) otherwise; measured on the
-  // workload layers: K = 12288 and 13824 6-7% faster in the 4-wave kernel, K = 5120 3%
-  // slower.
-  if (comp && tn == 256 && K > 8192) {
+  // K > 4096, measured 3-14% faster than the 8-wave one at K = 5120-13824 (below that the
+  // 128-wide tiling is nearly always the pick); the 8-wave one otherwise.
+  if (comp && tn == 256 && K > 4096) {
     SkPlan sp;
     if (rv == kVariantStreamK && sk_plan(M, N, K, sp)) {
       uint8_t* skb = const_cast<uint8_t*>(base) + align256(ws_layout(M, K, R, true).total);
