@@ -307,6 +307,26 @@ def test_fused_stream_k(R):
     assert torch.equal(Y.view(torch.int16), Y3.view(torch.int16))
 
 
+@pytest.mark.parametrize("K,R", [(4160, 64), (4224, 0), (4288, 96)])
+def test_fused_partial_last_period(K, R):
+    """256-wide tiles on the one-workgroup-per-CU kernel (K > 4096) with K / 64 one, two and
+    three steps past a whole number of its 4-step periods, so the last period carries empty
+    steps; rank-R branch first (R = 64), absent (R = 0) and at the end (R = 96).  Y on rows of
+    every tile against the oracle, and a second call into a workspace of random bytes
+    bit-identical."""
+    M, N = 1540, 8000
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=9700 + K + R)
+    Y, _ = check_tiles(d, f"partial-period K={K} R={R}", variant=rtl.RTL_VARIANT_AUTO)
+    dev = {k: to_dev(d[k]) for k in ("X", "W", "LA", "LB")}
+    need = rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R)
+    g = torch.Generator(device="cuda").manual_seed(78)
+    ws = torch.randint(0, 256, (max(need, 1),), dtype=torch.uint8, device="cuda", generator=g)
+    Y2 = rtl.rtl_linear_fused(dev["X"], dev["W"], dev["LA"], dev["LB"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+
+
 def test_fused_stream_k_mlp_down():
     """The stream-K variant at the text-to-image MLP's down-projection shape (4608 x 3072,
     K = 12288: 216 tiles, 162 K steps per workgroup): Y in full against the oracle, and the
