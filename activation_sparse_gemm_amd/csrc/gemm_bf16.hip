@@ -2,14 +2,14 @@
 // activation-sparse linear layer ("RT-Lynx: Putting the GEMM Sparsity In a Right Way for
 // Diffusion Models", summary page, method steps 1, 2 and 4):
 //
-//  gemm_kernel<MODE, DBG, TN>: the product on a 256 x TN output tile.
-//    kModeComp:  the A operand arrives compressed from the pre-pass (kept values and
-//                2-bit positions in sparse-MFMA register order).
+//  gemm_kernel<MODE, DBG, TN>: the product on a 256 x TN output tile, 8 waves.
 //    kModeFused: the 2-of-4 selection and compression run in the GEMM's own A-operand
 //                prologue, one K step ahead of the sparse MFMAs (s comes from the
 //                pre-pass, which also selects to form ||X~||).
 //    kModeDense: the dense product X W^T (v_mfma_f32_16x16x32_bf16), same tiling.
-//  Sparse modes run v_smfmac_f32_16x16x64_bf16.  The rank-R branch goes into the same
+//  half_kernel<TW> (4 waves): the default, the A operand compressed by the pre-pass (kept
+//    values and 2-bit positions in sparse-MFMA register order).
+//  Sparse kernels run v_smfmac_f32_16x16x64_bf16.  The rank-R branch goes into the same
 //  accumulators as one extra K = R MFMA slice with T / s (formed by the pre-pass in double
 //  precision) as its A operand, and the single store writes Y = s * acc; so the M x N
 //  low-rank product never reaches device memory, and s * (T / s) L_A^T = T L_A^T.
@@ -20,37 +20,27 @@
 
 namespace rtl {
 
-constexpr int kModeDense = 0, kModeFused = 1, kModeComp = 2;
+constexpr int kModeDense = 0, kModeFused = 1;
 
-// GEMM workgroup: 8 waves (two per SIMD) on a 256 x TN output tile (TN = 192 or 256; the
-// pre-compressed mode only at 256, 192-wide pre-compressed tiles run in half_kernel); wave
-// w owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  W (and, in the pre-compressed
-// mode, the compressed operand) goes memory -> registers -> LDS: a 3-buffer ring in the
-// pre-compressed mode (loaded a step before it is written, written two steps before it
-// is used), a 2-buffer ring in the dense and fused modes.  Fused mode: of each row slab,
-// the two waves that share it select two 16-row blocks each and trade the compressed
-// operand through LDS.
+// GEMM workgroup: 8 waves (two per SIMD) on a 256 x TN output tile (TN = 192 or 256); wave
+// w owns rows 64(w % 4)..+63 and columns (TN/2)(w / 4)..  W (and the dense mode's X tile)
+// goes memory -> registers -> a 2-buffer LDS ring.  Fused mode: of each row slab, the two
+// waves that share it select two 16-row blocks each and trade the compressed operand
+// through LDS.
 constexpr int kGemmThreads = 512;
 constexpr int kXBlk = 64 * 16 + 64 * 2;   // fused: one row block of the compressed operand
 constexpr int kALds = kBM * 128;          // A tile bytes per LDS buffer (dense layout, the largest)
-constexpr int kCompIdx = 16384;           // pre-compressed: offset of the position words in an A buffer
-constexpr int kCompStage = 16384 + 2048;  // pre-compressed: one K step of the tile's four panels
 
 template <int MODE, bool DBG, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const GemmArgs a) {
   static_assert(TN == 256 || TN == 192, "tile widths");
-  static_assert(MODE != kModeComp || TN == 256, "192-wide pre-compressed tiles run in half_kernel<192>");
   constexpr int NB = TN / 32;                     // 16-column blocks per wave (each wave: TN/2 columns)
   constexpr int WLD = TN * 8 / kGemmThreads;      // 16-byte W chunks per thread per K step
   constexpr bool SPARSE = MODE != kModeDense;
   constexpr bool FUSED = MODE == kModeFused;
-  constexpr int ALD = MODE == kModeDense ? 4 : 3;  // 16-byte A chunks per thread per K step (not fused)
-  __shared__ __attribute__((aligned(1024))) uint8_t wl[(MODE == kModeComp ? 3 : 2) * TN * 128];
-  // Pre-compressed mode (256-wide tiles): the compressed operand goes through LDS too, so
-  // the two waves that share a row slab load it once.
-  constexpr bool CALDS = MODE == kModeComp && TN == 256;
-  __shared__ __attribute__((aligned(1024))) uint8_t alc[CALDS ? 3 * kCompStage : 16];
+  constexpr int ALD = 4;                          // dense: 16-byte X chunks per thread per K step
+  __shared__ __attribute__((aligned(1024))) uint8_t wl[2 * TN * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
 
   int tm, tn;
@@ -66,7 +56,7 @@ void gemm_kernel(const GemmArgs a) {
   // Buffer resources anchored at this tile: 32-bit offsets, and loads past the end of
   // the matrix (ragged M or N tails) return zeros.
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(a.W + n0 * K, (N - n0) * K * 2);
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.X + (MODE == kModeComp ? 0 : m0 * K), (M - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(a.X + m0 * K, (M - m0) * K * 2);
 
   // Tile staging: thread t moves 16-byte chunks id = t + 512 i; chunk id of a [rows][64]
   // bf16 tile is row id / 8, k chunk id % 8, stored XOR-swizzled (sw_off).
@@ -84,24 +74,13 @@ void gemm_kernel(const GemmArgs a) {
       *reinterpret_cast<u32x4*>(wl + buf * TN * 128 + sw_off(srow + 64 * i, schunk)) = st[i];
   };
 
-  // A staging (dense: X tile like W; pre-compressed: the tile's four 64-row panels, values
-  // then position words).
+  // Dense mode: the X tile, staged like W.
   typedef u32x4 AStage[ALD];
-  const int64_t panel0 = (int64_t)tm * 4;
-  auto cpanel = [&](int pp) { return min(panel0 + pp, (int64_t)a.n_panels - 1); };
   auto load_at = [&](int kt, AStage& st) {
     if (MODE == kModeDense) {
 #pragma unroll
       for (int i = 0; i < ALD; i++)
         st[i] = __builtin_amdgcn_raw_buffer_load_b128(xres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
-    } else if (MODE == kModeComp) {
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const int id = tid + 512 * i, pp = id >> 8;
-        st[i] = *reinterpret_cast<const u32x4*>(a.cvals + cvals_off(cpanel(pp), KT, kt) + (id & 255) * 16);
-      }
-      const int id = tid & 127, pp = id >> 5;
-      st[2] = *reinterpret_cast<const u32x4*>(a.cidx + cidx_off(cpanel(pp), KT, kt) + (id & 31) * 16);
     }
   };
   auto store_at = [&](const AStage& st, int buf) {
@@ -109,14 +88,6 @@ void gemm_kernel(const GemmArgs a) {
     if (MODE == kModeDense) {
 #pragma unroll
       for (int i = 0; i < ALD; i++) *reinterpret_cast<u32x4*>(b + sw_off(srow + 64 * i, schunk)) = st[i];
-    } else if (MODE == kModeComp) {
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const int id = tid + 512 * i;
-        *reinterpret_cast<u32x4*>(b + (id >> 8) * 4096 + (id & 255) * 16) = st[i];
-      }
-      const int id = tid & 127;  // threads beyond 128 rewrite the same bytes
-      *reinterpret_cast<u32x4*>(b + kCompIdx + (id >> 5) * 512 + (id & 31) * 16) = st[2];
     }
   };
 
@@ -124,7 +95,7 @@ void gemm_kernel(const GemmArgs a) {
     u32x4 v[4][2];   // dense: [rb][kk]; sparse: [rb][0] kept values
     uint32_t iw[2];  // sparse: 16-bit position words, row block rb in half rb & 1 of iw[rb / 2]
   };
-  auto read_a = [&](int buf, AFrag& f) {  // dense / pre-compressed: the wave's rows from LDS
+  auto read_a = [&](int buf, AFrag& f) {  // dense: the wave's rows from LDS
     const uint8_t* b = al + buf * kALds;
     if (MODE == kModeDense) {
 #pragma unroll
@@ -133,12 +104,6 @@ void gemm_kernel(const GemmArgs a) {
         f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + sw_off(row, q));
         f.v[rb][1] = *reinterpret_cast<const u32x4*>(b + sw_off(row, 4 + q));
       }
-    } else if (MODE == kModeComp) {
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + wm * 4096 + rb * 1024 + lane * 16);
-      const uint2 w = *reinterpret_cast<const uint2*>(b + kCompIdx + wm * 512 + lane * 8);
-      f.iw[0] = w.x;
-      f.iw[1] = w.y;
     }
   };
 
@@ -262,10 +227,6 @@ void gemm_kernel(const GemmArgs a) {
   auto load_w_part = [&](int kt, WStage& st, int i) {
     st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
   };
-  // The first two B fragments of a pre-compressed step arrive in bp0, bp1, read at the end
-  // of the previous step: with three buffers, that buffer is complete before the barrier,
-  // so no LDS latency is exposed at the step boundary.
-  u32x8 bp0, bp1;
   // K order: tile (tm, tn) starts at K step (tm + tn) % 8 and wraps around, so the
   // workgroups of an XCD that share a W column block (same tn) or a compressed row panel
   // (same tm) reach each K step at different times: one of them takes the L2 miss and the
@@ -275,94 +236,7 @@ void gemm_kernel(const GemmArgs a) {
     const int k = min(i, KT - 1) + koff;
     return k >= KT ? k - KT : k;
   };
-  auto read_bc = [&](int buf, int nb) {
-    const uint8_t* base = wl + buf * TN * 128;
-    const int n = (TN / 2) * wn + nb * 16 + r16;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + sw_off(n, q));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + sw_off(n, 4 + q));
-    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  // Compressed operand through LDS: thread t moves value chunks t and t + 512 (panels
-  // t / 256 and t / 256 + 2) and position word t (panel t / 128) of a K step; one LDS
-  // stage holds the tile's four panels (values, then position words).
-  struct AStg {
-    u32x4 v[2];
-    uint32_t i;
-  };
-  const int64_t pan4 = (int64_t)tm * 4;
-  const int64_t npan4 = min<int64_t>(4, (int64_t)a.n_panels - pan4);
-  const __amdgpu_buffer_rsrc_t tvres = make_rsrc(MODE == kModeComp ? a.cvals + cvals_off(pan4, KT, 0) : nullptr, npan4 * KT * 4096);
-  const __amdgpu_buffer_rsrc_t tires = make_rsrc(MODE == kModeComp ? a.cidx + cidx_off(pan4, KT, 0) : nullptr, npan4 * KT * 512);
-  const uint32_t av0 = (uint32_t)((tid >> 8) * KT * 4096 + (tid & 255) * 16);
-  const uint32_t av1 = av0 + (uint32_t)(2 * KT * 4096);
-  const uint32_t ai = (uint32_t)((tid >> 7) * KT * 512 + (tid & 127) * 4);
-  const uint32_t lv0 = (uint32_t)((tid >> 8) * 4096 + (tid & 255) * 16), lv1 = lv0 + 2 * 4096;
-  const uint32_t li = (uint32_t)(16384 + (tid >> 7) * 512 + (tid & 127) * 4);
-  auto load_ast_part = [&](int kt, AStg& st, int part) {
-    if (part == 0) st.v[0] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av0, kt * 4096, 0);
-    if (part == 1) st.v[1] = __builtin_amdgcn_raw_buffer_load_b128(tvres, av1, kt * 4096, 0);
-    if (part == 2) st.i = __builtin_amdgcn_raw_buffer_load_b32(tires, ai, kt * 512, 0);
-  };
-  auto load_ast = [&](int kt, AStg& st) {
-#pragma unroll
-    for (int part = 0; part < 3; part++) load_ast_part(kt, st, part);
-  };
-  auto store_ast = [&](const AStg& st, int buf) {
-    uint8_t* b = alc + buf * kCompStage;
-    *reinterpret_cast<u32x4*>(b + lv0) = st.v[0];
-    *reinterpret_cast<u32x4*>(b + lv1) = st.v[1];
-    *reinterpret_cast<uint32_t*>(b + li) = st.i;
-  };
-  auto read_afrag = [&](int buf, AFrag& f) {
-    const uint8_t* b = alc + buf * kCompStage;
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++) f.v[rb][0] = *reinterpret_cast<const u32x4*>(b + wm * 4096 + rb * 1024 + lane * 16);
-    const uint2 w = *reinterpret_cast<const uint2*>(b + 16384 + wm * 512 + lane * 8);
-    f.iw[0] = w.x;
-    f.iw[1] = w.y;
-  };
-  // Pre-compressed step kt on the 3-buffer LDS rings (buffer kt % 3), the memory
-  // operations spread over the MFMA loop with at most two loads per column block (a burst
-  // of loads holds up the wave's next MFMAs): blocks 0-2 load one part each of A stage
-  // kt + 3, block NB - WLD - 1 writes A stage kt + 2 (loaded a step ago) to buffer
-  // (kt + 2) % 3, each of the last WLD blocks writes one chunk of W stage kt + 2 and loads
-  // one of stage kt + 3, and the next step's A fragments and first B fragments are read
-  // from buffer (kt + 1) % 3 before the barrier.
-  auto step_ca = [&](int kt, int buf, WStage& wst, WStage& wfree, AStg& ast, AStg& afree, const AFrag& cur,
-                     AFrag& nxt) {
-    const int sbuf = buf == 0 ? 2 : buf - 1, nbuf = buf == 2 ? 0 : buf + 1;
-    u32x8 bq[3];
-    bq[0] = bp0;
-    bq[1] = bp1;
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-      if (nb + 2 < NB) bq[(nb + 2) % 3] = read_bc(buf, nb + 2);
-      if (nb < 3) load_ast_part(kp(kt + 3), afree, nb);
-      if (nb == NB - WLD - 1) store_ast(ast, sbuf);
-      if (nb >= NB - WLD) {
-        const int i = nb - (NB - WLD);
-        *reinterpret_cast<u32x4*>(wl + sbuf * TN * 128 + sw_off(srow + 64 * i, schunk)) = wst[i];
-        load_w_part(kp(kt + 3), wfree, i);
-      }
-      const bf16x16 bv = __builtin_bit_cast(bf16x16, bq[nb % 3]);
-      acc[0][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[0][0]), bv, acc[0][nb],
-                                                             (int)cur.iw[0], 0, 0);
-      acc[1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[1][0]), bv, acc[1][nb],
-                                                             (int)cur.iw[0], 0, 1);
-      acc[2][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[2][0]), bv, acc[2][nb],
-                                                             (int)cur.iw[1], 0, 0);
-      acc[3][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, cur.v[3][0]), bv, acc[3][nb],
-                                                             (int)cur.iw[1], 0, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bp0 = read_bc(nbuf, 0);
-    bp1 = read_bc(nbuf, 1);
-    read_afrag(nbuf, nxt);
-    __syncthreads();
-  };
-
-  // Dense step with the memory operations spread over the MFMA loop (as in the
-  // pre-compressed steps): column block 1 issues the A loads and block 2 the W loads for
+  // Dense step with the memory operations spread over the MFMA loop: column block 1 issues the A loads and block 2 the W loads for
   // step kt + 2, and the last blocks write stage kt + 1 (loaded a step ago) to the other
   // LDS buffer.  K order staggered per tile as above.
   auto step_d = [&](int kt, WStage& wnext, WStage& wfar, AStage& anext, AStage& afar) {
@@ -408,8 +282,6 @@ void gemm_kernel(const GemmArgs a) {
 
   Raw xr0, xr1;
   WStage w0, w1;
-  const bool lfirst = CALDS && a.R > 0 && a.R <= 64;
-  float s_first[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (MODE == kModeDense) {
     AStage a0, a1;
     // same issue order as the loop (A, then W) so the wait counts at the loop head match
@@ -431,66 +303,6 @@ void gemm_kernel(const GemmArgs a) {
       step_d(kt + 1, w0, w1, a0, a1);
     }
     if (kt < KT) step_d(kt, w1, w0, a1, a0);
-  } else if constexpr (CALDS) {
-    AFrag f0, f1;
-    AStg s0, s1;
-    // R <= 64: the rank-R slice first, from T / s, L_A and s copied into the W ring (its
-    // first two buffers, which the first stages fill only after the slice), while the
-    // first stages' loads are in flight; s then stays in registers.
-    if (lfirst) lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    // same issue order as the loop (A, then W, per stage) so the wait counts at the loop
-    // head match the steady state
-    load_ast(kp(0), s0);
-    load_w(kp(0), w0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_ast(kp(1), s1);
-    load_w(kp(1), w1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (lfirst) {
-      wait_vmcnt<2 * (3 + WLD)>();  // the rank-R operands (issued before the two stages)
-      barrier_nofence();
-      lora_slice_lds<NB>(acc, wl, (int)a.R, 64 * wm, (TN / 2) * wn, lane);
-#pragma unroll
-      for (int rb = 0; rb < 4; rb++) s_first[rb] = lora_s_lds<TN>(wl, 64 * wm + 16 * rb + r16);
-      __syncthreads();  // every wave is done with the copy
-    }
-    store_ast(s0, 0);
-    store_w(w0, 0);
-    store_ast(s1, 1);
-    store_w(w1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_ast(kp(2), s0);
-    load_w(kp(2), w0);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    bp0 = read_bc(0, 0);
-    bp1 = read_bc(0, 1);
-    read_afrag(0, f0);
-    // LDS buffers cycle with period 3, register sets with period 2: whole periods of 6
-    // steps in the loop (no exit in its body, as for the dense steps), then the rest.
-    int kt = 0;
-    for (; kt + 6 <= KT; kt += 6) {
-      step_ca(kt, 0, w0, w1, s0, s1, f0, f1);
-      step_ca(kt + 1, 1, w1, w0, s1, s0, f1, f0);
-      step_ca(kt + 2, 2, w0, w1, s0, s1, f0, f1);
-      step_ca(kt + 3, 0, w1, w0, s1, s0, f1, f0);
-      step_ca(kt + 4, 1, w0, w1, s0, s1, f0, f1);
-      step_ca(kt + 5, 2, w1, w0, s1, s0, f1, f0);
-    }
-    if (kt < KT) {
-      step_ca(kt, 0, w0, w1, s0, s1, f0, f1);
-      if (kt + 1 < KT) {
-        step_ca(kt + 1, 1, w1, w0, s1, s0, f1, f0);
-        if (kt + 2 < KT) {
-          step_ca(kt + 2, 2, w0, w1, s0, s1, f0, f1);
-          if (kt + 3 < KT) {
-            step_ca(kt + 3, 0, w1, w0, s1, s0, f1, f0);
-            if (kt + 4 < KT) step_ca(kt + 4, 1, w0, w1, s0, s1, f0, f1);
-          }
-        }
-      }
-    }
   } else {
   AStage a0, a1;
   load_w(0, w0);
@@ -514,16 +326,15 @@ void gemm_kernel(const GemmArgs a) {
   }
 
   if (SPARSE) {
-    // Epilogue: unless taken first, acc += (T / s)_tile L_A_tile^T (K = R in slices of
-    // 32, loaded by every wave straight from memory); then Y = s * acc.
-    const bool lds_slice = lfirst;
+    // Epilogue: acc += (T / s)_tile L_A_tile^T (K = R in slices of 32, loaded by every
+    // wave straight from memory); then Y = s * acc.
     // s of row 16rb + r16 (the row this lane feeds as A operand), then of the accumulator
     // rows 16rb + 4q + j, held by lane 4q + j.
     float s_row[4];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       const int64_t row = m0 + 64 * wm + 16 * rb + r16;
-      s_row[rb] = lds_slice ? s_first[rb] : a.s[row < M ? row : M - 1];
+      s_row[rb] = a.s[row < M ? row : M - 1];
     }
     float s_acc[4][4];
 #pragma unroll
@@ -531,7 +342,7 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; j++) s_acc[rb][j] = __shfl(s_row[rb], 4 * q + j, 64);
     const int64_t R = a.R;
-    for (int kk = 0; kk < (lds_slice ? 0 : (int)(R / 32)); kk++) {
+    for (int kk = 0; kk < (int)(R / 32); kk++) {
       u32x4 ta[4];
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
@@ -1272,8 +1083,8 @@ static GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, int64_t R, const void
 // Pre-compressed GEMM: two 256 x 128 workgroups per CU instead of one 256 x TN one, when
 // that gives the busiest CU less work.  Per output column the 128-wide kernel is a little
 // cheaper for short K (its two workgroups per CU hide each other's tile prologue and
-// epilogue) and dearer for long K (it moves more operand bytes per K step than the
-// 256-wide kernel, which shares the compressed rows through LDS).
+// epilogue) and dearer for long K (its tiles re-read the compressed rows for half as many
+// output columns).
 static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
   const int64_t tm = (M + kBM - 1) / kBM;
   const int tn = choose_tn(M, N);
@@ -1283,15 +1094,10 @@ static bool use_half_tiles(int64_t M, int64_t N, int64_t K) {
   return half_cost < full_cost;
 }
 
+// The prologue variant's GEMM (selection in the A-operand prologue).
 template <int TN>
-static void launch_main_tn(bool comp, GemmArgs g, uint8_t* dbg_idx, hipStream_t stream) {
+static void launch_main_tn(GemmArgs g, uint8_t* dbg_idx, hipStream_t stream) {
   const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(kGemmThreads);
-  if constexpr (TN == 256) {
-    if (comp) {
-      hipLaunchKernelGGL((gemm_kernel<kModeComp, false, TN>), grid, block, 0, stream, g);
-      return;
-    }
-  }
   if (dbg_idx != nullptr) {
     hipLaunchKernelGGL((gemm_kernel<kModeFused, true, TN>), grid, block, 0, stream, g);
   } else {
@@ -1326,10 +1132,10 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     hipLaunchKernelGGL((half_kernel<192>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream, g);
     return hipGetLastError();
   }
-  // 256-wide pre-compressed tiles: the 4-wave kernel (less LDS traffic per K step) for
-  // K > 4096, measured 3-14% faster than the 8-wave one at K = 5120-13824 (below that the
-  // 128-wide tiling is nearly always the pick); the 8-wave one otherwise.
-  if (comp && tn == 256 && K > 4096) {
+  // 256-wide pre-compressed tiles: the 4-wave kernel (the 128-wide tiling wins wherever
+  // K <= 4096, so these have K > 4096, where it measured 3-14% faster than an 8-wave form
+  // that shared the compressed rows through LDS).
+  if (comp) {
     SkPlan sp;
     if (rv == kVariantStreamK && sk_plan(M, N, K, sp)) {
       uint8_t* skb = const_cast<uint8_t*>(base) + align256(ws_layout(M, K, R, true).total);
@@ -1345,8 +1151,8 @@ hipError_t launch_main_bf16(int variant, int64_t M, int64_t N, int64_t K, int64_
     hipLaunchKernelGGL((half_kernel<256>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(kHalfThreads), 0, stream, g);
     return hipGetLastError();
   }
-  if (tn == 192) launch_main_tn<192>(comp, g, dbg_idx, stream);
-  else launch_main_tn<256>(comp, g, dbg_idx, stream);
+  if (tn == 192) launch_main_tn<192>(g, dbg_idx, stream);
+  else launch_main_tn<256>(g, dbg_idx, stream);
   return hipGetLastError();
 }
 
