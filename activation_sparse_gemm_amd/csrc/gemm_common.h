@@ -71,24 +71,31 @@ struct SkArgs {
 };
 
 // Output tile store through LDS: the accumulator layout (lane = column 16nb + r16, rows
-// 4q + j) goes 16 rows at a time into a per-wave LDS block and comes back as 16-byte row
-// chunks, so Y is written with full 16-byte stores along its rows.  `blk` is the wave's
-// block of 16 * (2 CW + 16) bytes (CW = the wave's columns; the 16-byte pad puts the four
-// row groups of a write in different banks); `val(rb, nb, j)` gives the float to store.
+// 4q + j) goes 16 rows at a time into a per-wave LDS block, rounded to bf16 (nearest even)
+// two values per conversion, and comes back as 16-byte row chunks, so Y is written with
+// full 16-byte stores along its rows.  `blk` is the wave's block of 16 * (2 CW + 16) bytes
+// (CW = the wave's columns; the 16-byte pad puts the four row groups of a write in
+// different banks); `val(rb, nb, j)` gives the float to store.
 template <int RB, int NBW, typename Val>
 __device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, int64_t row0, int64_t col0, uint8_t* blk,
                                            int lane, Val val) {
   constexpr int CW = NBW * 16, PITCH = 2 * CW + 16, CPR = CW / 8;  // 16-byte chunks per row
   const int q = lane >> 4, r16 = lane & 15;
   const bool vec = (N & 7) == 0;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
     for (int nb = 0; nb < NBW; nb++)
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        *reinterpret_cast<uint16_t*>(blk + (4 * q + j) * PITCH + (nb * 16 + r16) * 2) =
-            (uint16_t)f32_to_bf16_bits(val(rb, nb, j));
+      for (int j = 0; j < 4; j += 2) {
+        // rows 4q + j and 4q + j + 1 rounded to bf16 (nearest even) by one packed conversion
+        const bf16x2_t pr = {(__bf16)val(rb, nb, j), (__bf16)val(rb, nb, j + 1)};
+        const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+        uint8_t* at = blk + (4 * q + j) * PITCH + (nb * 16 + r16) * 2;
+        *reinterpret_cast<uint16_t*>(at) = (uint16_t)w;
+        *reinterpret_cast<uint16_t*>(at + PITCH) = (uint16_t)(w >> 16);
+      }
 #pragma unroll
     for (int c = 0; c < 16 * CPR / 64; c++) {
       const int id = lane + 64 * c, rr = id / CPR, cc = id % CPR;
