@@ -114,6 +114,52 @@ __device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, in
   }
 }
 
+// Column permutation of the 128- and 256-wide 4-wave tiles: MFMA column position p = 16 nb + r16
+// (column block nb, lane r16) computes tile column perm_col(p), so that lane r16 of the blocks
+// 8h..8h+7 holds the eight consecutive columns 128h + 8 r16 .. + 7.  Applied where W and L_A
+// rows are staged; the tile store then writes 16-byte row chunks straight from the
+// accumulators.  perm_col(32 i + t) = perm_col(32 i) + perm_col(t) for t < 32.
+__device__ __forceinline__ int perm_col(int p) { return 128 * (p >> 7) + 8 * (p & 15) + ((p >> 4) & 7); }
+
+// Output tile store from the accumulators of a perm_col tile (NB = 8 or 16 column blocks):
+// for accumulator row 16 rb + 4q + j and half h, lane r16 rounds the eight values of blocks
+// 8h..8h+7 to bf16 (nearest even, two per conversion) and writes them as one 16-byte chunk
+// at column col0 + 128h + 8 r16; each store instruction covers four whole 256-byte row
+// segments.  `val(rb, nb, j)` gives the float to store.
+template <int NB, typename Val>
+__device__ __forceinline__ void store_tile_regs(uint16_t* Y, int64_t M, int64_t N, int64_t row0, int64_t col0,
+                                                int lane, Val val) {
+  static_assert(NB % 8 == 0, "whole 128-column halves");
+  const int q = lane >> 4, r16 = lane & 15;
+  const bool vec = (N & 7) == 0;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t row = row0 + 16 * rb + 4 * q + j;
+#pragma unroll
+      for (int h = 0; h < NB / 8; h++) {
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const bf16x2_t pr = {(__bf16)val(rb, 8 * h + 2 * e, j), (__bf16)val(rb, 8 * h + 2 * e + 1, j)};
+          v[e] = __builtin_bit_cast(uint32_t, pr);
+        }
+        const int64_t col = col0 + 128 * h + 8 * r16;
+        if (row >= M) continue;
+        uint16_t* y = Y + row * N + col;
+        if (vec && col + 8 <= N) {
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y));  // Y is not read again here
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++)
+            if (col + e < N) y[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+}
+
 // Output tile width: the candidate whose tile count best fills whole waves of
 // workgroups over the 256 CUs (a 192-wide tile costs a little more per column).
 inline int choose_tn(int64_t M, int64_t N) {

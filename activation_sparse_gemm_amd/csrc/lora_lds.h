@@ -14,16 +14,23 @@ namespace rtl {
 // l mod R / 8 of row l / (R / 8) and so loads the chunk stored there; s: 1024 / NW bytes
 // per wave); the caller waits for them (vmcnt) and then synchronises the workgroup.
 constexpr int kLoraT = 256 * 64 * 2;
-// The tile's L_A rows (columns n0..n0 + TW - 1 of the output) into dst, swizzled as above.
-template <int TW, int NW>
+// The tile's L_A rows (columns n0..n0 + TW - 1 of the output) into dst, swizzled as above;
+// with PERM, position p holds the row of tile column perm_col(p).
+template <int TW, int NW, bool PERM = false>
 __device__ __forceinline__ void lora_stage_la(uint8_t* dst, const GemmArgs& a, int64_t n0, int wave, int lane) {
   const int64_t R = a.R;
   const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.LA + n0 * R, (a.N - n0) * R * 2);
   const int ch = R >= 8 ? (int)(R / 8) : 1;                  // 16-byte chunks per row
   const int src = (lane & ~(ch - 1)) | ((lane ^ (lane / ch)) & (ch - 1));  // chunk this lane loads
-  for (int j = wave; j < (int)(TW * R / 512); j += NW)  // 1 KB blocks of the TW x R tile of L_A
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
-                                             (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
+  for (int j = wave; j < (int)(TW * R / 512); j += NW) {  // 1 KB blocks of the TW x R tile of L_A
+    uint32_t off = (uint32_t)(j * 1024 + src * 16);
+    if (PERM) {
+      const int p = j * (int)(512 / R) + lane / ch;  // position (tile column slot) of the row
+      off = (uint32_t)(perm_col(p) * R * 2 + (src & (ch - 1)) * 16);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, off,
+                                             0, 0, 0);
+  }
 }
 // The tile's T rows (rows m0..m0 + 255) into dst, swizzled as above.
 template <int NW>
