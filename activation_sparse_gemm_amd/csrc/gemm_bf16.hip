@@ -40,6 +40,8 @@ void gemm_kernel(const GemmArgs a) {
   constexpr bool SPARSE = MODE != kModeDense;
   constexpr bool FUSED = MODE == kModeFused;
   constexpr int ALD = 4;                          // dense: 16-byte X chunks per thread per K step
+  // 256 wide: permuted columns (perm_col, within each wave's 128), stored from the accumulators
+  constexpr bool PERM = TN == 256;
   __shared__ __attribute__((aligned(1024))) uint8_t wl[2 * TN * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t al[FUSED ? 2 * 16 * kXBlk : (MODE == kModeDense ? 2 * kALds : 16)];
 
@@ -62,11 +64,15 @@ void gemm_kernel(const GemmArgs a) {
   // bf16 tile is row id / 8, k chunk id % 8, stored XOR-swizzled (sw_off).
   const int srow = tid >> 3, schunk = tid & 7;
   const uint32_t w_voff = (uint32_t)(srow * K * 2 + 16 * schunk);
+  // W chunk id goes to LDS row srow + 64 i, which holds W row n0 + perm_col(srow + 64 i)
+  // in a permuted tile.
+  const uint32_t wp_voff = (uint32_t)((PERM ? perm_col(srow) : srow) * K * 2 + 16 * schunk);
   typedef u32x4 WStage[WLD];
   auto load_w = [&](int kt, WStage& st) {
 #pragma unroll
     for (int i = 0; i < WLD; i++)
-      st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          wres, wp_voff, (int)((PERM ? perm_col(64 * i) : 64 * i) * K * 2 + (int64_t)kt * kBK * 2), 0);
   };
   auto store_w = [&](const WStage& st, int buf) {
 #pragma unroll
@@ -224,9 +230,6 @@ void gemm_kernel(const GemmArgs a) {
     __syncthreads();
   };
 
-  auto load_w_part = [&](int kt, WStage& st, int i) {
-    st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K * 2 + (int64_t)kt * kBK * 2), 0);
-  };
   // K order: tile (tm, tn) starts at K step (tm + tn) % 8 and wraps around, so the
   // workgroups of an XCD that share a W column block (same tn) or a compressed row panel
   // (same tm) reach each K step at different times: one of them takes the L2 miss and the
@@ -351,13 +354,18 @@ void gemm_kernel(const GemmArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) {
-        const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
+        const int64_t col = n0 + (PERM ? perm_col((TN / 2) * wn + nb * 16 + r16) : (TN / 2) * wn + nb * 16 + r16);
         const u32x4 la = *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
 #pragma unroll
         for (int rb = 0; rb < 4; rb++)
           acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, ta[rb]), __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
       }
+    }
+    if constexpr (PERM) {
+      store_tile_regs<NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, lane,
+                          [&](int rb, int nb, int j) { return acc[rb][nb][j] * s_acc[rb][j]; });
+      return;
     }
     __syncthreads();  // the LDS rings are free
     store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
@@ -366,7 +374,12 @@ void gemm_kernel(const GemmArgs a) {
   }
 
   // Dense: store Y (bf16, round to nearest even).  Lane holds column 16nb + r16 of its
-  // half, rows 16rb + 4q + j of its slab.
+  // half (perm_col of it in a permuted tile), rows 16rb + 4q + j of its slab.
+  if constexpr (PERM) {
+    store_tile_regs<NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, lane,
+                        [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
+    return;
+  }
   __syncthreads();  // the LDS rings are free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
                     [&](int rb, int nb, int j) { return acc[rb][nb][j]; });

@@ -1,6 +1,7 @@
 // gemm_common.h -- pieces shared by the GEMM kernels (gemm_bf16.hip, gemm_fp8.hip): the
 // output tile height, the XCD-aware tile order, the kernel argument block, the output
-// tile store through LDS, and the choice of the output tile width.
+// tile stores (through LDS, or from the accumulators of a column-permuted tile), and the
+// choice of the output tile width.
 #pragma once
 #include "bf16_common.h"
 
@@ -114,11 +115,12 @@ __device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, in
   }
 }
 
-// Column permutation of the 128- and 256-wide 4-wave tiles: MFMA column position p = 16 nb + r16
-// (column block nb, lane r16) computes tile column perm_col(p), so that lane r16 of the blocks
-// 8h..8h+7 holds the eight consecutive columns 128h + 8 r16 .. + 7.  Applied where W and L_A
+// Column permutation of the 128- and 256-wide tiles (the 8-wave kernel's: within each wave's
+// 128 columns): MFMA column position p = 16 nb + r16 (column block nb, lane r16) computes tile
+// column perm_col(p), so that lane r16 of the blocks 8h..8h+7 holds the eight consecutive
+// columns 128h + 8 r16 .. + 7.  Applied where W and L_A
 // rows are staged; the tile store then writes 16-byte row chunks straight from the
-// accumulators.  perm_col(32 i + t) = perm_col(32 i) + perm_col(t) for t < 32.
+// accumulators.  perm_col(x + y) = perm_col(x) + perm_col(y) when x and y share no set bit.
 __device__ __forceinline__ int perm_col(int p) { return 128 * (p >> 7) + 8 * (p & 15) + ((p >> 4) & 7); }
 
 // Output tile store from the accumulators of a perm_col tile (NB = 8 or 16 column blocks):
