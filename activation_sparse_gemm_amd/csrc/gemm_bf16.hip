@@ -778,8 +778,8 @@ void half_kernel(const GemmArgs a) {
   // read into registers; for R > 64 they take it at the end with T / s from memory.  The
   // single store writes Y = s * acc.
   constexpr bool ONE = TW >= 192, LSTG = TW == 192, LAST = !LSTG;
-  // 128 and 256 wide: permuted columns (perm_col), stored straight from the accumulators
-  constexpr bool PERM = !LSTG && !PROD;
+  // permuted columns (perm_tile), stored straight from the accumulators
+  constexpr bool PERM = !PROD;
   __shared__ __attribute__((aligned(1024)))
   uint8_t wl[WBUF * TW * 128 + (LSTG ? kLoraT + TW * 128 + 1024 : LAST ? TW * 128 : 0)];
   uint8_t* const lora = wl + WBUF * TW * 128;
@@ -845,12 +845,16 @@ void half_kernel(const GemmArgs a) {
   // Direct-to-LDS W staging (DTL): the i-th 16-byte load of lane l in wave w lands at
   // byte (4 i + w) * 1024 + 16 l of its stage, row n = 32 i + 8 w + l / 8 at swizzled
   // position l % 8, which sw_off assigns to logical chunk (l % 8) ^ (n % 8).  Row n holds
-  // W row n0 + n, or n0 + perm_col(n) in a permuted tile.
-  const uint32_t d_voff = (uint32_t)((PERM ? perm_col(srow) : srow) * K * 2 + 16 * ((lane & 7) ^ (srow & 7)));
+  // W row n0 + n, or n0 + perm_tile<TW>(n) in a permuted tile: the lane's part of that row
+  // in d_voff, or d_voff2 for loads i >= 4 of a 192-wide tile (its columns 128..191), the
+  // uniform part perm_tile<TW>(32 i) in the load's scalar offset.
+  const uint32_t d_chunk = 16 * ((lane & 7) ^ (srow & 7));
+  const uint32_t d_voff = (uint32_t)((PERM ? perm_col(srow) : srow) * K * 2 + d_chunk);
+  const uint32_t d_voff2 = (uint32_t)((PERM && TW == 192 ? perm_tile<TW>(128 + srow) - 128 : srow) * K * 2 + d_chunk);
   auto dtl_w = [&](int kt, int buf, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        wres, (__attribute__((address_space(3))) void*)(wl + buf * TW * 128 + (4 * i + wave) * 1024), 16, d_voff,
-        (int)((PERM ? perm_col(32 * i) : 32 * i) * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
+        wres, (__attribute__((address_space(3))) void*)(wl + buf * TW * 128 + (4 * i + wave) * 1024), 16,
+        TW == 192 && i >= 4 ? d_voff2 : d_voff, (int)((PERM ? perm_tile<TW>(32 * i) : 32 * i) * K * 2 + (int64_t)kt * kBK * 2), 0, 0);
   };
   // DTL step kt on ring buffer kt % 4: blocks 0-4 load one part each of A for step
   // kt + AAH, each of the last WLD blocks loads one chunk of W stage kt + 3 into buffer
@@ -909,7 +913,7 @@ void half_kernel(const GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     lora_stage_t<4>(lora3, a, m0, wave, lane);
   }
-  if (lfirst) lora_stage_lds<TW, 4>(lora, a, m0, n0, wave, lane);
+  if (lfirst) lora_stage_lds<TW, 4, PERM>(lora, a, m0, n0, wave, lane);
   if (lalds) lora_stage_la<TW, 4, PERM>(lora, a, n0, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -983,7 +987,7 @@ void half_kernel(const GemmArgs a) {
     }
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
-      const int64_t col = n0 + (PERM ? perm_col(nb * 16 + r16) : nb * 16 + r16);
+      const int64_t col = n0 + (PERM ? perm_tile<TW>(nb * 16 + r16) : nb * 16 + r16);
       const u32x4 la = lalds ? lora_la_lds(lora, (int)R, nb * 16 + r16, kk, q)
                              : *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
 #pragma unroll

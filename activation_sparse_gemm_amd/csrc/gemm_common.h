@@ -115,25 +115,32 @@ __device__ __forceinline__ void store_tile(uint16_t* Y, int64_t M, int64_t N, in
   }
 }
 
-// Column permutation of the 128- and 256-wide tiles (the 8-wave kernel's: within each wave's
-// 128 columns): MFMA column position p = 16 nb + r16 (column block nb, lane r16) computes tile
-// column perm_col(p), so that lane r16 of the blocks 8h..8h+7 holds the eight consecutive
-// columns 128h + 8 r16 .. + 7.  Applied where W and L_A
-// rows are staged; the tile store then writes 16-byte row chunks straight from the
-// accumulators.  perm_col(x + y) = perm_col(x) + perm_col(y) when x and y share no set bit.
+// Column permutation of the output tiles stored from the accumulators: MFMA column position
+// p = 16 nb + r16 (column block nb, lane r16) computes tile column perm_col(p), so that lane
+// r16 of the blocks 8h..8h+7 holds the eight consecutive columns 128h + 8 r16 .. + 7 (the
+// 8-wave kernel: within each wave's 128 columns).  Applied where W and L_A rows are staged;
+// the tile store then writes 16-byte row chunks straight from the accumulators.
+// perm_col(x + y) = perm_col(x) + perm_col(y) when x and y share no set bit.
 __device__ __forceinline__ int perm_col(int p) { return 128 * (p >> 7) + 8 * (p & 15) + ((p >> 4) & 7); }
+// The same for a TW-wide tile: at TW = 192 the last four blocks (columns 128..191) give lane
+// r16 the four consecutive columns 128 + 4 r16 .. + 3.
+template <int TW>
+__device__ __forceinline__ int perm_tile(int p) {
+  if (TW == 192 && p >= 128) return 128 + 4 * (p & 15) + ((p >> 4) & 3);
+  return perm_col(p);
+}
 
-// Output tile store from the accumulators of a perm_col tile (NB = 8 or 16 column blocks):
-// for accumulator row 16 rb + 4q + j and half h, lane r16 rounds the eight values of blocks
-// 8h..8h+7 to bf16 (nearest even, two per conversion) and writes them as one 16-byte chunk
-// at column col0 + 128h + 8 r16; each store instruction covers four whole 256-byte row
-// segments.  `val(rb, nb, j)` gives the float to store.
+// Output tile store from the accumulators of a perm_tile tile (NB = 8, 12 or 16 column
+// blocks): for accumulator row 16 rb + 4q + j and half h, lane r16 rounds the values of blocks
+// 8h..8h+7 (eight, or the last four at NB = 12) to bf16 (nearest even, two per conversion)
+// and writes them as one 16-byte (8-byte) chunk at column col0 + 128h + 8 r16 (+ 4 r16); each
+// store instruction covers four whole row segments of 256 (128) bytes.  `val(rb, nb, j)`
+// gives the float to store.
 template <int NB, typename Val>
 __device__ __forceinline__ void store_tile_regs(uint16_t* Y, int64_t M, int64_t N, int64_t row0, int64_t col0,
                                                 int lane, Val val) {
-  static_assert(NB % 8 == 0, "whole 128-column halves");
+  static_assert(NB == 8 || NB == 12 || NB == 16, "halves of 8 blocks, or 8 + 4");
   const int q = lane >> 4, r16 = lane & 15;
-  const bool vec = (N & 7) == 0;
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int rb = 0; rb < 4; rb++)
@@ -141,21 +148,25 @@ __device__ __forceinline__ void store_tile_regs(uint16_t* Y, int64_t M, int64_t 
     for (int j = 0; j < 4; j++) {
       const int64_t row = row0 + 16 * rb + 4 * q + j;
 #pragma unroll
-      for (int h = 0; h < NB / 8; h++) {
-        u32x4 v;
+      for (int h = 0; h < (NB + 7) / 8; h++) {
+        constexpr int kFull = 8;
+        const int nv = NB - 8 * h >= kFull ? kFull : NB - 8 * h;  // values per lane: 8 or 4
+        uint32_t v[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
+        for (int e = 0; e < nv / 2; e++) {
           const bf16x2_t pr = {(__bf16)val(rb, 8 * h + 2 * e, j), (__bf16)val(rb, 8 * h + 2 * e + 1, j)};
           v[e] = __builtin_bit_cast(uint32_t, pr);
         }
-        const int64_t col = col0 + 128 * h + 8 * r16;
+        const int64_t col = col0 + 128 * h + nv * r16;
         if (row >= M) continue;
         uint16_t* y = Y + row * N + col;
-        if (vec && col + 8 <= N) {
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y));  // Y is not read again here
+        if (nv == 8 && (N & 7) == 0 && col + 8 <= N) {
+          __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<u32x4*>(y));  // not read again here
+        } else if (nv == 4 && (N & 3) == 0 && col + 4 <= N) {
+          __builtin_nontemporal_store(u32x2{v[0], v[1]}, reinterpret_cast<u32x2*>(y));
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; e++)
+          for (int e = 0; e < nv; e++)
             if (col + e < N) y[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
         }
       }

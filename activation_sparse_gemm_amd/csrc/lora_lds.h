@@ -15,7 +15,7 @@ namespace rtl {
 // per wave); the caller waits for them (vmcnt) and then synchronises the workgroup.
 constexpr int kLoraT = 256 * 64 * 2;
 // The tile's L_A rows (columns n0..n0 + TW - 1 of the output) into dst, swizzled as above;
-// with PERM, position p holds the row of tile column perm_col(p).
+// with PERM, position p holds the row of tile column perm_tile<TW>(p).
 template <int TW, int NW, bool PERM = false>
 __device__ __forceinline__ void lora_stage_la(uint8_t* dst, const GemmArgs& a, int64_t n0, int wave, int lane) {
   const int64_t R = a.R;
@@ -26,7 +26,7 @@ __device__ __forceinline__ void lora_stage_la(uint8_t* dst, const GemmArgs& a, i
     uint32_t off = (uint32_t)(j * 1024 + src * 16);
     if (PERM) {
       const int p = j * (int)(512 / R) + lane / ch;  // position (tile column slot) of the row
-      off = (uint32_t)(perm_col(p) * R * 2 + (src & (ch - 1)) * 16);
+      off = (uint32_t)(perm_tile<TW>(p) * R * 2 + (src & (ch - 1)) * 16);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, off,
                                              0, 0, 0);
@@ -43,8 +43,8 @@ __device__ __forceinline__ void lora_stage_t(uint8_t* dst, const GemmArgs& a, in
     __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
                                              (uint32_t)(j * 1024 + src * 16), 0, 0, 0);
 }
-// T, L_A and s of the tile (layout above).
-template <int TW, int NW>
+// T, L_A and s of the tile (layout above; L_A permuted as in lora_stage_la).
+template <int TW, int NW, bool PERM = false>
 __device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a, int64_t m0, int64_t n0, int wave,
                                                int lane) {
   constexpr int kLoraA = TW * 64 * 2, SPW = 1024 / NW;
@@ -54,7 +54,7 @@ __device__ __forceinline__ void lora_stage_lds(uint8_t* lora, const GemmArgs& a,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (__attribute__((address_space(3))) void*)(lora + kLoraT + kLoraA + wave * SPW),
                                              16, (uint32_t)(wave * SPW + lane * 16), 0, 0, 0);
   lora_stage_t<NW>(lora, a, m0, wave, lane);
-  lora_stage_la<TW, NW>(lora + kLoraT, a, n0, wave, lane);
+  lora_stage_la<TW, NW, PERM>(lora + kLoraT, a, n0, wave, lane);
 }
 // Fragment of staged L_A for tile column c, K = R slice kk: chunk 4 kk + q of row c.
 __device__ __forceinline__ u32x4 lora_la_lds(const uint8_t* la, int R, int c, int kk, int q) {
