@@ -212,14 +212,13 @@ def test_fused_workload_layers(name, variant):
 
 
 # Output shapes that make the library pick each GEMM tiling (ragged M and N tails in all):
-#   4000 x 4000, K = 4160: 16 x 16 tiles of 256 x 256, one per CU (256-wide kernels; 65 K
-#                steps = ten whole turns of the 6-step ring and a 5-step tail);
+#   4000 x 4000, K = 4160: 16 x 16 tiles of 256 x 256, one per CU (the 4-wave kernel; 65 K
+#                steps = 16 whole turns of its 4-step ring and one step, padded);
 #   4000 x 4000, K = 512: two 256 x 128 workgroups per CU (pre-compressed variant);
 #   2000 x 6100: 8 x 32 tiles of 256 x 192, one per CU (192-wide kernels; K = 256 and 320
 #                are 4 and 5 K steps, shorter than one turn of the ring; K = 704 is one turn
 #                and a 5-step tail);
-#   4000 x 4000, K = 8256: 256 x 256 tiles in the 4-wave kernel (pre-compressed variant,
-#                K > 8192; 129 K steps, 32 whole turns of its 4-step ring and one step).
+#   4000 x 4000, K = 8256: the same tiles with 129 K steps (32 whole turns and one step).
 WIDE = [(4000, 4000, 4160), (4000, 4000, 512), (2000, 6100, 256), (2000, 6100, 320), (2000, 6100, 704),
         (4000, 4000, 8256)]
 
@@ -272,15 +271,31 @@ def test_fused_128_tiles_every_rank(K, R):
     check_tiles(synth.make_layer(lay, seed_base=9390 + K + R), "fused-128")
 
 
-# 256-wide pre-compressed tiles in both kernels (K = 4160: the 8-wave kernel, which copies
-# the rank-R operands into LDS for R <= 64; K = 8256: the 4-wave kernel) with every
-# other supported rank.
+# 256-wide pre-compressed tiles (the 4-wave kernel, K > 4096) with every other supported
+# rank: none, T / s and L_A staged in LDS (R <= 64), L_A read from memory (R > 64).
 @pytest.mark.parametrize("R", [0, 32, 128])
 @pytest.mark.parametrize("K", [4160, 8256])
 def test_fused_256_tiles_every_rank(K, R):
     M, N = 4000, 4000
     lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
     check_tiles(synth.make_layer(lay, seed_base=9290 + R + K), "fused-256")
+
+
+# Output widths that are not a multiple of 8 (or of 4) at every pre-compressed tiling: the
+# kernels compute a permuted column order and store each lane's 8 (at 192-wide tiles, in
+# columns 128..191, 4) consecutive columns as one chunk, so a ragged last tile-column
+# takes the element-wise store.  2000 x 6098 and x 6101: 192-wide tiles (last tile 146 and
+# 149 columns); 4000 x 4003: 128-wide tiles (K = 512, last tile 35 columns) and 256-wide
+# ones (K > 4096, last tile 161 or 165 columns); R from none to read-from-memory.
+ODD_N = [(2000, 6098, 320, 64), (2000, 6101, 704, 96), (4000, 4003, 512, 64), (4000, 4003, 512, 128),
+         (4000, 4001, 4160, 32), (4000, 4005, 8256, 128)]
+
+
+@pytest.mark.parametrize("shape", ODD_N, ids=lambda c: "x".join(map(str, c)))
+def test_fused_tiles_odd_widths(shape):
+    M, N, K, R = shape
+    lay = synth.Layer("t", M, K, N, R, "bf16", "heavy", 0.08)
+    check_tiles(synth.make_layer(lay, seed_base=9690 + N + K + R), "fused-odd-n")
 
 
 # Stream-K: fewer 256 x 256 tiles than CUs with K > 8192.  1540 x 8000 is 7 x 32 = 224
@@ -408,7 +423,8 @@ def test_fused_extreme_row_scales(shape, variant):
 # ------------------------------------------------------------------ rtl_linear_dense_ref
 
 @pytest.mark.parametrize("case", [(300, 520, 192, "bf16"), (1, 16, 64, "bf16"), (64, 256, 256, "f32"),
-                                  (50, 70, 36, "f32"), (2000, 6100, 320, "bf16"), (4000, 4000, 4160, "bf16")],
+                                  (50, 70, 36, "f32"), (2000, 6100, 320, "bf16"), (4000, 4000, 4160, "bf16"),
+                                  (2000, 6098, 320, "bf16"), (4000, 4003, 512, "bf16")],
                          ids=lambda c: "x".join(map(str, c)))
 def test_dense_small(case):
     M, N, K, dt = case
