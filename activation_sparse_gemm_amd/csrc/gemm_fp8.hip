@@ -68,6 +68,8 @@ void gemm_fp8_kernel(const GemmArgs a) {
   static_assert(TN == 256 || TN == 192, "tile widths");
   constexpr int NB = TN / 32;                 // 16-column blocks per wave
   constexpr int WLD = TN * 8 / kFp8Threads;   // 16-byte W chunks per thread per K step
+  // 256 wide: permuted columns (perm_col, within each wave's 128), stored from the accumulators
+  constexpr bool PERM = TN == 256;
   __shared__ __attribute__((aligned(1024))) uint8_t wl[3 * TN * 128];
   static_assert(3 * TN * 128 >= kLoraT + TN * 128 + 1024, "the ring holds the staged rank-R operands");
 
@@ -81,15 +83,16 @@ void gemm_fp8_kernel(const GemmArgs a) {
   const int64_t M = a.M, N = a.N, K = a.K;
   const int KT = (int)(K / kBK8);
 
-  // W codes: chunk (row srow + 64i, 16-byte chunk schunk) of each [TN][128] stage; rows
-  // past N read as zeros.
+  // W codes: chunk (row srow + 64i, 16-byte chunk schunk) of each [TN][128] stage, which
+  // holds W row n0 + perm_col(srow + 64i) in a permuted tile; rows past N read as zeros.
   const uint8_t* W8 = reinterpret_cast<const uint8_t*>(a.W);
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(W8 + n0 * K, (N - n0) * K);
   const int srow = tid >> 3, schunk = tid & 7;
-  const uint32_t w_voff = (uint32_t)(srow * K + 16 * schunk);
+  const uint32_t w_voff = (uint32_t)((PERM ? perm_col(srow) : srow) * K + 16 * schunk);
   typedef u32x4 WStage[WLD];
   auto load_w_part = [&](int kt, WStage& st, int i) {
-    st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff, (int)(i * 64 * K + (int64_t)kt * kBK8), 0);
+    st[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, w_voff,
+                                                  (int)((PERM ? perm_col(64 * i) : 64 * i) * K + (int64_t)kt * kBK8), 0);
   };
   auto load_w = [&](int kt, WStage& st) {
 #pragma unroll
@@ -208,9 +211,9 @@ void gemm_fp8_kernel(const GemmArgs a) {
     }
   }
 
-  // Epilogue: acc *= sw (column scale of the lane's column 16nb + r16) and s * sx (row
-  // scale; s_row[rb] belongs to row 16rb + r16, the row this lane feeds as A operand), then
-  // acc += T L_A^T (K = R in slices of 32), then the single bf16 store.
+  // Epilogue: acc *= sw (column scale of the lane's column, 16nb + r16 or perm_col of it)
+  // and s * sx (row scale; s_row[rb] belongs to row 16rb + r16, the row this lane feeds as
+  // A operand), then acc += T L_A^T (K = R in slices of 32), then the single bf16 store.
   float s_row[4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
@@ -220,7 +223,7 @@ void gemm_fp8_kernel(const GemmArgs a) {
   }
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) {
-    const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
+    const int64_t col = n0 + (PERM ? perm_col((TN / 2) * wn + nb * 16 + r16) : (TN / 2) * wn + nb * 16 + r16);
     const float swc = a.sw[col < N ? col : N - 1];
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) acc[rb][nb] *= swc;
@@ -232,7 +235,7 @@ void gemm_fp8_kernel(const GemmArgs a) {
     // from there.
     wait_vmcnt<0>();
     __syncthreads();
-    lora_stage_lds<TN, 8>(wl, a, m0, n0, wave, lane);
+    lora_stage_lds<TN, 8, PERM>(wl, a, m0, n0, wave, lane);
     wait_vmcnt<0>();
     __syncthreads();
     lora_slice_lds<NB>(acc, wl, (int)R, 64 * wm, (TN / 2) * wn, lane);
@@ -246,13 +249,18 @@ void gemm_fp8_kernel(const GemmArgs a) {
     }
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
-      const int64_t col = n0 + (TN / 2) * wn + nb * 16 + r16;
+      const int64_t col = n0 + (PERM ? perm_col((TN / 2) * wn + nb * 16 + r16) : (TN / 2) * wn + nb * 16 + r16);
       const u32x4 la = *reinterpret_cast<const u32x4*>(a.LA + (col < N ? col : N - 1) * R + 32 * kk + 8 * q);
 #pragma unroll
       for (int rb = 0; rb < 4; rb++)
         acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta[rb]),
                                                               __builtin_bit_cast(bf16x8, la), acc[rb][nb], 0, 0, 0);
     }
+  }
+  if constexpr (PERM) {
+    store_tile_regs<NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, lane,
+                        [&](int rb, int nb, int j) { return acc[rb][nb][j]; });
+    return;
   }
   __syncthreads();  // the LDS ring is free
   store_tile<4, NB>(a.Y, M, N, m0 + 64 * wm, n0 + (TN / 2) * wn, wl + wave * 16 * (TN + 16), lane,
