@@ -73,6 +73,21 @@ def test_fp8_small_shapes(shape):
     check_fp8(d, f"heavy{shape}")
 
 
+# 256-wide tiles (the 4000 x 4000-class shapes need two rounds of 192-wide ones), whose
+# kernel computes a permuted column order and stores each lane's 8 consecutive columns as
+# one chunk: output widths that are not a multiple of 8 (last tile 163 and 161 columns),
+# rank-R staged in LDS (R = 64) and read from memory (R = 128); rows of every tile.
+WIDE_ODD = [(4000, 512, 4003, 64), (4000, 256, 4001, 128)]
+
+
+@pytest.mark.parametrize("shape", WIDE_ODD)
+def test_fp8_wide_tiles_odd_widths(shape):
+    M, K, N, R = shape
+    lay = synth.Layer("fp8", M, K, N, R, "bf16", "heavy", 0.08)
+    d = synth.make_layer(lay, seed_base=7100 + K + N + R)
+    check_fp8(d, f"wide{shape}", rows=tile_rows(M))
+
+
 def test_fp8_zero_tiny_and_tied_rows():
     """All-zero rows (sx = 0, Y = 0), rows whose largest magnitude is too small for an
     fp32 448 / a (coded as zeros on both sides: only the rank-R branch remains), rows far
