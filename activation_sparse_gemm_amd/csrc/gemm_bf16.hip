@@ -13,6 +13,9 @@
 //  accumulators as one extra K = R MFMA slice with T / s (formed by the pre-pass in double
 //  precision) as its A operand, and the single store writes Y = s * acc; so the M x N
 //  low-rank product never reaches device memory, and s * (T / s) L_A^T = T L_A^T.
+//  The 4-wave kernels and the 256-wide 8-wave ones compute their tile's columns in the
+//  perm_col order (gemm_common.h), so each lane stores 16-byte row chunks of Y straight from
+//  its accumulators.
 #include <atomic>
 #include <random>
 
