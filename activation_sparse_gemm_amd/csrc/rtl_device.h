@@ -58,20 +58,16 @@ __device__ __forceinline__ void select_f32(const uint32_t x[4], int& lo, int& hi
   uint32_t a[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) a[j] = x[j] & 0x7FFFFFFFu;
-  int kept[2] = {0, 0}, nk = 0;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    int rank = 0;
-#pragma unroll
-    for (int l = 0; l < 4; l++)
-      if (l != j) rank += (a[l] > a[j]) || (a[l] == a[j] && l < j);
-    if (rank < 2) {
-      if (nk < 2) kept[nk] = j;
-      nk++;
-    }
-  }
-  lo = kept[0];
-  hi = kept[1];
+  // For l < j, l beats j when a_l >= a_j (a tie goes to the lower index) and j beats l
+  // otherwise; rank_j counts the positions that beat j, and j is kept when rank_j < 2.
+  const uint32_t c01 = a[0] >= a[1], c02 = a[0] >= a[2], c03 = a[0] >= a[3];
+  const uint32_t c12 = a[1] >= a[2], c13 = a[1] >= a[3], c23 = a[2] >= a[3];
+  const uint32_t r0 = 3u - (c01 + c02 + c03), r1 = c01 + 2u - (c12 + c13);
+  const uint32_t r2 = c02 + c12 + 1u - c23, r3 = c03 + c13 + c23;
+  const uint32_t keep = (uint32_t)(r0 < 2u) | ((uint32_t)(r1 < 2u) << 1) | ((uint32_t)(r2 < 2u) << 2) |
+                        ((uint32_t)(r3 < 2u) << 3);
+  lo = __builtin_ctz(keep);
+  hi = 31 - __builtin_clz(keep);
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t d) { return __uint_as_float(d << 16); }

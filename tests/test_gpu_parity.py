@@ -138,6 +138,8 @@ FUSED_SMALL = [
     (64, 256, 256, 8, "f32"),
     (50, 70, 36, 5, "f32"),
     (33, 40, 64, 0, "f32"),
+    (70, 100, 300, 32, "f32"),      # 3 K steps, the last one ragged; 4 L_B chunks per thread
+    (40, 64, 520, 128, "f32"),      # 5 K steps; the largest rank the fp32 path takes
 ]
 
 
