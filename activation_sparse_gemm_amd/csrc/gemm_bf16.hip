@@ -708,6 +708,9 @@ __device__ __forceinline__ void sk_tile(const GemmArgs& a, const SkArgs& sk, uin
           if (__hip_atomic_load(sk.flag + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sk.epoch) break;
           __builtin_amdgcn_s_sleep(2);
         }
+        // only this workgroup reads that flag: clear it, so that a replay of the launch
+        // with the same stamp (a captured graph) waits for the new partial
+        __hip_atomic_store(sk.flag + w, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();

@@ -25,7 +25,7 @@ struct PrepArgs {
   double* npart;      // [ks, Mp, 2] partial squared norms when ks > 1
   uint64_t* pflag;    // [ks, Mp / 64] flags: the last split sums the partials in the launch
                       // (null: a separate reduction does, from the [ks, Mp, R] layout)
-  uint64_t epoch;     // this launch's flag stamp
+  uint64_t epoch;     // this launch's flag stamp (nonzero; a consumed flag is reset to 0)
   int ks;             // K splits
   int kts;            // K steps per split
   int fold;           // write T / s (formed in double precision) instead of T
@@ -273,6 +273,13 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
           __builtin_amdgcn_s_sleep(2);
         }
       }
+      // Each flag is read by this workgroup alone: clear it once seen, so that a launch
+      // replayed with the same stamp (a captured graph) finds no flag set before its own
+      // splits set them.
+      for (int s0 = 0; s0 < a.ks - 1; s0 += 64)
+        if (s0 + lane < a.ks - 1)
+          __hip_atomic_store(a.pflag + (int64_t)(s0 + lane) * gx + bx, (uint64_t)0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     asm volatile("" ::: "memory");

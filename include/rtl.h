@@ -41,6 +41,9 @@
  *    atomic counter that stamps the launches whose workgroups hand partial sums to one
  *    another through the workspace (the K-split pre-pass, the stream-K GEMM) and the
  *    per-device address of the allocation-free call's device array (resolved once).
+ *  - Capturable: a call enqueues kernel launches only (no allocation, copy or memset), so
+ *    it can be recorded in a HIP graph; a replayed launch reuses its stamp, and each
+ *    consumer of a hand-off clears the flag it read, so replays on new inputs are exact.
  */
 #ifndef RTL_H
 #define RTL_H

@@ -179,3 +179,41 @@ def test_explicit_stream_without_workspace():
     for Y in outs:
         assert torch.equal(Y.view(torch.int16), ref.view(torch.int16))
     log(f"[stream] {len(outs)} side-stream calls with binding-allocated workspaces match the lone call")
+
+
+# A call captured in a graph and replayed on new inputs.  The K-split pre-pass and the
+# stream-K GEMM hand partials between workgroups behind flags stamped with the launch's
+# epoch, which a captured launch replays unchanged; the consumer clears each flag it has
+# seen, so a replay cannot take the previous replay's partials.  Consecutive replays get
+# different inputs (copied in eagerly between them) and each must equal an eager call.
+@pytest.mark.parametrize("case", [(300, 200, 1024, 64, 0), (4096, 3072, 3072, 64, 0), (1540, 8000, 8256, 64, 3)],
+                         ids=["prep-4-splits", "attn-proj-8-splits", "stream-k"])
+def test_graph_replay_on_new_inputs(case):
+    M, N, K, R, vcode = case
+    variant = {0: rtl.RTL_VARIANT_AUTO, 3: rtl.RTL_VARIANT_STREAM_K}[vcode]
+    ds = [synth.make_layer(synth.Layer("g", M, K, N, R, "bf16", "heavy", 0.08), seed_base=8100 + 7 * i)
+          for i in range(3)]
+    X = to_dev(ds[0]["X"])
+    W, LA, LB = (to_dev(ds[0][k]) for k in ("W", "LA", "LB"))
+    ws = torch.empty((rtl.rtl_linear_fused_workspace_bytes(rtl.RTL_BF16, M, N, K, R),), dtype=torch.uint8,
+                     device="cuda")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws, variant=variant)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rtl.rtl_linear_fused(X, W, LA, LB, Y=Y, workspace=ws, variant=variant)
+    for rep in range(6):
+        X.copy_(to_dev(ds[rep % 3]["X"]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = Y.clone()
+        ref = rtl.rtl_linear_fused(X, W, LA, LB, variant=variant)  # eager, its own workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+    log(f"[graph] {M}x{N}x{K} variant {variant}: 6 replays on alternating inputs equal eager calls")
