@@ -140,6 +140,8 @@ FUSED_SMALL = [
     (33, 40, 64, 0, "f32"),
     (70, 100, 300, 32, "f32"),      # 3 K steps, the last one ragged; 4 L_B chunks per thread
     (40, 64, 520, 128, "f32"),      # 5 K steps; the largest rank the fp32 path takes
+    (1, 1, 4, 1, "f32"),            # one row, one column, one group of 4, rank 1
+    (3, 33, 132, 9, "f32"),         # 2 K steps, the second one group long; 4 L_B chunks per thread
 ]
 
 
