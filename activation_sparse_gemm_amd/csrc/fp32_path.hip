@@ -90,16 +90,16 @@ __global__ __launch_bounds__(256) void f32_kernel(int64_t M, int64_t N, int64_t 
         *reinterpret_cast<u32x4*>(&Xs[lr][kl]) = cur.x[j];
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) nx2 = fma((double)__uint_as_float(x[jj]), (double)__uint_as_float(x[jj]), nx2);
-        int lo, hi;
-        select_f32(x, lo, hi);
+        const uint32_t keep = keep_mask_f32(x);
+        // dropped positions become +0; the kept squares are added in position order (the
+        // zeros add nothing, so the sum is the one over the two kept values)
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++)
-          if (jj != lo && jj != hi) kept[jj] = 0u;
-        const float vlo = __uint_as_float(x[lo]), vhi = __uint_as_float(x[hi]);
-        nt2 = fma((double)vlo, (double)vlo, nt2);
-        nt2 = fma((double)vhi, (double)vhi, nt2);
+        for (int jj = 0; jj < 4; jj++) {
+          kept[jj] = (keep >> jj) & 1u ? x[jj] : 0u;
+          nt2 = fma((double)__uint_as_float(kept[jj]), (double)__uint_as_float(kept[jj]), nt2);
+        }
         if (dbg_idx != nullptr && blockIdx.x == 0 && m0 + lr < M && k < K)
-          dbg_idx[(m0 + lr) * (K / 4) + k / 4] = (uint8_t)(lo | (hi << 2));
+          dbg_idx[(m0 + lr) * (K / 4) + k / 4] = (uint8_t)(__builtin_ctz(keep) | ((31 - __builtin_clz(keep)) << 2));
       }
       *reinterpret_cast<u32x4*>(&As[lr][kl]) = kept;
       *reinterpret_cast<u32x4*>(&Ws[lr][kl]) = cur.w[j];

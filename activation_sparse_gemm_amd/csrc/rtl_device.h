@@ -53,8 +53,9 @@ __device__ __forceinline__ void select_bf16(uint32_t d0, uint32_t d1, uint32_t& 
 }
 
 // 2-of-4 selection on one fp32 group (magnitudes as 31-bit patterns, ties to the lower
-// index).  Writes the two kept positions lo < hi.
-__device__ __forceinline__ void select_f32(const uint32_t x[4], int& lo, int& hi) {
+// index): keep_mask_f32 gives the kept positions as a 4-bit mask (two bits set),
+// select_f32 the two positions lo < hi.
+__device__ __forceinline__ uint32_t keep_mask_f32(const uint32_t x[4]) {
   uint32_t a[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) a[j] = x[j] & 0x7FFFFFFFu;
@@ -64,8 +65,10 @@ __device__ __forceinline__ void select_f32(const uint32_t x[4], int& lo, int& hi
   const uint32_t c12 = a[1] >= a[2], c13 = a[1] >= a[3], c23 = a[2] >= a[3];
   const uint32_t r0 = 3u - (c01 + c02 + c03), r1 = c01 + 2u - (c12 + c13);
   const uint32_t r2 = c02 + c12 + 1u - c23, r3 = c03 + c13 + c23;
-  const uint32_t keep = (uint32_t)(r0 < 2u) | ((uint32_t)(r1 < 2u) << 1) | ((uint32_t)(r2 < 2u) << 2) |
-                        ((uint32_t)(r3 < 2u) << 3);
+  return (uint32_t)(r0 < 2u) | ((uint32_t)(r1 < 2u) << 1) | ((uint32_t)(r2 < 2u) << 2) | ((uint32_t)(r3 < 2u) << 3);
+}
+__device__ __forceinline__ void select_f32(const uint32_t x[4], int& lo, int& hi) {
+  const uint32_t keep = keep_mask_f32(x);
   lo = __builtin_ctz(keep);
   hi = 31 - __builtin_clz(keep);
 }
