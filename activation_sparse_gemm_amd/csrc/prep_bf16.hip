@@ -273,13 +273,6 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
           __builtin_amdgcn_s_sleep(2);
         }
       }
-      // Each flag is read by this workgroup alone: clear it once seen, so that a launch
-      // replayed with the same stamp (a captured graph) finds no flag set before its own
-      // splits set them.
-      for (int s0 = 0; s0 < a.ks - 1; s0 += 64)
-        if (s0 + lane < a.ks - 1)
-          __hip_atomic_store(a.pflag + (int64_t)(s0 + lane) * gx + bx, (uint64_t)0, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     asm volatile("" ::: "memory");
@@ -313,6 +306,15 @@ __global__ __launch_bounds__(64 * PW) void prep_kernel(const PrepArgs a) {
     for (int cb = 0; cb < CB; cb++) tacc[cb] = tsum[cb] + tacc[cb];
     nx2 = xs + nx2;
     nt2 = ts + nt2;
+    // Each flag is read by this workgroup alone: clear it, so that a launch replayed with
+    // the same stamp (a captured graph) finds no flag set before its own splits set them.
+    // Issued after the partials are in registers: a later load's wait (the memory counter
+    // completes in order) would otherwise also wait for these stores.
+    if (wave == 0)
+      for (int s0 = 0; s0 < a.ks - 1; s0 += 64)
+        if (s0 + lane < a.ks - 1)
+          __hip_atomic_store(a.pflag + (int64_t)(s0 + lane) * gx + bx, (uint64_t)0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
   // Rows whose total lies in [2^-80, 2^100] keep it: no square or fp32 step sum exceeds the
   // total, so none overflowed, and squares that underflowed add at most K 2^-126 <= 2^-104,
